@@ -1,0 +1,469 @@
+/*
+ * halo_oracle.c -- plain, slow CPU oracle for the Hadamard-rotated low-precision
+ * linear layer (forward Y = X W^T, backward dX = dY W and dW = dY^T X).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU-baseline leg
+ * of the benchmark may load this library.  It shares no code, header, table or helper
+ * with the GPU library, and the GPU library never calls it.
+ *
+ * Pages followed (cited by title and section):
+ *   [QWHA]  "QWHA方法：基于Walsh-Hadamard变换的高效大模型微调技术"
+ *           s2.1  the Walsh-Hadamard matrix by the Kronecker (Sylvester) recursion, with
+ *                 the 1/sqrt(2) factor per level, i.e. an orthonormal transform;
+ *           s2.2  the iterative in-place butterfly (half-width h = 1, 2, 4, ...) followed
+ *                 by division of every element by sqrt(n); the absmax k-bit quantiser with
+ *                 qmax = 2^(bits-1) - 1, round-to-nearest (numpy's, i.e. ties to even)
+ *                 and clipping to [-qmax, qmax];
+ *           s3.1  the transform applied blockwise to large matrices.
+ *   [HALO]  "HALO: Hadamard-Assisted Lower-Precision Optimization for LLMs"
+ *           abstract: Hadamard rotations in the forward and in the backward pass, and every
+ *           large matrix product of both passes computed in low precision;
+ *           method section, key design 2: the low-precision type is INT8 or FP8.
+ *
+ * Readings taken where the pages are garbled or silent (each is listed with its reason
+ * in the design notes of the repository):
+ *   - the quantiser's garbled expression is read as q = round(x * qmax / absmax);
+ *   - one scale per vector: the whole row (or column) along the contraction dimension;
+ *   - the transform is block-diagonal over contiguous blocks of `block` indices;
+ *   - FP8 uses the OCP formats E4M3FN (max 448) and E5M2 (max 57344) with qmax equal to
+ *     the format's largest finite value, round to nearest even, saturating;
+ *   - a zero vector gets scale 0 and all-zero codes.
+ *
+ * Two precisions are offered for the transform + quantisation step:
+ *   precision 64: fp64 butterflies, divide by sqrt(b), q = rne(y * qmax / a) with the
+ *                 quotient taken in long double (a real tie stays a tie).
+ *   precision 32: the same butterflies in fp32 (same stage and pairing order), the code
+ *                 decided in fp32 from the un-normalised butterfly output:
+ *                 m = fl32(qmax / a), q = rne(y * m) with the product taken exactly
+ *                 (INT8) or rounded to fp32 first (FP8).  The 1/sqrt(b) factor cancels
+ *                 between y and max|y| in exact arithmetic, so both are evaluations of
+ *                 the same formula; precision 32 is the one a single-precision device
+ *                 takes its integer decisions in.
+ *
+ * Build: gcc -O2 -fopenmp -ffp-contract=off -fPIC -shared (no fast-math).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* element types (the oracle's own numbering) */
+enum { OR_F32 = 0, OR_BF16 = 1, OR_I8 = 2, OR_E4M3 = 3, OR_E5M2 = 4, OR_F64 = 5 };
+/* axis */
+enum { OR_ROWS = 0, OR_COLS = 1 };
+/* status */
+enum { OR_OK = 0, OR_EARG = 1, OR_ENOMEM = 2 };
+
+/* ------------------------------------------------------------------------- */
+/* scalar helpers                                                             */
+/* ------------------------------------------------------------------------- */
+
+/* round half to even, written out (numpy's np.round semantics); long double keeps the
+ * quotients below exact enough that a real tie stays a tie */
+static long double rne(long double t)
+{
+    long double f = floorl(t);
+    long double d = t - f; /* exact */
+    if (d > 0.5L) return f + 1.0L;
+    if (d < 0.5L) return f;
+    return (fmodl(f, 2.0L) == 0.0L) ? f : f + 1.0L;
+}
+
+static double load_elem(const void* x, int xtype, int64_t idx)
+{
+    if (xtype == OR_F32) return (double)((const float*)x)[idx];
+    /* bf16: the upper 16 bits of an IEEE single */
+    uint32_t bits = (uint32_t)((const uint16_t*)x)[idx] << 16;
+    float f;
+    memcpy(&f, &bits, 4);
+    return (double)f;
+}
+
+/* ------------------------------------------------------------------------- */
+/* OCP FP8 codec (E4M3FN and E5M2), from the format definitions               */
+/* ------------------------------------------------------------------------- */
+
+typedef struct {
+    int mbits, bias;
+    double maxv;
+} fp8_fmt;
+
+static const fp8_fmt FMT_E4M3 = {3, 7, 448.0};
+static const fp8_fmt FMT_E5M2 = {2, 15, 57344.0};
+
+static const fp8_fmt* fmt_of(int t) { return t == OR_E4M3 ? &FMT_E4M3 : &FMT_E5M2; }
+
+/* Nearest-even encoding of a finite value, saturating to +-max. */
+static uint8_t fp8_encode(long double v, const fp8_fmt* f)
+{
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    long double a = fabsl(v);
+    int emin = 1 - f->bias; /* exponent of the smallest normal */
+    int e;
+    if (a < ldexpl(1.0L, emin)) {
+        e = emin; /* the subnormal range shares the smallest normal's quantum */
+    } else {
+        frexpl(a, &e);
+        e -= 1; /* a in [2^e, 2^(e+1)) */
+    }
+    long double quantum = ldexpl(1.0L, e - f->mbits);
+    long double r = rne(a / quantum) * quantum; /* exact: quantum is a power of two */
+    if (r > (long double)f->maxv) r = (long double)f->maxv;
+    if (r == 0.0L) return sign;
+    if (r < ldexpl(1.0L, emin)) {
+        int mant = (int)(r / ldexpl(1.0L, emin - f->mbits));
+        return (uint8_t)(sign | mant);
+    }
+    int er;
+    frexpl(r, &er);
+    er -= 1;
+    int mant = (int)((r / ldexpl(1.0L, er) - 1.0L) * (long double)(1 << f->mbits));
+    return (uint8_t)(sign | ((er + f->bias) << f->mbits) | mant);
+}
+
+/* Exact decode; NaN codes decode to NaN, E5M2 infinities to +-inf. */
+static double fp8_decode(uint8_t c, const fp8_fmt* f)
+{
+    int ebits = 7 - f->mbits;
+    int ex = (c >> f->mbits) & ((1 << ebits) - 1);
+    int mant = c & ((1 << f->mbits) - 1);
+    double s = (c & 0x80) ? -1.0 : 1.0;
+    if (f == &FMT_E4M3 && ex == 15 && mant == 7) return NAN;
+    if (f == &FMT_E5M2 && ex == 31) return mant == 0 ? s * INFINITY : NAN;
+    if (ex == 0) return s * ldexp((double)mant, 1 - f->bias - f->mbits);
+    return s * ldexp(1.0 + (double)mant / (double)(1 << f->mbits), ex - f->bias);
+}
+
+uint8_t hor_fp8_encode(double v, int fmt) { return fp8_encode((long double)v, fmt_of(fmt)); }
+double hor_fp8_decode(uint8_t c, int fmt) { return fp8_decode(c, fmt_of(fmt)); }
+
+/* ------------------------------------------------------------------------- */
+/* Walsh-Hadamard transform: [QWHA] s2.2 butterfly, blockwise per s3.1        */
+/* ------------------------------------------------------------------------- */
+
+/* One block of length b (a power of two), fp64: butterflies, then divide by sqrt(b). */
+static void fwht_block_f64(double* v, int64_t b)
+{
+    for (int64_t h = 1; h < b; h *= 2) {
+        for (int64_t i = 0; i < b; i += 2 * h) {
+            for (int64_t t = i; t < i + h; ++t) {
+                double p = v[t], q = v[t + h];
+                v[t] = p + q;
+                v[t + h] = p - q;
+            }
+        }
+    }
+    double root = sqrt((double)b);
+    for (int64_t t = 0; t < b; ++t) v[t] = v[t] / root;
+}
+
+/* The same butterflies in fp32, without the final normalisation. */
+static void fwht_block_f32_unnorm(float* v, int64_t b)
+{
+    for (int64_t h = 1; h < b; h *= 2) {
+        for (int64_t i = 0; i < b; i += 2 * h) {
+            for (int64_t t = i; t < i + h; ++t) {
+                float p = v[t], q = v[t + h];
+                v[t] = p + q;
+                v[t + h] = p - q;
+            }
+        }
+    }
+}
+
+/* malloc size for n elements, never zero */
+static size_t nz(int64_t n) { return (size_t)(n > 0 ? n : 1); }
+
+static int is_pow2(int64_t b) { return b >= 1 && (b & (b - 1)) == 0; }
+
+/* In-place blockwise orthonormal transform of a contiguous fp64 vector. */
+int hor_fwht_f64(double* v, int64_t len, int64_t block)
+{
+    if (!v || !is_pow2(block) || len < 0 || len % block) return OR_EARG;
+    for (int64_t j = 0; j < len; j += block) fwht_block_f64(v + j, block);
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Quantisation of one rotated vector ([QWHA] s2.2 quantiser)                 */
+/* ------------------------------------------------------------------------- */
+
+static double qmax_of(int qtype)
+{
+    if (qtype == OR_I8) return 127.0;
+    if (qtype == OR_E4M3) return 448.0;
+    return 57344.0; /* E5M2 */
+}
+
+/* fp64: y holds the normalised rotated vector. */
+static void quant_vec_f64(const double* y, int64_t L, int qtype, void* q, double* scale)
+{
+    double a = 0.0;
+    for (int64_t i = 0; i < L; ++i)
+        if (fabs(y[i]) > a) a = fabs(y[i]);
+    double qmax = qmax_of(qtype);
+    if (qtype == OR_F64) {
+        memcpy(q, y, (size_t)L * sizeof(double));
+        *scale = a;
+        return;
+    }
+    if (a == 0.0) {
+        memset(q, 0, (size_t)L);
+        *scale = 0.0;
+        return;
+    }
+    for (int64_t i = 0; i < L; ++i) {
+        /* y * qmax is exact in long double; the quotient is rounded once, at 64 bits */
+        long double t = (long double)y[i] * (long double)qmax / (long double)a;
+        if (qtype == OR_I8) {
+            long double n = rne(t);
+            if (n > 127.0L) n = 127.0L;
+            if (n < -127.0L) n = -127.0L;
+            ((int8_t*)q)[i] = (int8_t)n;
+        } else {
+            ((uint8_t*)q)[i] = fp8_encode(t, fmt_of(qtype));
+        }
+    }
+    *scale = a / qmax;
+}
+
+/* fp32: yu holds the un-normalised butterfly output of every block of the vector. */
+static void quant_vec_f32(const float* yu, int64_t L, int64_t block, int qtype, void* q,
+                          double* scale)
+{
+    float a = 0.0f;
+    for (int64_t i = 0; i < L; ++i)
+        if (fabsf(yu[i]) > a) a = fabsf(yu[i]);
+    if (qtype == OR_F64) {
+        float r = (float)(1.0 / sqrt((double)block));
+        for (int64_t i = 0; i < L; ++i) ((double*)q)[i] = (double)(yu[i] * r);
+        *scale = (double)(a * r);
+        return;
+    }
+    float qmax = (float)qmax_of(qtype);
+    float denom = (float)((double)qmax * sqrt((double)block));
+    if (a == 0.0f) {
+        memset(q, 0, (size_t)L);
+        *scale = 0.0;
+        return;
+    }
+    float m = qmax / a;
+    for (int64_t i = 0; i < L; ++i) {
+        if (qtype == OR_I8) {
+            long double n = rne((long double)yu[i] * (long double)m); /* exact product */
+            if (n > 127.0L) n = 127.0L;
+            if (n < -127.0L) n = -127.0L;
+            ((int8_t*)q)[i] = (int8_t)n;
+        } else {
+            float t = yu[i] * m; /* rounded to fp32, then to the fp8 grid */
+            ((uint8_t*)q)[i] = fp8_encode((long double)t, fmt_of(qtype));
+        }
+    }
+    *scale = (double)(a / denom);
+}
+
+/*
+ * Rotate + quantise vectors of a row-major matrix x[rows x cols] (leading dimension ldx).
+ *   axis OR_ROWS: vector r is row r, length L = cols.
+ *   axis OR_COLS: vector c is column c, length L = rows.
+ * vec_idx (may be NULL = all vectors, in order) selects nvec vectors.
+ * q receives nvec x L codes, vector-major (int8, fp8 bytes, or doubles for OR_F64 = the
+ * normalised rotated values); scale receives nvec scales (absmax/qmax; for OR_F64 the
+ * absmax of the normalised vector).
+ */
+int hor_fwht_quant(const void* x, int xtype, int64_t rows, int64_t cols, int64_t ldx, int axis,
+                   int64_t block, int qtype, int precision, const int64_t* vec_idx,
+                   int64_t nvec, void* q, double* scale)
+{
+    if (!x || !q || !scale) return OR_EARG;
+    if (xtype != OR_F32 && xtype != OR_BF16) return OR_EARG;
+    if (qtype != OR_I8 && qtype != OR_E4M3 && qtype != OR_E5M2 && qtype != OR_F64) return OR_EARG;
+    if (precision != 32 && precision != 64) return OR_EARG;
+    if (rows < 0 || cols < 0 || ldx < cols) return OR_EARG;
+    int64_t L = axis == OR_ROWS ? cols : rows;
+    int64_t total = axis == OR_ROWS ? rows : cols;
+    if (!is_pow2(block) || (L > 0 && L % block)) return OR_EARG;
+    if (nvec < 0 || (!vec_idx && nvec > total)) return OR_EARG;
+    for (int64_t v = 0; vec_idx && v < nvec; ++v)
+        if (vec_idx[v] < 0 || vec_idx[v] >= total) return OR_EARG;
+    size_t qbytes = qtype == OR_F64 ? sizeof(double) : 1;
+    int err = OR_OK;
+
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t v = 0; v < nvec; ++v) {
+        int64_t id = vec_idx ? vec_idx[v] : v;
+        void* qv = (char*)q + (size_t)v * (size_t)L * qbytes;
+        if (precision == 64) {
+            double* y = (double*)malloc(nz(L) * sizeof(double));
+            if (!y) { err = OR_ENOMEM; continue; }
+            for (int64_t i = 0; i < L; ++i)
+                y[i] = axis == OR_ROWS ? load_elem(x, xtype, id * ldx + i)
+                                       : load_elem(x, xtype, i * ldx + id);
+            for (int64_t i = 0; i < L; ++i)
+                if (!isfinite(y[i])) abort(); /* non-finite input is outside the method */
+            for (int64_t j = 0; j < L; j += block) fwht_block_f64(y + j, block);
+            quant_vec_f64(y, L, qtype, qv, &scale[v]);
+            free(y);
+        } else {
+            float* y = (float*)malloc(nz(L) * sizeof(float));
+            if (!y) { err = OR_ENOMEM; continue; }
+            for (int64_t i = 0; i < L; ++i)
+                y[i] = (float)(axis == OR_ROWS ? load_elem(x, xtype, id * ldx + i)
+                                               : load_elem(x, xtype, i * ldx + id));
+            for (int64_t j = 0; j < L; j += block) fwht_block_f32_unnorm(y + j, block);
+            quant_vec_f32(y, L, block, qtype, qv, &scale[v]);
+            free(y);
+        }
+    }
+    return err;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Low-precision products ([HALO] abstract: every large matmul in low precision) */
+/* ------------------------------------------------------------------------- */
+
+/* acc[i,j] = sum_k a[i,k] * b[j,k] in int64 (a: m x k, b: n x k, both k-contiguous). */
+int hor_gemm_i8(const int8_t* a, const int8_t* b, int64_t m, int64_t n, int64_t k, int64_t* acc)
+{
+    if ((!a && m * k != 0) || (!b && n * k != 0) || (!acc && m * n != 0) || m < 0 || n < 0 || k < 0) return OR_EARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < m; ++i)
+        for (int64_t j = 0; j < n; ++j) {
+            int64_t s = 0;
+            for (int64_t t = 0; t < k; ++t) s += (int64_t)a[i * k + t] * (int64_t)b[j * k + t];
+            acc[i * n + j] = s;
+        }
+    return OR_OK;
+}
+
+/* out[i,j] = sum_k dec(a[i,k]) * dec(b[j,k]) in fp64. */
+int hor_gemm_fp8(const uint8_t* a, int afmt, const uint8_t* b, int bfmt, int64_t m, int64_t n,
+                 int64_t k, double* out)
+{
+    if ((!a && m * k != 0) || (!b && n * k != 0) || (!out && m * n != 0) || m < 0 || n < 0 || k < 0) return OR_EARG;
+    if ((afmt != OR_E4M3 && afmt != OR_E5M2) || (bfmt != OR_E4M3 && bfmt != OR_E5M2)) return OR_EARG;
+    const fp8_fmt* fa = fmt_of(afmt);
+    const fp8_fmt* fb = fmt_of(bfmt);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < m; ++i)
+        for (int64_t j = 0; j < n; ++j) {
+            double s = 0.0;
+            for (int64_t t = 0; t < k; ++t)
+                s += fp8_decode(a[i * k + t], fa) * fp8_decode(b[j * k + t], fb);
+            out[i * n + j] = s;
+        }
+    return OR_OK;
+}
+
+/* Exact fp64 product out = A B^T (A: m x k, B: n x k); the unquantised reference. */
+int hor_matmul_f64(const double* a, const double* b, int64_t m, int64_t n, int64_t k, double* out)
+{
+    if ((!a && m * k != 0) || (!b && n * k != 0) || (!out && m * n != 0)) return OR_EARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < m; ++i)
+        for (int64_t j = 0; j < n; ++j) {
+            double s = 0.0;
+            for (int64_t t = 0; t < k; ++t) s += a[i * k + t] * b[j * k + t];
+            out[i * n + j] = s;
+        }
+    return OR_OK;
+}
+
+/* out[i,j] = acc[i,j] * sa[i] * sb[j] in fp64 (the scale dequant). */
+void hor_dequant(const double* acc, const double* sa, const double* sb, int64_t m, int64_t n,
+                 double* out)
+{
+    for (int64_t i = 0; i < m; ++i)
+        for (int64_t j = 0; j < n; ++j) out[i * n + j] = acc[i * n + j] * sa[i] * sb[j];
+}
+
+/* ------------------------------------------------------------------------- */
+/* The layer: quantise both operands along the contraction dim, multiply,     */
+/* dequantise.                                                               */
+/* ------------------------------------------------------------------------- */
+
+/* C[p x q] = dequant(Qa[p x L] . Qb[q x L]^T) for codes of one type pair. */
+static int lowp_product(const void* qa, int ta, const double* sa, const void* qb, int tb,
+                        const double* sb, int64_t p, int64_t qn, int64_t L, double* out)
+{
+    double* acc = (double*)malloc(nz(p * qn) * sizeof(double));
+    if (!acc) return OR_ENOMEM;
+    int rc;
+    if (ta == OR_I8) {
+        int64_t* iacc = (int64_t*)malloc(nz(p * qn) * sizeof(int64_t));
+        if (!iacc) { free(acc); return OR_ENOMEM; }
+        rc = hor_gemm_i8((const int8_t*)qa, (const int8_t*)qb, p, qn, L, iacc);
+        for (int64_t i = 0; i < p * qn; ++i) acc[i] = (double)iacc[i];
+        free(iacc);
+    } else {
+        rc = hor_gemm_fp8((const uint8_t*)qa, ta, (const uint8_t*)qb, tb, p, qn, L, acc);
+    }
+    if (rc == OR_OK) hor_dequant(acc, sa, sb, p, qn, out);
+    free(acc);
+    return rc;
+}
+
+/* One low-precision product along one contraction dimension:
+ * out = dequant(Q(A along L) Q(B along L)^T), where each operand is a row-major matrix
+ * given with its axis (the vectors quantised are rows or columns of it). */
+static int rotated_product(const void* a, int64_t ar, int64_t ac, int aaxis, int qa_t,
+                           const void* b, int64_t br, int64_t bc, int baxis, int qb_t,
+                           int xtype, int64_t block, int precision, double* out)
+{
+    int64_t p = aaxis == OR_ROWS ? ar : ac;
+    int64_t L = aaxis == OR_ROWS ? ac : ar;
+    int64_t qn = baxis == OR_ROWS ? br : bc;
+    void* qa = malloc(nz(p * L));
+    void* qb = malloc(nz(qn * L));
+    double* sa = (double*)malloc(nz(p) * sizeof(double));
+    double* sb = (double*)malloc(nz(qn) * sizeof(double));
+    int rc = OR_ENOMEM;
+    if (qa && qb && sa && sb) {
+        rc = hor_fwht_quant(a, xtype, ar, ac, ac, aaxis, block, qa_t, precision, NULL, p, qa, sa);
+        if (rc == OR_OK)
+            rc = hor_fwht_quant(b, xtype, br, bc, bc, baxis, block, qb_t, precision, NULL, qn, qb, sb);
+        if (rc == OR_OK) rc = lowp_product(qa, qa_t, sa, qb, qb_t, sb, p, qn, L, out);
+    }
+    free(qa); free(qb); free(sa); free(sb);
+    return rc;
+}
+
+/* Forward: Y[m x n] = X[m x k] W[n x k]^T, both rotated and quantised along k. */
+int hor_linear_fwd(const void* x, const void* w, int xtype, int64_t m, int64_t n, int64_t k,
+                   int64_t block, int qtype, int precision, double* y)
+{
+    if (!x || !w || !y || qtype == OR_F64) return OR_EARG;
+    return rotated_product(x, m, k, OR_ROWS, qtype, w, n, k, OR_ROWS, qtype, xtype, block,
+                           precision, y);
+}
+
+/* Backward: dX[m x k] = dY[m x n] W[n x k]   (contraction over n),
+ *           dW[n x k] = dY^T X               (contraction over m).
+ * dY is quantised with grad_qtype, X and W with qtype.  Either output may be NULL. */
+int hor_linear_bwd(const void* dy, const void* x, const void* w, int xtype, int64_t m, int64_t n,
+                   int64_t k, int64_t block, int qtype, int grad_qtype, int precision,
+                   double* dx, double* dw)
+{
+    if (!dy || !x || !w || qtype == OR_F64 || grad_qtype == OR_F64) return OR_EARG;
+    int rc = OR_OK;
+    if (dx) /* A = rows of dY (length n), B = columns of W (length n) */
+        rc = rotated_product(dy, m, n, OR_ROWS, grad_qtype, w, n, k, OR_COLS, qtype, xtype, block,
+                             precision, dx);
+    if (rc == OR_OK && dw) /* A = columns of dY (length m), B = columns of X (length m) */
+        rc = rotated_product(dy, m, n, OR_COLS, grad_qtype, x, m, k, OR_COLS, qtype, xtype, block,
+                             precision, dw);
+    return rc;
+}
+
+int hor_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
