@@ -1,0 +1,192 @@
+"""Python binding of libhalo.so, the MI355X Hadamard-rotated low-precision linear layer.
+
+Argument marshalling only: torch tensors supply device pointers and the current HIP stream;
+every step of the computation runs in the library's gfx950 kernels.  The library must be
+built (``python -m hadamard_rotated_precision_halo_amd.build``); importing the functions below
+without it raises immediately -- there is no fallback path.
+
+Method: "HALO: Hadamard-Assisted Lower-Precision Optimization for LLMs" (abstract: rotations
+in the forward and backward pass, all large products in 8 bits; key design 2: INT8 or FP8),
+with the orthonormal Walsh-Hadamard transform and absmax quantiser of
+"QWHA方法：基于Walsh-Hadamard变换的高效大模型微调技术" s2.1-s2.2, applied blockwise (s3.1).
+"""
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhalo.so")
+
+# halo_dtype / halo_axis / halo_status values of include/halo.h
+F32, BF16, I8, E4M3, E5M2, I32 = range(6)
+ROWS, COLS = 0, 1
+STATUS = {0: "HALO_OK", 1: "HALO_ERR_NULL", 2: "HALO_ERR_SHAPE", 3: "HALO_ERR_BLOCK",
+          4: "HALO_ERR_DTYPE", 5: "HALO_ERR_ALIGN", 6: "HALO_ERR_WORKSPACE", 7: "HALO_ERR_HIP"}
+
+EXPORTS = ("halo_fwht_quant", "halo_gemm_i8", "halo_gemm_fp8", "halo_linear_workspace_bytes",
+           "halo_linear_fwd", "halo_linear_bwd", "halo_status_str")
+
+_TORCH_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.int8: I8,
+               torch.float8_e4m3fn: E4M3, torch.float8_e5m2: E5M2, torch.int32: I32}
+
+
+class HaloError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({_status_str(status)})")
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libhalo.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run "
+                              "`python -m hadamard_rotated_precision_halo_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, vp, i32, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        e = ctypes.c_int  # enums
+        L.halo_fwht_quant.argtypes = [vp, e, i64, i64, i64, e, i32, e, vp, i64, vp, vp]
+        L.halo_gemm_i8.argtypes = [vp, i64, vp, vp, i64, vp, i64, i64, i64, vp, e, i64, vp]
+        L.halo_gemm_fp8.argtypes = [vp, e, i64, vp, vp, e, i64, vp, i64, i64, i64, vp, e, i64, vp]
+        L.halo_linear_workspace_bytes.argtypes = [i64, i64, i64, e, ctypes.c_int]
+        L.halo_linear_workspace_bytes.restype = sz
+        L.halo_linear_fwd.argtypes = [vp, vp, e, i64, i64, i64, i32, e, vp, e, vp, sz, vp]
+        L.halo_linear_bwd.argtypes = [vp, vp, vp, e, i64, i64, i64, i32, e, e, vp, vp, vp, sz, vp]
+        L.halo_status_str.argtypes = [e]
+        L.halo_status_str.restype = ctypes.c_char_p
+        for f in ("halo_fwht_quant", "halo_gemm_i8", "halo_gemm_fp8", "halo_linear_fwd",
+                  "halo_linear_bwd"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _status_str(s):
+    try:
+        return lib().halo_status_str(int(s)).decode()
+    except Exception:  # pragma: no cover
+        return "?"
+
+
+def _code(dtype):
+    try:
+        return _TORCH_CODE[dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {dtype}") from None
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(status, what):
+    if status != 0:
+        raise HaloError(status, what)
+
+
+def _ld(t):
+    assert t.dim() == 2, "matrices are 2-D"
+    if t.numel() == 0:  # an empty matrix has no meaningful stride; any aligned value works
+        return max(t.shape[1], 16)
+    assert t.stride(1) == 1, "matrices must be row-major with unit column stride"
+    return t.stride(0)
+
+
+def fwht_quant(x, axis=ROWS, block=256, q_dtype=torch.int8, q=None, scale=None, stream=None):
+    """Rotate + quantise the rows (axis ROWS) or columns (axis COLS) of x.
+
+    Returns (q, scale): q is [rows x cols] (ROWS) or [cols x rows] (COLS) of q_dtype
+    (torch.int8 / float8_e4m3fn / float8_e5m2, or torch.float32 for the rotated values
+    themselves), scale is float32 with one entry per vector.
+    """
+    rows, cols = x.shape
+    nvec, L = (rows, cols) if axis == ROWS else (cols, rows)
+    if q is None:
+        q = torch.empty((nvec, L), dtype=q_dtype, device=x.device)
+    if scale is None:
+        scale = torch.empty(nvec, dtype=torch.float32, device=x.device)
+    st = lib().halo_fwht_quant(_ptr(x), _code(x.dtype), rows, cols, _ld(x), axis, int(block),
+                               _code(q.dtype), _ptr(q), _ld(q), _ptr(scale), _stream(stream))
+    _check(st, "halo_fwht_quant")
+    return q, scale
+
+
+def gemm_i8(a, sa, b, sb, out_dtype=torch.bfloat16, c=None, stream=None):
+    """c = (a . b^T) * sa[:, None] * sb[None, :] with int8 codes (int32 raw if out is int32)."""
+    m, k = a.shape
+    n = b.shape[0]
+    if c is None:
+        c = torch.empty((m, n), dtype=out_dtype, device=a.device)
+    st = lib().halo_gemm_i8(_ptr(a), _ld(a), _ptr(sa), _ptr(b), _ld(b), _ptr(sb), m, n, k,
+                            _ptr(c), _code(c.dtype), _ld(c), _stream(stream))
+    _check(st, "halo_gemm_i8")
+    return c
+
+
+def gemm_fp8(a, sa, b, sb, out_dtype=torch.bfloat16, c=None, stream=None):
+    """c = (dec(a) . dec(b)^T) * sa[:, None] * sb[None, :] with fp8 codes (E4M3 / E5M2)."""
+    m, k = a.shape
+    n = b.shape[0]
+    if c is None:
+        c = torch.empty((m, n), dtype=out_dtype, device=a.device)
+    st = lib().halo_gemm_fp8(_ptr(a), _code(a.dtype), _ld(a), _ptr(sa), _ptr(b), _code(b.dtype),
+                             _ld(b), _ptr(sb), m, n, k, _ptr(c), _code(c.dtype), _ld(c),
+                             _stream(stream))
+    _check(st, "halo_gemm_fp8")
+    return c
+
+
+def linear_workspace_bytes(m, n, k, q_dtype=torch.int8, backward=False):
+    return int(lib().halo_linear_workspace_bytes(m, n, k, _code(q_dtype), 1 if backward else 0))
+
+
+def _workspace(nbytes, device, ws):
+    if ws is None:
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    return ws
+
+
+def linear_fwd(x, w, block, q_dtype=torch.int8, y=None, y_dtype=None, workspace=None,
+               stream=None):
+    """Y = X W^T with both operands rotated and quantised along K (the layer's forward)."""
+    m, k = x.shape
+    n = w.shape[0]
+    if y is None:
+        y = torch.empty((m, n), dtype=y_dtype or x.dtype, device=x.device)
+    need = linear_workspace_bytes(m, n, k, q_dtype, False)
+    ws = _workspace(need, x.device, workspace)
+    st = lib().halo_linear_fwd(_ptr(x), _ptr(w), _code(x.dtype), m, n, k, int(block),
+                               _code(q_dtype), _ptr(y), _code(y.dtype), _ptr(ws),
+                               ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "halo_linear_fwd")
+    return y
+
+
+def linear_bwd(dy, x, w, block, q_dtype=torch.int8, grad_q_dtype=None, want_dx=True,
+               want_dw=True, dx=None, dw=None, workspace=None, stream=None):
+    """dX = dY W (rotated along N) and dW = dY^T X (rotated along M), 8-bit products."""
+    m, k = x.shape
+    n = w.shape[0]
+    grad_q_dtype = grad_q_dtype or q_dtype
+    if want_dx and dx is None:
+        dx = torch.empty((m, k), dtype=x.dtype, device=x.device)
+    if want_dw and dw is None:
+        dw = torch.empty((n, k), dtype=x.dtype, device=x.device)
+    need = linear_workspace_bytes(m, n, k, q_dtype, True)
+    ws = _workspace(need, x.device, workspace)
+    st = lib().halo_linear_bwd(_ptr(dy), _ptr(x), _ptr(w), _code(x.dtype), m, n, k, int(block),
+                               _code(q_dtype), _code(grad_q_dtype),
+                               _ptr(dx) if want_dx else None, _ptr(dw) if want_dw else None,
+                               _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "halo_linear_bwd")
+    return (dx if want_dx else None), (dw if want_dw else None)

@@ -1,0 +1,121 @@
+// halo_device.h -- gfx950 device helpers shared by the rotation and GEMM kernels.
+//
+// Lane exchanges for the cross-lane butterfly stages, bf16/fp32 unpacking, and the 8-bit
+// encoders.  Every exchange pairs lane l with lane l ^ (1 << s) inside a wave64.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace halo {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// ---------------------------------------------------------------------------
+// element loads
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ void unpack_bf16x8(uint4 w, float* o) {
+  o[0] = __uint_as_float(w.x << 16);
+  o[1] = __uint_as_float(w.x & 0xffff0000u);
+  o[2] = __uint_as_float(w.y << 16);
+  o[3] = __uint_as_float(w.y & 0xffff0000u);
+  o[4] = __uint_as_float(w.z << 16);
+  o[5] = __uint_as_float(w.z & 0xffff0000u);
+  o[6] = __uint_as_float(w.w << 16);
+  o[7] = __uint_as_float(w.w & 0xffff0000u);
+}
+
+// 8 consecutive elements (16 B of bf16 or 32 B of fp32) starting at p.
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float* o);
+
+template <>
+__device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float* o) {
+  unpack_bf16x8(*reinterpret_cast<const uint4*>(p), o);
+}
+
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float* o) {
+  float4 a = reinterpret_cast<const float4*>(p)[0];
+  float4 b = reinterpret_cast<const float4*>(p)[1];
+  o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+  o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+}
+
+// ---------------------------------------------------------------------------
+// cross-lane partner values
+// ---------------------------------------------------------------------------
+
+// Value held by lane (l ^ (1 << S)).  S = 0, 1: DPP quad permutations; S = 2, 3, 4:
+// ds_swizzle in bit mode (xor within 32 lanes); S = 5: permlane32 swap.
+template <int S>
+__device__ __forceinline__ float partner(float v) {
+  int i = __float_as_int(v);
+  if constexpr (S == 0) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, i, 0xB1, 0xF, 0xF, false));
+  } else if constexpr (S == 1) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, i, 0x4E, 0xF, 0xF, false));
+  } else if constexpr (S == 2) {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(i, 0x101F));
+  } else if constexpr (S == 3) {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(i, 0x201F));
+  } else if constexpr (S == 4) {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(i, 0x401F));
+  } else {
+    static_assert(S == 5, "lane exchange stage out of range");
+    auto r = __builtin_amdgcn_permlane32_swap(i, i, false, false);
+    // lanes 0-31 receive lanes 32-63 in r[1]; lanes 32-63 receive lanes 0-31 in r[0]
+    return __int_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+  }
+}
+
+// One butterfly stage across lanes: the lane whose bit S is clear holds the lower index p
+// and becomes p + q; its partner holds q and becomes p - q.  `c` is +1 on the lower lane and
+// -1 on the upper one, so one fma gives v + o or o - v with a single rounding each -- the
+// same association as an in-register butterfly, hence bit-identical to a sequential fp32
+// butterfly.
+template <int S>
+__device__ __forceinline__ float xbutterfly(float v, float c) {
+  return __builtin_fmaf(c, v, partner<S>(v));
+}
+
+template <int S>
+__device__ __forceinline__ float xmax(float v) {
+  return fmaxf(v, partner<S>(v));
+}
+
+// ---------------------------------------------------------------------------
+// encoders
+// ---------------------------------------------------------------------------
+
+// Round-to-nearest-even of y * m for |y * m| <= 2^22, returned as the int8 bit pattern in the
+// low byte: fma adds 1.5 * 2^23 to the exact product and rounds once, leaving the integer in
+// the low mantissa bits.
+__device__ __forceinline__ uint32_t i8_code(float y, float m) {
+  return __float_as_uint(__builtin_fmaf(y, m, 12582912.0f)) & 0xffu;
+}
+
+__device__ __forceinline__ uint32_t pack4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  return a | (b << 8) | (c << 16) | (d << 24);
+}
+
+// Two fp32 values to two OCP FP8 codes (round to nearest even), placed in the low 16 bits.
+template <int FMT>  // 0: E4M3, 1: E5M2
+__device__ __forceinline__ uint32_t fp8_pair(float a, float b) {
+  if constexpr (FMT == 0)
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;
+  else
+    return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false) & 0xffffu;
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+}  // namespace halo

@@ -1,0 +1,47 @@
+// halo_kernels.h -- internal launch interface between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace halo {
+
+// Arguments of one fused rotation + quantisation pass.
+struct FqArgs {
+  const void* x;       // input, row-major [rows x cols], leading dim ldx (elements)
+  int64_t ldx;
+  int64_t nvec;        // number of vectors (rows for the rows axis, cols for the cols axis)
+  int64_t len;         // rotated length L
+  void* q;             // codes [nvec x L], leading dim ldq (elements)
+  int64_t ldq;
+  float* scale;        // [nvec]
+  int64_t vec_per_wg;  // rows kernel: vectors per workgroup (set by the launcher)
+  int block;
+  float qmax;          // 127, 448, 57344
+  float denom;         // fl32(qmax * sqrt(block)): scale = max|b| / denom
+  float inv_sqrt_b;    // fl32(1 / sqrt(block)) for the fp32 test mode
+};
+
+// in_bf16: 1 for bf16 input, 0 for fp32.  qt: 0 INT8, 1 E4M3, 2 E5M2, 3 fp32 values.
+// axis: 0 rows, 1 cols.
+hipError_t launch_fwht_quant(const FqArgs& a, int in_bf16, int qt, int axis, hipStream_t st);
+
+// Longest row the single-pass rows kernel takes for this block size.
+int64_t fq_rows_max_len(int block);
+
+struct GemmArgs {
+  const void* a;  // [m x k], lda (bytes = elements)
+  int64_t lda;
+  const void* b;  // [n x k], ldb
+  int64_t ldb;
+  const float* sa;
+  const float* sb;
+  void* c;        // [m x n], ldc (elements)
+  int64_t ldc;
+  int64_t m, n, k;
+};
+
+// kind: 0 INT8, 1 FP8.  afmt/bfmt (FP8 only): 0 E4M3, 1 E5M2.  out: 0 int32, 1 fp32, 2 bf16.
+hipError_t launch_gemm(const GemmArgs& g, int kind, int afmt, int bfmt, int out, hipStream_t st);
+
+}  // namespace halo

@@ -1,0 +1,172 @@
+/*
+ * halo.h -- C ABI of libhalo.so: the Hadamard-rotated low-precision linear layer on
+ * MI355X (gfx950).
+ *
+ * The method ("HALO: Hadamard-Assisted Lower-Precision Optimization for LLMs", abstract and
+ * method section): every large matrix product of a linear layer's forward and backward pass
+ * runs in 8-bit precision (INT8 or FP8, key design 2) after a Hadamard rotation of both
+ * operands along the contraction dimension, which spreads outlier channels.  The rotation
+ * is the orthonormal Walsh-Hadamard transform in natural (Sylvester) order, applied to
+ * contiguous blocks of `block` indices ("QWHA方法：基于Walsh-Hadamard变换的高效大模型微调技术",
+ * s2.1 definition, s2.2 butterfly and 1/sqrt(n), s3.1 blockwise); every rotated vector is
+ * quantised with its own absmax scale (s2.2 quantiser, ties to even).  Because the rotation
+ * is orthogonal, (X H)(W H)^T = X W^T, so the dequantised product approximates the plain one.
+ *
+ * Conventions shared by every entry point
+ *   - Matrices are row-major with an explicit leading dimension (in elements).
+ *   - Every pointer is DEVICE memory owned by the caller.  The library never allocates,
+ *     frees or synchronises; work is enqueued on `stream` (a hipStream_t; NULL = the
+ *     default stream) and the call returns once it is enqueued.
+ *   - A pointer may be NULL only when the matrix it describes is empty (a zero size).
+ *   - All arguments are validated on the host before anything is launched.  On any error
+ *     the call returns a non-zero status, launches nothing and writes no output.  A failed
+ *     launch returns HALO_ERR_HIP.  Nothing is printed and no global state is kept, so calls
+ *     are thread-safe; calls on one stream run in order.
+ *   - Alignment: every pointer 16-byte aligned, every leading dimension a multiple of 16
+ *     bytes (HALO_ERR_ALIGN otherwise).
+ *   - Scales are fp32 dequant multipliers: the vector's absmax after the orthonormal
+ *     rotation divided by qmax (127 for INT8, 448 for E4M3, 57344 for E5M2).  A zero vector
+ *     gets scale 0 and all-zero codes.
+ *   - FP8 is the OCP format pair E4M3 ("FN": max 448, no infinities) and E5M2 (max 57344);
+ *     codes are rounded to nearest even and never exceed the format's largest finite value.
+ */
+#ifndef HALO_H
+#define HALO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    HALO_OK = 0,
+    HALO_ERR_NULL = 1,      /* a required pointer is NULL                                  */
+    HALO_ERR_SHAPE = 2,     /* a size is negative, too large, or not a supported multiple  */
+    HALO_ERR_BLOCK = 3,     /* block not a power of two in [1, 4096] or not dividing the   */
+                            /* rotated length                                              */
+    HALO_ERR_DTYPE = 4,     /* unsupported element type or type pair                      */
+    HALO_ERR_ALIGN = 5,     /* pointer or leading dimension not 16-byte aligned            */
+    HALO_ERR_WORKSPACE = 6, /* workspace NULL or smaller than the size query returns       */
+    HALO_ERR_HIP = 7        /* the HIP runtime refused a launch                            */
+} halo_status;
+
+typedef enum {
+    HALO_F32 = 0,  /* IEEE binary32                                      */
+    HALO_BF16 = 1, /* bfloat16                                           */
+    HALO_I8 = 2,   /* signed 8-bit integer codes in [-127, 127]         */
+    HALO_E4M3 = 3, /* OCP FP8 E4M3FN codes                              */
+    HALO_E5M2 = 4, /* OCP FP8 E5M2 codes                                */
+    HALO_I32 = 5   /* signed 32-bit integer (raw INT8 GEMM accumulators) */
+} halo_dtype;
+
+typedef enum {
+    HALO_ALONG_ROWS = 0, /* vectors are the rows: rotate the contiguous dimension        */
+    HALO_ALONG_COLS = 1  /* vectors are the columns: rotate the strided dimension; the   */
+                         /* codes are written transposed, one row per column             */
+} halo_axis;
+
+/*
+ * Rotate and quantise every vector of x[rows x cols] (leading dimension ldx).
+ *
+ * Defined by: the blockwise orthonormal Walsh-Hadamard transform of each vector (QWHA page
+ * s2.1-s2.2, s3.1) followed by the per-vector absmax quantiser (s2.2), i.e. for a vector v
+ * of length L:  y = v (I_{L/block} (x) H_block) / sqrt(block),  a = max|y|,
+ * code = round_to_nearest_even(y * qmax / a),  scale = a / qmax.
+ *
+ *   x_type   HALO_F32 or HALO_BF16.
+ *   axis     HALO_ALONG_ROWS: vector r = x[r, :], L = cols; q is [rows x cols] (ldq >= cols)
+ *                             and scale has `rows` entries.
+ *            HALO_ALONG_COLS: vector c = x[:, c], L = rows; q is [cols x rows] (ldq >= rows),
+ *                             i.e. the codes of column c form row c of q; scale has `cols`
+ *                             entries.  cols must be a multiple of 8.
+ *   block    power of two in [1, 4096] dividing L; L must be a multiple of 8.  block 1 is the
+ *            identity (plain per-vector absmax quantisation).
+ *   q_type   HALO_I8, HALO_E4M3, HALO_E5M2: 1-byte codes.
+ *            HALO_F32: test mode, q receives the rotated values themselves (fp32) and scale
+ *            the absmax of each rotated vector.
+ *   ldq      leading dimension of q in elements.
+ * Rows-axis vectors are limited to L <= 16384 elements (one workgroup holds a whole row).
+ * Codes are decided in fp32: m = qmax / max|b| with b the un-normalised butterfly output and
+ * code = round(b * m); the 1/sqrt(block) factor cancels between b and max|b|.
+ */
+halo_status halo_fwht_quant(const void* x, halo_dtype x_type, int64_t rows, int64_t cols,
+                            int64_t ldx, halo_axis axis, int32_t block, halo_dtype q_type,
+                            void* q, int64_t ldq, float* scale, void* stream);
+
+/*
+ * INT8 product with wide accumulation and a fused scale dequant ("HALO: Hadamard-Assisted
+ * Lower-Precision Optimization for LLMs", abstract: all large products in low precision):
+ *   acc[i, j] = sum_t a[i, t] * b[j, t]   (int32; exact for k <= 133144 with |codes| <= 127)
+ *   c[i, j]   = acc[i, j] * sa[i] * sb[j] (c_type HALO_F32 or HALO_BF16, rounded to nearest even)
+ *   c[i, j]   = acc[i, j]                 (c_type HALO_I32; sa and sb are not read and may be NULL)
+ * a is [m x k] (lda), b is [n x k] (ldb), both contiguous along k; c is [m x n] (ldc).
+ * k must be a positive multiple of 16; m and n are arbitrary (>= 0).
+ */
+halo_status halo_gemm_i8(const int8_t* a, int64_t lda, const float* sa, const int8_t* b,
+                         int64_t ldb, const float* sb, int64_t m, int64_t n, int64_t k, void* c,
+                         halo_dtype c_type, int64_t ldc, void* stream);
+
+/*
+ * FP8 product (key design 2 of the HALO page: FP8 as the alternative 8-bit type) with fp32
+ * accumulation on the CDNA4 FP8 matrix cores and the same fused dequant:
+ *   c[i, j] = (sum_t dec(a[i, t]) * dec(b[j, t])) * sa[i] * sb[j]
+ * a_type, b_type: HALO_E4M3 or HALO_E5M2 each (any pair); c_type: HALO_F32 or HALO_BF16.
+ * Shapes and layouts as for halo_gemm_i8; k must be a positive multiple of 32.
+ * The fp32 sum's order is the matrix core's: the result lies within
+ * k * 2^-24 / (1 - k * 2^-24) * sum_t |dec(a) dec(b)| of the exact sum before the dequant.
+ */
+halo_status halo_gemm_fp8(const void* a, halo_dtype a_type, int64_t lda, const float* sa,
+                          const void* b, halo_dtype b_type, int64_t ldb, const float* sb,
+                          int64_t m, int64_t n, int64_t k, void* c, halo_dtype c_type,
+                          int64_t ldc, void* stream);
+
+/*
+ * Workspace bytes the layer calls need (codes + scales of every quantised operand, each
+ * region 256-byte aligned).  backward = 0 for halo_linear_fwd, 1 for halo_linear_bwd.
+ * Returns 0 for invalid sizes or types.
+ */
+size_t halo_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, halo_dtype q_type,
+                                   int backward);
+
+/*
+ * Forward of the rotated low-precision linear layer: Y[m x n] = X[m x k] W[n x k]^T with
+ * both operands rotated along k, quantised per row and multiplied in 8 bits (the HALO
+ * page's forward pass; rotation and quantiser per the QWHA page s2.1-s2.2).
+ *   io_type  HALO_F32 or HALO_BF16 for x and w (dense, leading dimension k).
+ *   q_type   HALO_I8 or HALO_E4M3.
+ *   y_type   HALO_F32 or HALO_BF16 (dense, leading dimension n).
+ *   ws       caller workspace of at least halo_linear_workspace_bytes(m, n, k, q_type, 0).
+ * k must be a multiple of 32 (and of block); block as for halo_fwht_quant.
+ */
+halo_status halo_linear_fwd(const void* x, const void* w, halo_dtype io_type, int64_t m,
+                            int64_t n, int64_t k, int32_t block, halo_dtype q_type, void* y,
+                            halo_dtype y_type, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Backward of the layer (the HALO page: rotations in the backward pass too, both gradient
+ * products in 8 bits), each product rotated along its own contraction dimension:
+ *   dX[m x k] = dY[m x n] W[n x k]    rows of dY and columns of W rotated along n
+ *   dW[n x k] = dY^T X                columns of dY and of X rotated along m
+ * Operands are re-quantised from the high-precision x, w and dy.
+ *   io_type      HALO_F32 or HALO_BF16 for dy, x, w and the outputs dx, dw (dense).
+ *   q_type       codes of X and W: HALO_I8 or HALO_E4M3.
+ *   grad_q_type  codes of dY: HALO_I8 (with q_type HALO_I8) or HALO_E5M2 / HALO_E4M3 (with
+ *                q_type HALO_E4M3).
+ *   dx, dw       outputs; either may be NULL to skip that product.
+ * m, n and k must be multiples of 32 (and of block); block as for halo_fwht_quant.
+ */
+halo_status halo_linear_bwd(const void* dy, const void* x, const void* w, halo_dtype io_type,
+                            int64_t m, int64_t n, int64_t k, int32_t block, halo_dtype q_type,
+                            halo_dtype grad_q_type, void* dx, void* dw, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* halo_status_str(halo_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HALO_H */

@@ -1,0 +1,176 @@
+"""Host-side checks of the C ABI: the library loads without a GPU, exports every symbol the
+header declares, and rejects every invalid call with its status code before any HIP call
+(the fake device pointers below are never dereferenced)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "halo.h")
+
+import hadamard_rotated_precision_halo_amd as H  # noqa: E402
+
+OK, NULL, SHAPE, BLOCK, DTYPE, ALIGN, WORKSPACE, HIP = range(8)
+F32, BF16, I8, E4M3, E5M2, I32 = range(6)
+
+P = ctypes.c_void_p(0x10000)    # 16-byte aligned fake device pointer
+P2 = ctypes.c_void_p(0x20000)
+P3 = ctypes.c_void_p(0x30000)
+BAD = ctypes.c_void_p(0x10008)  # misaligned
+NUL = None
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(H.LIB_PATH):
+        import hadamard_rotated_precision_halo_amd.build as b
+        b.build()
+    return H.lib()
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    return sorted(set(re.findall(r"^\s*(?:const char\*|halo_status|size_t)\s+(halo_\w+)\s*\(",
+                                 text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for f in ("halo_fwht_quant", "halo_gemm_i8", "halo_gemm_fp8", "halo_linear_fwd",
+              "halo_linear_bwd", "halo_linear_workspace_bytes", "halo_status_str"):
+        assert f in names
+    assert set(names) == set(H.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", H.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(halo_\w+)$", out, re.M))
+    for f in declared_functions():
+        assert f in exported, f
+        getattr(L, f)  # resolvable through ctypes
+
+
+def test_status_strings(L):
+    for s in range(8):
+        assert L.halo_status_str(s)
+    assert L.halo_status_str(0) == b"ok"
+
+
+def fq(L, x=P, xt=BF16, rows=64, cols=256, ldx=256, axis=0, block=256, qt=I8, q=P2, ldq=256,
+       scale=P3):
+    return L.halo_fwht_quant(x, xt, rows, cols, ldx, axis, block, qt, q, ldq, scale, None)
+
+
+def test_fwht_quant_validation(L):
+    assert fq(L, x=NUL) == NULL
+    assert fq(L, q=NUL) == NULL
+    assert fq(L, scale=NUL) == NULL
+    assert fq(L, xt=I8) == DTYPE
+    assert fq(L, qt=BF16) == DTYPE
+    assert fq(L, qt=I32) == DTYPE
+    assert fq(L, block=3) == BLOCK
+    assert fq(L, block=0) == BLOCK
+    assert fq(L, block=8192, cols=8192, ldx=8192, ldq=8192) == BLOCK
+    assert fq(L, block=512) == BLOCK             # 512 does not divide 256
+    assert fq(L, axis=1, block=128) == BLOCK     # cols axis rotates the 64 rows
+    assert fq(L, rows=-1) == SHAPE
+    assert fq(L, ldx=128) == SHAPE
+    assert fq(L, ldq=128) == SHAPE
+    assert fq(L, axis=7) == SHAPE
+    assert fq(L, block=4, cols=12, ldx=16, ldq=16) == SHAPE          # length not a multiple of 8
+    assert fq(L, axis=1, block=16, rows=64, cols=12, ldx=16, ldq=64) == SHAPE  # 12 columns
+    big = 1 << 20
+    assert fq(L, cols=big, ldx=big, ldq=big, block=256) == SHAPE     # beyond the rows kernel
+    assert fq(L, x=BAD) == ALIGN
+    assert fq(L, q=BAD) == ALIGN
+    assert fq(L, ldx=260, cols=256) == ALIGN  # 520 bytes per bf16 row
+    assert fq(L, ldq=260) == ALIGN
+
+
+def gi8(L, a=P, lda=128, sa=P2, b=P3, ldb=128, sb=P2, m=64, n=64, k=128, c=P, ct=BF16, ldc=64):
+    return L.halo_gemm_i8(a, lda, sa, b, ldb, sb, m, n, k, c, ct, ldc, None)
+
+
+def test_gemm_i8_validation(L):
+    assert gi8(L, a=NUL) == NULL
+    assert gi8(L, c=NUL) == NULL
+    assert gi8(L, sa=NUL) == NULL
+    assert gi8(L, ct=I8) == DTYPE
+    assert gi8(L, ct=E4M3) == DTYPE
+    assert gi8(L, k=0) == SHAPE
+    assert gi8(L, k=120, lda=128, ldb=128) == SHAPE
+    assert gi8(L, m=-1) == SHAPE
+    assert gi8(L, lda=64) == SHAPE
+    assert gi8(L, ldc=32) == SHAPE
+    assert gi8(L, a=BAD) == ALIGN
+    assert gi8(L, lda=136, k=128) == ALIGN        # rows not 16-byte aligned
+    assert gi8(L, ct=BF16, ldc=68) == ALIGN       # 136-byte output rows
+    assert gi8(L, sa=BAD) == ALIGN
+
+
+def gf8(L, a=P, at=E4M3, lda=128, sa=P2, b=P3, bt=E4M3, ldb=128, sb=P2, m=64, n=64, k=128, c=P,
+        ct=BF16, ldc=64):
+    return L.halo_gemm_fp8(a, at, lda, sa, b, bt, ldb, sb, m, n, k, c, ct, ldc, None)
+
+
+def test_gemm_fp8_validation(L):
+    assert gf8(L, at=I8) == DTYPE
+    assert gf8(L, bt=BF16) == DTYPE
+    assert gf8(L, ct=I32) == DTYPE
+    assert gf8(L, k=112, lda=128, ldb=128) == SHAPE   # not a multiple of 32
+    assert gf8(L, sb=NUL) == NULL
+    assert gf8(L, b=BAD) == ALIGN
+
+
+def test_workspace_bytes(L):
+    r = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    m, n, k = 300, 520, 1024
+    assert L.halo_linear_workspace_bytes(m, n, k, I8, 0) == r(m * k) + r(4 * m) + r(n * k) + r(4 * n)
+    want = (r(m * n) + r(4 * m) + r(k * n) + r(4 * k) + r(n * m) + r(4 * n) + r(k * m) + r(4 * k))
+    assert L.halo_linear_workspace_bytes(m, n, k, E4M3, 1) == want
+    assert L.halo_linear_workspace_bytes(-1, n, k, I8, 0) == 0
+    assert L.halo_linear_workspace_bytes(m, n, k, BF16, 0) == 0
+
+
+def fwd(L, x=P, w=P2, io=BF16, m=256, n=256, k=256, block=128, qt=I8, y=P3, yt=BF16, ws=P,
+        wsb=None):
+    if wsb is None:
+        wsb = L.halo_linear_workspace_bytes(m, n, k, I8, 0)
+    return L.halo_linear_fwd(x, w, io, m, n, k, block, qt, y, yt, ws, wsb, None)
+
+
+def test_linear_fwd_validation(L):
+    assert fwd(L, x=NUL) == NULL
+    assert fwd(L, io=I8) == DTYPE
+    assert fwd(L, qt=E5M2) == DTYPE
+    assert fwd(L, yt=I32) == DTYPE
+    assert fwd(L, k=240) == SHAPE
+    assert fwd(L, block=512) == BLOCK
+    assert fwd(L, block=6) == BLOCK
+    assert fwd(L, ws=NUL) == WORKSPACE
+    assert fwd(L, wsb=1000) == WORKSPACE
+    assert fwd(L, y=BAD) == ALIGN
+
+
+def bwd(L, dy=P, x=P2, w=P3, io=BF16, m=256, n=256, k=256, block=128, qt=I8, gqt=I8, dx=P,
+        dw=P2, ws=P3, wsb=None):
+    if wsb is None:
+        wsb = L.halo_linear_workspace_bytes(m, n, k, I8, 1)
+    return L.halo_linear_bwd(dy, x, w, io, m, n, k, block, qt, gqt, dx, dw, ws, wsb, None)
+
+
+def test_linear_bwd_validation(L):
+    assert bwd(L, dy=NUL) == NULL
+    assert bwd(L, gqt=E5M2) == DTYPE          # INT8 operands need INT8 gradients
+    assert bwd(L, qt=E4M3, gqt=I8) == DTYPE
+    assert bwd(L, qt=E5M2, gqt=E5M2) == DTYPE
+    assert bwd(L, m=240) == SHAPE
+    assert bwd(L, m=0) == SHAPE
+    assert bwd(L, block=512) == BLOCK
+    assert bwd(L, m=384, block=256) == BLOCK  # 256 does not divide 384 tokens
+    assert bwd(L, wsb=10) == WORKSPACE
+    assert bwd(L, dx=BAD) == ALIGN

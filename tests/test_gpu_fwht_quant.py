@@ -1,0 +1,164 @@
+"""GPU parity of halo_fwht_quant (rows and columns axes) against the CPU oracle.
+
+Bars: codes and scales bit-identical to the oracle's fp32 decision (same butterfly order,
+same fp32 quotient); rotated values (fp32 test mode) bit-identical to the oracle's fp32
+butterflies and within 1e-5 relative L2 per vector of its fp64 transform; codes within the
++-1 / 0.01% budget of its fp64 decision and scales within 1e-5 of its fp64 scales.
+"""
+import numpy as np
+import pytest
+import torch
+
+import hadamard_rotated_precision_halo_amd as H
+import oracle as O
+import synth
+from parity_util import (Q_TORCH, assert_codes_close_to_fp64, codes_to_np, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def _input(rows, cols, io, seed, kind="act"):
+    rng = np.random.default_rng(seed)
+    if kind == "act":
+        a = synth.activations(rng, rows, cols)
+    elif kind == "grad":
+        a = synth.grads(rng, rows, cols)
+    else:
+        a = synth.weights(rng, rows, cols)
+    return synth.bf16_bits(a) if io == "bf16" else a
+
+
+def _run(x_np, axis, block, qtype):
+    x = to_dev(x_np)
+    q, s = H.fwht_quant(x, axis=axis, block=block, q_dtype=Q_TORCH[qtype])
+    torch.cuda.synchronize()
+    return codes_to_np(q), s.cpu().numpy().astype(np.float64)
+
+
+ROW_CASES = [
+    # (io, block, rows, cols, qtype)
+    ("bf16", 256, 37, 4096, O.I8),
+    ("bf16", 128, 19, 11008, O.I8),        # 86 blocks: the last lane groups of a row idle
+    ("f32", 1024, 9, 1024, O.I8),
+    ("bf16", 512, 5, 14336, O.E5M2),
+    ("bf16", 512, 33, 4096, O.E4M3),
+    ("bf16", 1, 17, 64, O.I8),
+    ("bf16", 2, 17, 64, O.I8),
+    ("bf16", 4, 300, 16, O.I8),
+    ("bf16", 8, 301, 16, O.E4M3),
+    ("bf16", 16, 129, 48, O.I8),
+    ("bf16", 32, 70, 96, O.E5M2),
+    ("f32", 64, 65, 320, O.I8),
+    ("bf16", 2048, 3, 4096, O.I8),
+    ("bf16", 4096, 4, 8192, O.E4M3),
+    ("bf16", 128, 2, 16384, O.I8),         # longest row the rows kernel takes at block 128
+    ("bf16", 256, 1000, 256, O.I8),        # many short rows per workgroup
+]
+
+
+@pytest.mark.parametrize("io,block,rows,cols,qtype", ROW_CASES)
+def test_rows_match_oracle(io, block, rows, cols, qtype):
+    x = _input(rows, cols, io, seed=rows * 7 + cols)
+    q, s = _run(x, H.ROWS, block, qtype)
+    r32, s32 = O.fwht_quant(x, O.ROWS, block, qtype, precision=32)
+    assert np.array_equal(q, r32), f"{int((q != r32).sum())} codes differ from the fp32 decision"
+    assert np.array_equal(s, s32)
+    r64, s64 = O.fwht_quant(x, O.ROWS, block, qtype, precision=64)
+    assert_codes_close_to_fp64(q, r64, qtype, block)
+    np.testing.assert_allclose(s, s64, rtol=1e-5)
+
+
+COL_CASES = [
+    ("bf16", 256, 4096, 64, O.I8),
+    ("bf16", 128, 1024, 200, O.I8),       # 200 columns: a partial workgroup
+    ("bf16", 512, 2048, 40, O.E5M2),
+    ("bf16", 512, 1024, 56, O.E4M3),
+    ("f32", 256, 512, 24, O.I8),
+    ("bf16", 1, 64, 16, O.I8),
+    ("bf16", 2, 64, 8, O.I8),
+    ("bf16", 4, 48, 16, O.I8),
+    ("bf16", 8, 64, 16, O.E4M3),
+    ("bf16", 16, 96, 32, O.I8),
+    ("bf16", 32, 64, 8, O.I8),
+    ("bf16", 64, 192, 24, O.E5M2),
+    ("bf16", 1024, 2048, 16, O.I8),
+    ("bf16", 2048, 4096, 8, O.E4M3),
+    ("bf16", 4096, 8192, 8, O.I8),
+]
+
+
+@pytest.mark.parametrize("io,block,rows,cols,qtype", COL_CASES)
+def test_cols_match_oracle(io, block, rows, cols, qtype):
+    x = _input(rows, cols, io, seed=rows * 5 + cols, kind="grad")
+    q, s = _run(x, H.COLS, block, qtype)
+    assert q.shape == (cols, rows)
+    r32, s32 = O.fwht_quant(x, O.COLS, block, qtype, precision=32)
+    assert np.array_equal(q, r32), f"{int((q != r32).sum())} codes differ from the fp32 decision"
+    assert np.array_equal(s, s32)
+    r64, s64 = O.fwht_quant(x, O.COLS, block, qtype, precision=64)
+    assert_codes_close_to_fp64(q, r64, qtype, block)
+    np.testing.assert_allclose(s, s64, rtol=1e-5)
+
+
+@pytest.mark.parametrize("axis,block,rows,cols", [(H.ROWS, 256, 24, 1024), (H.ROWS, 128, 6, 11008),
+                                                  (H.COLS, 256, 1024, 64), (H.COLS, 512, 2048, 16),
+                                                  (H.ROWS, 4096, 2, 4096), (H.COLS, 4096, 4096, 8)])
+def test_rotated_values_fp32_mode(axis, block, rows, cols):
+    x = _input(rows, cols, "bf16", seed=rows + cols)
+    y, s = _run(x, axis, block, O.F64)
+    oax = O.ROWS if axis == H.ROWS else O.COLS
+    y32, s32 = O.fwht_quant(x, oax, block, O.F64, precision=32)
+    assert np.array_equal(y.astype(np.float64), y32)       # bit-identical fp32 butterflies
+    assert np.array_equal(s, s32)
+    y64, _ = O.fwht_quant(x, oax, block, O.F64, precision=64)
+    err = np.linalg.norm(y - y64, axis=1) / np.linalg.norm(y64, axis=1)
+    assert err.max() <= 1e-5
+
+
+def test_zero_vectors_and_constant_rows():
+    x = _input(16, 512, "bf16", seed=3)
+    x[3] = 0
+    x[7] = synth.bf16_bits(np.full(512, 2.5, dtype=np.float32))
+    for qt in (O.I8, O.E4M3, O.E5M2):
+        q, s = _run(x, H.ROWS, 128, qt)
+        r, rs = O.fwht_quant(x, O.ROWS, 128, qt, precision=32)
+        assert np.array_equal(q, r) and np.array_equal(s, rs)
+        assert s[3] == 0 and not q[3].any()
+    xc = _input(256, 16, "bf16", seed=4)
+    xc[:, 5] = 0
+    q, s = _run(xc, H.COLS, 64, O.I8)
+    assert s[5] == 0 and not q[5].any()
+
+
+def test_empty_inputs():
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    q, s = H.fwht_quant(x, axis=H.ROWS, block=256)
+    assert q.shape == (0, 256) and s.shape == (0,)
+    x = torch.empty((256, 0), dtype=torch.bfloat16, device="cuda")
+    q, s = H.fwht_quant(x, axis=H.COLS, block=256)
+    assert q.shape == (0, 256)
+
+
+def test_leading_dimensions_and_repeatability():
+    # a strided view (ld > cols) for the input, and bit-identical repeated runs
+    base = to_dev(_input(64, 1536, "bf16", seed=9))
+    view = base[:, :1024]
+    q1, s1 = H.fwht_quant(view, axis=H.ROWS, block=256)
+    q2, s2 = H.fwht_quant(view.contiguous(), axis=H.ROWS, block=256)
+    assert torch.equal(q1, q2) and torch.equal(s1, s2)
+    c1, t1 = H.fwht_quant(view, axis=H.COLS, block=64)
+    c2, t2 = H.fwht_quant(view.contiguous(), axis=H.COLS, block=64)
+    assert torch.equal(c1, c2) and torch.equal(t1, t2)
+    for _ in range(3):
+        q3, s3 = H.fwht_quant(view, axis=H.ROWS, block=256)
+        assert torch.equal(q1, q3) and torch.equal(s1, s3)
+
+
+def test_invalid_call_leaves_outputs_untouched():
+    x = to_dev(_input(8, 256, "bf16", seed=1))
+    q = torch.full((8, 256), 7, dtype=torch.int8, device="cuda")
+    s = torch.full((8,), 3.0, device="cuda")
+    with pytest.raises(H.HaloError):
+        H.fwht_quant(x, axis=H.ROWS, block=512, q=q, scale=s)
+    torch.cuda.synchronize()
+    assert (q == 7).all() and (s == 3.0).all()

@@ -1,0 +1,142 @@
+"""GPU parity of the layer entry points halo_linear_fwd / halo_linear_bwd against the oracle.
+
+Bars: relative Frobenius error <= 1e-2 against the oracle's fp64 quantised path (the
+spec bar); against the oracle's fp32-decision path the codes are identical, so the only
+difference left is the output rounding (bf16: 2^-8 relative per element, with slack for the
+fp32 epilogue).  Workloads are the synth layer tensors (outlier channels, Student-t grads).
+"""
+import numpy as np
+import pytest
+import torch
+
+import hadamard_rotated_precision_halo_amd as H
+import oracle as O
+import synth
+from parity_util import Q_TORCH, fp8_acc_bound, rel_fro, to_dev
+
+pytestmark = pytest.mark.gpu
+
+QT = {"i8": O.I8, "e4m3": O.E4M3, "e5m2": O.E5M2}
+
+
+def _np(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def _elementwise_bound(got, ref, rel, extra=0.0):
+    scale = np.abs(ref) + 1e-6 * np.abs(ref).max()
+    return (np.abs(got - ref) <= rel * scale + extra).all()
+
+
+def _fp8_extra(a, aax, at, b, bax, bt, block):
+    """Accumulation bound of the FP8 matrix cores for the product of the oracle's codes of
+    operand a (vectors along axis aax) and operand b, in output units (scales applied)."""
+    qa, sa = O.fwht_quant(a, aax, block, at, precision=32)
+    qb, sb = O.fwht_quant(b, bax, block, bt, precision=32)
+    absum = O.matmul_f64(np.abs(O.fp8_table(at)[qa]), np.abs(O.fp8_table(bt)[qb]))
+    return fp8_acc_bound(absum, qa.shape[1]) * np.outer(sa, sb) * (1 + 1e-6)
+
+
+FWD = [  # m, n, k, block, io, q
+    (256, 1024, 1024, 1024, synth.F32, "i8"),     # the single-linear workload, full size
+    (320, 384, 1024, 256, synth.BF16, "i8"),
+    (96, 200, 11008, 128, synth.BF16, "i8"),      # ragged n, 86 blocks along k
+    (256, 512, 4096, 512, synth.BF16, "e4m3"),
+    (64, 64, 512, 1, synth.BF16, "i8"),           # block 1: no rotation
+    (0, 256, 256, 256, synth.BF16, "i8"),         # no tokens
+]
+
+
+@pytest.mark.parametrize("m,n,k,block,io,q", FWD)
+def test_linear_fwd(m, n, k, block, io, q):
+    x, w, _ = synth.layer(m, n, k, seed=m + n + k, io=io, with_grad=False)
+    y = H.linear_fwd(to_dev(x), to_dev(w), block, q_dtype=Q_TORCH[QT[q]])
+    torch.cuda.synchronize()
+    got = _np(y)
+    assert got.shape == (m, n)
+    if m == 0:
+        return
+    ref64 = O.linear_fwd(x, w, block, QT[q], precision=64)
+    assert rel_fro(got, ref64) <= 1e-2
+    ref32 = O.linear_fwd(x, w, block, QT[q], precision=32)
+    rel = 4 * 2.0 ** -24 if io == synth.F32 else 2.0 ** -8 + 4 * 2.0 ** -24
+    extra = 0.0
+    if QT[q] != O.I8:  # grouped accumulation of the FP8 matrix cores
+        extra = _fp8_extra(x, O.ROWS, QT[q], w, O.ROWS, QT[q], block)
+    assert _elementwise_bound(got, ref32, rel, extra)
+
+
+BWD = [  # m, n, k, block, io, q, gq
+    (512, 384, 256, 128, synth.BF16, "i8", "i8"),
+    (256, 512, 768, 256, synth.BF16, "i8", "i8"),
+    (1024, 512, 256, 512, synth.BF16, "e4m3", "e5m2"),
+    (256, 256, 128, 64, synth.F32, "i8", "i8"),
+    (512, 512, 256, 256, synth.BF16, "e4m3", "e4m3"),
+]
+
+
+@pytest.mark.parametrize("m,n,k,block,io,q,gq", BWD)
+def test_linear_bwd(m, n, k, block, io, q, gq):
+    x, w, dy = synth.layer(m, n, k, seed=7 * m + n + k, io=io)
+    dx, dw = H.linear_bwd(to_dev(dy), to_dev(x), to_dev(w), block, q_dtype=Q_TORCH[QT[q]],
+                          grad_q_dtype=Q_TORCH[QT[gq]])
+    torch.cuda.synchronize()
+    gdx, gdw = _np(dx), _np(dw)
+    r64 = O.linear_bwd(dy, x, w, block, QT[q], QT[gq], precision=64)
+    assert rel_fro(gdx, r64[0]) <= 1e-2
+    assert rel_fro(gdw, r64[1]) <= 1e-2
+    r32 = O.linear_bwd(dy, x, w, block, QT[q], QT[gq], precision=32)
+    rel = 4 * 2.0 ** -24 if io == synth.F32 else 2.0 ** -8 + 4 * 2.0 ** -24
+    ex_dx = ex_dw = 0.0
+    if QT[q] != O.I8:
+        ex_dx = _fp8_extra(dy, O.ROWS, QT[gq], w, O.COLS, QT[q], block)
+        ex_dw = _fp8_extra(dy, O.COLS, QT[gq], x, O.COLS, QT[q], block)
+    assert _elementwise_bound(gdx, r32[0], rel, ex_dx)
+    assert _elementwise_bound(gdw, r32[1], rel, ex_dw)
+
+
+def test_linear_bwd_single_outputs():
+    m, n, k, b = 256, 256, 512, 128
+    x, w, dy = synth.layer(m, n, k, seed=11)
+    dxo, dwo = H.linear_bwd(to_dev(dy), to_dev(x), to_dev(w), b, want_dw=False)
+    assert dwo is None
+    dxb, dwb = H.linear_bwd(to_dev(dy), to_dev(x), to_dev(w), b, want_dx=False)
+    assert dxb is None
+    dx, dw = H.linear_bwd(to_dev(dy), to_dev(x), to_dev(w), b)
+    assert torch.equal(dx, dxo) and torch.equal(dw, dwb)
+
+
+def test_rotation_beats_no_rotation_on_outliers():
+    # the method's purpose: with outlier channels the rotated INT8 layer is closer to the
+    # exact product than the same layer without rotation (block 1)
+    m, n, k = 512, 512, 4096
+    x, w, _ = synth.layer(m, n, k, seed=21, io=synth.BF16, with_grad=False)
+    xf, wf = synth.bf16_to_f32(x).astype(np.float64), synth.bf16_to_f32(w).astype(np.float64)
+    exact = xf @ wf.T
+    rot = _np(H.linear_fwd(to_dev(x), to_dev(w), 256))
+    raw = _np(H.linear_fwd(to_dev(x), to_dev(w), 1))
+    assert rel_fro(rot, exact) * 2.5 < rel_fro(raw, exact)
+
+
+def test_repeat_runs_bit_identical():
+    m, n, k, b = 512, 768, 1024, 256
+    x, w, dy = synth.layer(m, n, k, seed=31)
+    X, W, DY = to_dev(x), to_dev(w), to_dev(dy)
+    y0 = H.linear_fwd(X, W, b)
+    dx0, dw0 = H.linear_bwd(DY, X, W, b)
+    for _ in range(5):
+        assert torch.equal(H.linear_fwd(X, W, b), y0)
+        dx, dw = H.linear_bwd(DY, X, W, b)
+        assert torch.equal(dx, dx0) and torch.equal(dw, dw0)
+
+
+def test_non_default_stream():
+    m, n, k, b = 256, 256, 1024, 256
+    x, w, _ = synth.layer(m, n, k, seed=41, with_grad=False)
+    X, W = to_dev(x), to_dev(w)
+    ref = H.linear_fwd(X, W, b)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        y = H.linear_fwd(X, W, b)
+    s.synchronize()
+    assert torch.equal(y, ref)
