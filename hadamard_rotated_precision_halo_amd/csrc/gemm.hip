@@ -3,18 +3,29 @@
 // What is computed ("HALO: Hadamard-Assisted Lower-Precision Optimization for LLMs",
 // abstract: every large product of the forward and backward pass in low precision; key
 // design 2: INT8 or FP8):  acc[i, j] = sum_t a[i, t] b[j, t] with INT8 codes accumulated in
-// int32 (v_mfma_i32_32x32x32_i8) or FP8 codes accumulated in fp32 (the CDNA4
-// v_mfma_f32_32x32x64_f8f6f4 with a per-operand format select), then
-// c[i, j] = acc * sa[i] * sb[j] in fp32, rounded to bf16 or kept in fp32 (or the raw int32).
+// int32 (v_mfma_i32_32x32x32_i8) or FP8 codes on the CDNA4 v_mfma_*_32x32x64_f8f6f4 with a
+// per-operand format select, then c[i, j] = (acc * sa[i]) * sb[j] in fp32, rounded to bf16 or
+// kept in fp32 (or the raw int32 accumulators).
 //
 // Tiling.  A 256-thread workgroup (4 wave64s, 2 x 2) owns a 256 x 256 output tile; each wave
-// owns 128 x 128 = 4 x 4 MFMA tiles of 32 x 32 with the accumulators resident in registers.
-// Each K step moves a 256 x 128-byte slab of each operand global -> registers -> LDS, double
-// buffered (2 x 64 KB of the 160 KB LDS): the next slab's global loads are in flight while
-// the current slab feeds the matrix cores.  16-byte chunks are XOR-swizzled by the row's low
-// 3 bits in LDS so the fragment reads of 8 consecutive rows spread over all banks.
-// The product is formed transposed (the MFMA's first operand is the b tile), so each lane
-// ends with 4 consecutive output columns of one row: 8- or 16-byte vector stores.
+// owns 128 x 128 = 4 x 4 MFMA tiles of 32 x 32 with the accumulators resident in AGPRs.  K is
+// consumed in slabs of BK bytes: a slab (256 rows of each operand) is staged in LDS with
+// direct-to-LDS loads (global_load_lds_dwordx4: no VGPR staging, no ds_write) into a ring of
+// NSTAGE slabs filling 128 KB of the 160 KB LDS.  One barrier per slab, placed before the
+// slab's last MFMA sub-step: by then that sub-step's fragments are already in VGPRs, so the
+// slab's ring slot is refilled right after the barrier (with the slab NSTAGE ahead) while the
+// MFMAs keep the matrix cores busy, and the next slab's first fragments are read meanwhile.
+// Operand fragments are double buffered in VGPRs one sub-step ahead.
+//
+// LDS layout.  Row r of a slab is BK bytes = BK / 16 chunks of 16 B; logical chunk c is stored
+// at physical chunk c ^ swz(r).  A fragment read has the 16 lanes of a phase read 16
+// consecutive rows at one logical chunk; the swizzle puts them in 16 distinct bank groups of
+// the 64 banks.  Direct-to-LDS loads write 1 KB contiguous per wave instruction, so each lane
+// loads the global chunk that belongs in its physical slot.
+//
+// The product is formed transposed (the MFMA's first operand is the b tile).  The epilogue
+// stages each wave's accumulators in LDS and reads them back row-contiguous, so the stores
+// are full 256- or 512-byte row runs; the scales sa, sb were loaded into LDS at kernel start.
 // Workgroups are numbered so that each of the 8 XCDs (workgroup i runs on XCD i % 8) gets a
 // contiguous run of tiles, rastered in groups of 4 tile rows, for L2 reuse of both operands.
 #include "halo_device.h"
@@ -24,11 +35,44 @@
 
 namespace halo {
 
-constexpr int BM = 256, BN = 256, BK = 128;
-constexpr int STAGE_BYTES = (BM + BN) * BK;  // 64 KB
-constexpr int LDS_BYTES = 2 * STAGE_BYTES;   // 128 KB
+constexpr int BM = 256, BN = 256;
+constexpr int RING_BYTES = 128 * 1024;          // K-slab ring; the scales follow it
+constexpr int LDS_BYTES = RING_BYTES + 2 * 256 * 4;
 
-__device__ __forceinline__ int lds_off(int r, int c) { return r * BK + ((c ^ (r & 7)) << 4); }
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 values to packed bf16, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2_t h = __builtin_convertvector((f32x2_t){a, b}, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// One 16-byte direct-to-LDS load per lane: the lane's 16 bytes at g land at lds + 16 * lane.
+__device__ __forceinline__ void dma16(const void* g, lds_void* lds) {
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+}
+
+// s_waitcnt immediate for vmcnt(n) with expcnt and lgkmcnt unconstrained (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+#define HALO_VMCNT(n) ((((n) & 15) | (((n) >> 4) << 14)) | 0x0F70)
+
+// Slab geometry for BK bytes of K per row.
+template <int BK>
+struct Slab {
+  static constexpr int CHUNKS = BK / 16;               // 16-byte chunks per row
+  static constexpr int OPER = BM * BK;                 // bytes per operand per slab
+  static constexpr int STAGE = 2 * OPER;
+  static constexpr int NSTAGE = RING_BYTES / STAGE;    // 4 (BK 64) or 2 (BK 128)
+  static constexpr int INST = OPER / (256 * 16);       // loads per thread per operand
+  static constexpr int RPI = 1024 / BK;                // rows one wave instruction fills
+  // XOR the chunk with the row bits just above the 256-byte bank period.
+  __device__ static __forceinline__ int swz(int r) {
+    return BK == 64 ? ((r >> 2) & 3) : ((r >> 1) & 7);
+  }
+  __device__ static __forceinline__ int off(int r, int c) { return r * BK + ((c ^ swz(r)) << 4); }
+};
 
 template <int OUT>
 __device__ __forceinline__ void store4(void* c, int64_t ldc, int64_t row, int64_t col,
@@ -42,8 +86,8 @@ __device__ __forceinline__ void store4(void* c, int64_t ldc, int64_t row, int64_
           make_float4(v[0], v[1], v[2], v[3]);
     } else {
       uint2 w;
-      w.x = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
-      w.y = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
+      w.x = pack_bf16x2(v[0], v[1]);
+      w.y = pack_bf16x2(v[2], v[3]);
       *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(c) + row * ldc + col) = w;
     }
   } else {
@@ -54,16 +98,21 @@ __device__ __forceinline__ void store4(void* c, int64_t ldc, int64_t row, int64_
       else if constexpr (OUT == 1)
         reinterpret_cast<float*>(c)[row * ldc + col + i] = v[i];
       else
-        reinterpret_cast<uint16_t*>(c)[row * ldc + col + i] = (uint16_t)bf16_rne(v[i]);
+        reinterpret_cast<uint16_t*>(c)[row * ldc + col + i] = (uint16_t)pack_bf16x2(v[i], 0.f);
     }
   }
 }
 
 // KIND 0: INT8.  KIND 1: FP8 with formats AF (a) and BF (b): 0 = E4M3, 1 = E5M2.
-// OUT 0: int32 accumulators, 1: fp32, 2: bf16.
-template <int KIND, int AF, int BF, int OUT>
+// OUT 0: int32 accumulators, 1: fp32, 2: bf16.  MASK: fragments past k are zeroed (needed when
+// k is not a multiple of the slab, or when the FP8 loop pads one extra slab).
+template <int KIND, int AF, int BF, int OUT, bool MASK, int BK>
 __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
+  using SL = Slab<BK>;
+  constexpr int NSTAGE = SL::NSTAGE, INST = SL::INST, RPI = SL::RPI;
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  float* s_sa = reinterpret_cast<float*>(smem + RING_BYTES);
+  float* s_sb = s_sa + 256;
 
   // ---- tile of this workgroup -------------------------------------------------------
   const int tiles_m = (int)((g.m + BM - 1) / BM), tiles_n = (int)((g.n + BN - 1) / BN);
@@ -79,42 +128,56 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
   const int64_t m0 = (int64_t)(first_m + in_grp % gm) * BM;
   const int64_t n0 = (int64_t)(in_grp / gm) * BN;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS bases in SGPRs
   const int wm = wave >> 1, wn = wave & 1;
 
-  // ---- global -> LDS assignment: chunk lc of rows lr + 32 i ------------------------
-  const int lc = tid & 7, lr = tid >> 3;
+  // scales of this tile's rows and columns (written to LDS once the prologue loads landed)
+  float my_sa = 0.f, my_sb = 0.f;
+  if constexpr (OUT != 0) {
+    my_sa = g.sa[min(m0 + tid, g.m - 1)];
+    my_sb = g.sb[min(n0 + tid, g.n - 1)];
+  }
+
+  // ---- direct-to-LDS assignment -----------------------------------------------------
+  // Wave w's instruction i fills LDS bytes [(INST w + i) KB, +1 KB) of an operand's slab =
+  // rows 64 w + RPI i + [0, RPI); lane l lands in physical chunk l % CHUNKS of row
+  // 64 w + RPI i + l / CHUNKS and loads that row's logical chunk (l % CHUNKS) ^ swz(row).
   const char* __restrict__ A = reinterpret_cast<const char*>(g.a);
   const char* __restrict__ Bm = reinterpret_cast<const char*>(g.b);
-  int64_t aoff[8], boff[8];
+  uint32_t aoff[INST], boff[INST];  // byte offsets of the lane's rows (operands are < 4 GB)
+  uint32_t cbo[INST];               // byte offset of the lane's chunk within a slab row
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t ra = min(m0 + lr + 32 * i, g.m - 1);  // clamped rows feed unused outputs
-    const int64_t rb = min(n0 + lr + 32 * i, g.n - 1);
-    aoff[i] = ra * g.lda + lc * 16;
-    boff[i] = rb * g.ldb + lc * 16;
+  for (int i = 0; i < INST; ++i) {
+    const int r = wave * 64 + i * RPI + lane / SL::CHUNKS;
+    cbo[i] = (uint32_t)(((lane % SL::CHUNKS) ^ SL::swz(r)) << 4);
+    aoff[i] = (uint32_t)(min(m0 + r, g.m - 1) * g.lda);  // clamped rows feed unused outputs
+    boff[i] = (uint32_t)(min(n0 + r, g.n - 1) * g.ldb);
   }
-  uint4 ra_[8], rb_[8];
-  auto gload = [&](int kt) {
-    const int64_t koff = (int64_t)kt * BK;
-    const bool in = koff + lc * 16 < g.k;  // k is a multiple of 16: chunks are all-in or all-out
+  const int nk = (int)((g.k + BK - 1) / BK);
+  constexpr int KS = BK / (KIND == 0 ? 32 : 64);  // MFMA K sub-steps per slab
+  constexpr int UNROLL = KS == 1 ? 2 : 1;          // keeps the fragment buffer index constant
+  const int nkr = (nk + UNROLL - 1) / UNROLL * UNROLL;
+  const uint32_t klast = (uint32_t)g.k - 16;       // last in-bounds chunk of a row
+
+  // Stage slab kt into ring slot kt % NSTAGE: always 2 * INST direct-to-LDS loads per thread,
+  // so the vmcnt arithmetic is uniform.  Slabs past the end reload the last slab (never read)
+  // and chunks past k read the row's last chunk instead; their fragments are masked to zero.
+  auto stage = [&](int kt) __attribute__((always_inline)) {
+    char* sa = smem + (kt % NSTAGE) * SL::STAGE;
+    char* sb = sa + SL::OPER;
+    const uint32_t kb = (uint32_t)min(kt, nk - 1) * BK;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      ra_[i] = in ? *reinterpret_cast<const uint4*>(A + aoff[i] + koff) : make_uint4(0, 0, 0, 0);
-      rb_[i] = in ? *reinterpret_cast<const uint4*>(Bm + boff[i] + koff) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto lstore = [&](int buf) {
-    char* sa = smem + buf * STAGE_BYTES;
-    char* sb = sa + BM * BK;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      *reinterpret_cast<uint4*>(sa + lds_off(lr + 32 * i, lc)) = ra_[i];
-      *reinterpret_cast<uint4*>(sb + lds_off(lr + 32 * i, lc)) = rb_[i];
+    for (int i = 0; i < INST; ++i) {
+      uint32_t kc = kb + cbo[i];
+      if constexpr (MASK) kc = min(kc, klast);
+      dma16(A + aoff[i] + kc, (lds_void*)(sa + (wave * INST + i) * 1024));
+      dma16(Bm + boff[i] + kc, (lds_void*)(sb + (wave * INST + i) * 1024));
     }
   };
 
   using Acc = typename std::conditional<KIND == 0, v16i, v16f>::type;
+  using Frag = typename std::conditional<KIND == 0, v4i, v8i>::type;
   Acc acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -124,111 +187,194 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
 
   const int fr = lane & 31, fh = lane >> 5;  // fragment row and K half
-  auto compute = [&](int buf) {
-    const char* sa = smem + buf * STAGE_BYTES;
-    const char* sb = sa + BM * BK;
-    if constexpr (KIND == 0) {
+  Frag fa[2][4], fb[2][4];
+  auto load_frags = [&](int kt, int ks, Frag* da, Frag* db) __attribute__((always_inline)) {
+    const char* sa = smem + (kt % NSTAGE) * SL::STAGE;
+    const char* sb = sa + SL::OPER;
+    const int c0 = KIND == 0 ? ks * 2 + fh : ks * 4 + fh * 2;  // first 16-byte chunk
+    int keep0 = -1, keep1 = -1;
+    if constexpr (MASK) {
+      keep0 = (kt * BK + c0 * 16) < g.k ? -1 : 0;
+      keep1 = (kt * BK + c0 * 16 + 16) < g.k ? -1 : 0;
+    }
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {  // 32 bytes of K per MFMA
-        v4i fa[4], fb[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int rb = wn * 128 + t * 32 + fr, ra = wm * 128 + t * 32 + fr;
-          fb[t] = *reinterpret_cast<const v4i*>(sb + lds_off(rb, ks * 2 + fh));
-          fa[t] = *reinterpret_cast<const v4i*>(sa + lds_off(ra, ks * 2 + fh));
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[i], fa[j], acc[i][j], 0, 0, 0);
+    for (int t = 0; t < 4; ++t) {
+      const int rb = wn * 128 + t * 32 + fr, ra = wm * 128 + t * 32 + fr;
+      if constexpr (KIND == 0) {
+        db[t] = *reinterpret_cast<const v4i*>(sb + SL::off(rb, c0)) & keep0;
+        da[t] = *reinterpret_cast<const v4i*>(sa + SL::off(ra, c0)) & keep0;
+      } else {
+        v4i b0 = *reinterpret_cast<const v4i*>(sb + SL::off(rb, c0)) & keep0;
+        v4i b1 = *reinterpret_cast<const v4i*>(sb + SL::off(rb, c0 + 1)) & keep1;
+        v4i a0 = *reinterpret_cast<const v4i*>(sa + SL::off(ra, c0)) & keep0;
+        v4i a1 = *reinterpret_cast<const v4i*>(sa + SL::off(ra, c0 + 1)) & keep1;
+        db[t] = Frag{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+        da[t] = Frag{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
       }
-    } else {
+    }
+  };
+  auto mfma_step = [&](const Frag* da, const Frag* db) __attribute__((always_inline)) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {  // 64 bytes of K per MFMA
-        v8i fa[4], fb[4];
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int rb = wn * 128 + t * 32 + fr, ra = wm * 128 + t * 32 + fr;
-          const int c = ks * 4 + fh * 2;
-          v4i b0 = *reinterpret_cast<const v4i*>(sb + lds_off(rb, c));
-          v4i b1 = *reinterpret_cast<const v4i*>(sb + lds_off(rb, c + 1));
-          v4i a0 = *reinterpret_cast<const v4i*>(sa + lds_off(ra, c));
-          v4i a1 = *reinterpret_cast<const v4i*>(sa + lds_off(ra, c + 1));
-          fb[t] = v8i{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-          fa[t] = v8i{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-        }
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (KIND == 0)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(db[i], da[j], acc[i][j], 0, 0, 0);
+        else  // first operand = b tile (format BF), second = a tile (format AF); scales 2^0
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(db[i], da[j], acc[i][j], BF,
+                                                                      AF, 0, 127, 0, 127);
+      }
+  };
+
+  // ---- main loop -------------------------------------------------------------------
+  // Sub-steps run in one flat sequence (slab kt, sub-step ks); the next sub-step's fragments
+  // are read while the current one's 16 MFMAs issue.  Before the last sub-step of slab kt the
+  // wave waits for its own loads of slab kt + 1 (later slabs may stay in flight), the barrier
+  // makes every wave's loads visible, and slab kt + NSTAGE is issued into slab kt's slot,
+  // which no wave reads any more.  The loop body has no branches, so the accumulators stay in
+  // AGPRs; scheduling hints spread reads and loads between the MFMAs.
+  constexpr int FRAG_READS = KIND == 0 ? 8 : 16;  // ds_read_b128 per sub-step
+  auto hint_reads = [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < FRAG_READS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 fragment read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+  };
+  auto hint_reads_loads = [&]() __attribute__((always_inline)) {
+    constexpr int LD = 2 * INST;  // slab loads to spread over the 16 MFMAs
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            // first operand = b tile (format BF), second = a tile (format AF); scales 2^0
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                fb[i], fa[j], acc[i][j], BF, AF, 0, 127, 0, 127);
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // 1 MFMA
+      if (i < LD) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);     // 1 slab load
+      if (i < FRAG_READS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+  auto do_slab = [&](int kt, auto P) __attribute__((always_inline)) {
+    constexpr int P0 = decltype(P)::value;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int cur = (P0 + ks) & 1;
+      if (ks + 1 < KS) {
+        load_frags(kt, ks + 1, fa[cur ^ 1], fb[cur ^ 1]);
+        mfma_step(fa[cur], fb[cur]);
+        hint_reads();
+      } else {
+        __builtin_amdgcn_s_waitcnt(HALO_VMCNT(2 * INST * (NSTAGE - 2)));  // slab kt + 1 landed
+        __syncthreads();
+        stage(kt + NSTAGE);
+        load_frags(kt + 1, 0, fa[cur ^ 1], fb[cur ^ 1]);
+        mfma_step(fa[cur], fb[cur]);
+        hint_reads_loads();
       }
     }
   };
 
-  // ---- main loop -------------------------------------------------------------------
-  const int nk = (int)((g.k + BK - 1) / BK);
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    compute(cur);
-    if (kt + 1 < nk) lstore(cur ^ 1);
-    __syncthreads();
+#pragma unroll
+  for (int t = 0; t < NSTAGE; ++t) stage(t);
+  __builtin_amdgcn_s_waitcnt(HALO_VMCNT(2 * INST * (NSTAGE - 1)));  // slab 0 and the scales
+  if constexpr (OUT != 0) {
+    s_sa[tid] = my_sa;
+    s_sb[tid] = my_sb;
   }
+  __syncthreads();
+  load_frags(0, 0, fa[0], fb[0]);
+  for (int kt = 0; kt < nkr; kt += UNROLL) {
+    do_slab(kt, std::integral_constant<int, 0>{});
+    if constexpr (UNROLL == 2) do_slab(kt + 1, std::integral_constant<int, KS & 1>{});
+  }
+  __builtin_amdgcn_s_waitcnt(HALO_VMCNT(0));  // no LDS write may outlive the workgroup
 
-  // ---- epilogue: lane holds column block (r / 4) * 8 + fh * 4 + [0, 4) of row fr ----
+  // ---- epilogue -----------------------------------------------------------------------
+  // Each wave stages its accumulators in LDS, 32 output rows at a time (row pitch 132 words:
+  // the 16-byte writes of 16 consecutive rows fall in 16 different bank groups), and reads
+  // them back row-contiguous: 32 lanes cover one 128-column row, so stores are 256-byte (bf16)
+  // or 512-byte (fp32, int32) runs.  The dequant (acc * sa[row]) * sb[col] is applied after the
+  // read-back, where each lane owns 4 fixed columns.
+  __syncthreads();  // every wave is done with the K slabs
+  constexpr int PITCH = 132;
+  uint32_t* stile = reinterpret_cast<uint32_t*>(smem) + wave * (32 * PITCH);
+  const int ecol = (lane & 31) * 4;  // 4 consecutive columns of this lane after read-back
+  const int64_t col0 = n0 + wn * 128 + ecol;
+  float4 sbv = make_float4(0.f, 0.f, 0.f, 0.f);
+  if constexpr (OUT != 0) sbv = *reinterpret_cast<const float4*>(s_sb + wn * 128 + ecol);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int64_t row = m0 + wm * 128 + j * 32 + fr;
-    if (row >= g.m) continue;
-    const float sar = OUT == 0 ? 0.f : g.sa[row];
+    // lane (fr, fh) holds row fr, columns i * 32 + gq * 8 + fh * 4 + [0, 4) of this chunk
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
-        const int64_t col = n0 + wn * 128 + i * 32 + gq * 8 + fh * 4;
-        if (col >= g.n) continue;
+        uint4 w;
+        if constexpr (KIND == 0) {  // raw int32; converted after the read-back
+          w = make_uint4(acc[i][j][gq * 4 + 0], acc[i][j][gq * 4 + 1], acc[i][j][gq * 4 + 2],
+                         acc[i][j][gq * 4 + 3]);
+        } else {
+          w = make_uint4(__float_as_uint(acc[i][j][gq * 4 + 0]), __float_as_uint(acc[i][j][gq * 4 + 1]),
+                         __float_as_uint(acc[i][j][gq * 4 + 2]), __float_as_uint(acc[i][j][gq * 4 + 3]));
+        }
+        *reinterpret_cast<uint4*>(stile + fr * PITCH + i * 32 + gq * 8 + fh * 4) = w;
+      }
+    // the wave reads back only what it wrote: program order plus the LDS wait suffice
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int r = t * 2 + (lane >> 5);
+      const int64_t row = m0 + wm * 128 + j * 32 + r;
+      const uint4 w = *reinterpret_cast<const uint4*>(stile + r * PITCH + ecol);
+      if (row >= g.m || col0 >= g.n) continue;
+      if constexpr (OUT == 0) {
+        const int iv[4] = {(int)w.x, (int)w.y, (int)w.z, (int)w.w};
+        store4<0>(g.c, g.ldc, row, col0, g.n, nullptr, iv);
+      } else {
+        const float sar = s_sa[wm * 128 + j * 32 + r];
+        float a[4];
+        if constexpr (KIND == 0) {
+          a[0] = (float)(int)w.x; a[1] = (float)(int)w.y; a[2] = (float)(int)w.z; a[3] = (float)(int)w.w;
+        } else {
+          a[0] = __uint_as_float(w.x); a[1] = __uint_as_float(w.y);
+          a[2] = __uint_as_float(w.z); a[3] = __uint_as_float(w.w);
+        }
         float v[4];
-        int iv[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if constexpr (KIND == 0) iv[e] = acc[i][j][gq * 4 + e];
-          else iv[e] = 0;
-        }
-        if constexpr (OUT != 0) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float sbc = col + e < g.n ? g.sb[col + e] : 0.f;
-            const float af = KIND == 0 ? (float)iv[e] : (float)acc[i][j][gq * 4 + e];
-            v[e] = (af * sar) * sbc;
-          }
-        }
-        store4<OUT>(g.c, g.ldc, row, col, g.n, v, iv);
+        v[0] = (a[0] * sar) * sbv.x;
+        v[1] = (a[1] * sar) * sbv.y;
+        v[2] = (a[2] * sar) * sbv.z;
+        v[3] = (a[3] * sar) * sbv.w;
+        store4<OUT>(g.c, g.ldc, row, col0, g.n, v, nullptr);
       }
     }
   }
 }
 
-template <int KIND, int AF, int BF, int OUT>
-static hipError_t launch_t(const GemmArgs& g, hipStream_t st) {
+template <int KIND, int AF, int BF, int OUT, bool MASK, int BK>
+static hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
   std::call_once(once, [] {
-    attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<KIND, AF, BF, OUT>),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+    attr_err = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&gemm_kernel<KIND, AF, BF, OUT, MASK, BK>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
   });
   if (attr_err != hipSuccess) return attr_err;
   const int64_t tiles = ((g.m + BM - 1) / BM) * ((g.n + BN - 1) / BN);
   if (tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_kernel<KIND, AF, BF, OUT>), dim3((unsigned)tiles), dim3(256), LDS_BYTES,
-                     st, g);
+  hipLaunchKernelGGL((gemm_kernel<KIND, AF, BF, OUT, MASK, BK>), dim3((unsigned)tiles), dim3(256),
+                     LDS_BYTES, st, g);
   return hipGetLastError();
+}
+
+#ifndef HALO_GEMM_BK
+#define HALO_GEMM_BK 128
+#endif
+
+template <int KIND, int AF, int BF, int OUT>
+static hipError_t launch_t(const GemmArgs& g, hipStream_t st) {
+  constexpr int BK = HALO_GEMM_BK;
+  constexpr int KS = BK / (KIND == 0 ? 32 : 64);
+  const int64_t nk = (g.k + BK - 1) / BK;
+  const bool mask = (g.k % BK) != 0 || (KS == 1 && (nk & 1));
+  return mask ? launch_cfg<KIND, AF, BF, OUT, true, BK>(g, st)
+              : launch_cfg<KIND, AF, BF, OUT, false, BK>(g, st);
 }
 
 hipError_t launch_gemm(const GemmArgs& g, int kind, int afmt, int bfmt, int out, hipStream_t st) {
