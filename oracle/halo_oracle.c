@@ -27,7 +27,11 @@
  *   - the transform is block-diagonal over contiguous blocks of `block` indices;
  *   - FP8 uses the OCP formats E4M3FN (max 448) and E5M2 (max 57344) with qmax equal to
  *     the format's largest finite value, round to nearest even, saturating;
- *   - a zero vector gets scale 0 and all-zero codes.
+ *   - a zero vector gets scale 0 and all-zero codes;
+ *   - an element whose scaled value is exactly zero gets the code of +0 (0x00 in every
+ *     format): -0 and +0 are one real number, and the sign an fp zero picks up from the
+ *     order of the butterflies carries no meaning for the quantiser.  A nonzero value
+ *     that rounds to zero keeps its sign, as the OCP conversion rule has it.
  *
  * Two precisions are offered for the transform + quantisation step:
  *   precision 64: fp64 butterflies, divide by sqrt(b), q = rne(y * qmax / a) with the
@@ -207,7 +211,7 @@ static void quant_vec_f64(const double* y, int64_t L, int qtype, void* q, double
         if (fabs(y[i]) > a) a = fabs(y[i]);
     double qmax = qmax_of(qtype);
     if (qtype == OR_F64) {
-        memcpy(q, y, (size_t)L * sizeof(double));
+        for (int64_t i = 0; i < L; ++i) ((double*)q)[i] = y[i] == 0.0 ? 0.0 : y[i]; /* +0 */
         *scale = a;
         return;
     }
@@ -219,6 +223,7 @@ static void quant_vec_f64(const double* y, int64_t L, int qtype, void* q, double
     for (int64_t i = 0; i < L; ++i) {
         /* y * qmax is exact in long double; the quotient is rounded once, at 64 bits */
         long double t = (long double)y[i] * (long double)qmax / (long double)a;
+        if (t == 0.0L) t = 0.0L; /* exact zero: the +0 code */
         if (qtype == OR_I8) {
             long double n = rne(t);
             if (n > 127.0L) n = 127.0L;
@@ -240,7 +245,10 @@ static void quant_vec_f32(const float* yu, int64_t L, int64_t block, int qtype, 
         if (fabsf(yu[i]) > a) a = fabsf(yu[i]);
     if (qtype == OR_F64) {
         float r = (float)(1.0 / sqrt((double)block));
-        for (int64_t i = 0; i < L; ++i) ((double*)q)[i] = (double)(yu[i] * r);
+        for (int64_t i = 0; i < L; ++i) {
+            float v = yu[i] * r;
+            ((double*)q)[i] = v == 0.0f ? 0.0 : (double)v; /* exact zero: +0 */
+        }
         *scale = (double)(a * r);
         return;
     }
@@ -260,6 +268,7 @@ static void quant_vec_f32(const float* yu, int64_t L, int64_t block, int qtype, 
             ((int8_t*)q)[i] = (int8_t)n;
         } else {
             float t = yu[i] * m; /* rounded to fp32, then to the fp8 grid */
+            if (t == 0.0f) t = 0.0f; /* exact zero: the +0 code */
             ((uint8_t*)q)[i] = fp8_encode((long double)t, fmt_of(qtype));
         }
     }

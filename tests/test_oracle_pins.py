@@ -231,6 +231,24 @@ def test_zero_vector():
         assert not q[0].any() and not q[2].any()
 
 
+@pytest.mark.parametrize("precision", [32, 64])
+def test_signed_zeros(precision):
+    # reading: an exactly zero scaled value takes the +0 code (0x00); a nonzero value that
+    # rounds to zero keeps its sign (OCP conversion: 0x80 for a tiny negative)
+    x = np.zeros((1, 16), dtype=np.float32)
+    x[0, :8] = -0.0                      # a block of -0: its sum butterfly stays -0
+    x[0, 8:] = [448.0, -1e-9, 3.0, -0.0, 1.0, 2.0, 0.0, -5.0]
+    for qt in (O.E4M3, O.E5M2):
+        q1, _ = O.fwht_quant(x, O.ROWS, 1, qt, precision=precision)    # no rotation
+        assert (q1[0, :8] == 0).all() and q1[0, 11] == 0 and q1[0, 14] == 0
+        assert q1[0, 9] == 0x80            # -1e-9 * qmax / 448 underflows to -0
+        q8, _ = O.fwht_quant(x, O.ROWS, 8, qt, precision=precision)
+        assert (q8[0, :8] == 0).all()
+    # fp32 output mode: zeros come out as +0 too
+    y, _ = O.fwht_quant(x, O.ROWS, 8, O.F64, precision=precision)
+    assert not np.signbit(y[0, :8]).any()
+
+
 def test_precision32_agrees_with_precision64():
     rng = np.random.default_rng(8)
     x = synth.bf16_bits(synth.activations(rng, 64, 1024))
