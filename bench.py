@@ -36,6 +36,7 @@ N_SETS = 6                # 6 x (X, W, dY) bf16 = 576 MB > 256 MB Infinity Cache
 STEP_GOP = 3 * 2 * M * N * K / 1e9
 KERNEL_SOURCES = ["hadamard_rotated_precision_halo_amd/csrc/gemm.hip",
                   "hadamard_rotated_precision_halo_amd/csrc/fwht_quant.hip",
+                  "hadamard_rotated_precision_halo_amd/csrc/fwht_rows.hip",
                   "hadamard_rotated_precision_halo_amd/csrc/halo_device.h"]
 
 

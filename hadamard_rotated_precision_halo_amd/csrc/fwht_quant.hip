@@ -146,13 +146,13 @@ __device__ __forceinline__ void store_chunk(void* dst, const float* y, float m) 
   } else if constexpr (QT == 1 || QT == 2) {
     constexpr int F = QT - 1;
     uint2 w;
-    w.x = fp8_pair<F>(y[0] * m, y[1] * m) | (fp8_pair<F>(y[2] * m, y[3] * m) << 16);
-    w.y = fp8_pair<F>(y[4] * m, y[5] * m) | (fp8_pair<F>(y[6] * m, y[7] * m) << 16);
+    w.x = fp8_pair<F>(mulz(y[0], m), mulz(y[1], m)) | (fp8_pair<F>(mulz(y[2], m), mulz(y[3], m)) << 16);
+    w.y = fp8_pair<F>(mulz(y[4], m), mulz(y[5], m)) | (fp8_pair<F>(mulz(y[6], m), mulz(y[7], m)) << 16);
     *reinterpret_cast<uint2*>(dst) = w;
   } else {
     float4* d = reinterpret_cast<float4*>(dst);
-    d[0] = make_float4(y[0] * m, y[1] * m, y[2] * m, y[3] * m);
-    d[1] = make_float4(y[4] * m, y[5] * m, y[6] * m, y[7] * m);
+    d[0] = make_float4(mulz(y[0], m), mulz(y[1], m), mulz(y[2], m), mulz(y[3], m));
+    d[1] = make_float4(mulz(y[4], m), mulz(y[5], m), mulz(y[6], m), mulz(y[7], m));
   }
 }
 
@@ -416,6 +416,7 @@ int64_t fq_rows_max_len(int block) {
 }
 
 hipError_t launch_fwht_quant(const FqArgs& a, int in_bf16, int qt, int axis, hipStream_t st) {
+  if (axis == 0 && fq_rows2_supported(a.len, a.block)) return launch_fq_rows2(a, in_bf16, qt, st);
   if (in_bf16) {
     switch (qt) {
       case 0: return dispatch_block<uint16_t, 0>(a, axis, st);

@@ -103,6 +103,11 @@ __device__ __forceinline__ uint32_t pack4(uint32_t a, uint32_t b, uint32_t c, ui
   return a | (b << 8) | (c << 16) | (d << 24);
 }
 
+// fl32(y * m) with an exact zero product returned as +0: fma adds +0 to the exact product,
+// and -0 + +0 = +0 under round to nearest, while every nonzero product is rounded once as by
+// a plain multiply.  A zero has one code, +0, whichever sign the butterflies left on it.
+__device__ __forceinline__ float mulz(float y, float m) { return __builtin_fmaf(y, m, 0.0f); }
+
 // Two fp32 values to two OCP FP8 codes (round to nearest even), placed in the low 16 bits.
 template <int FMT>  // 0: E4M3, 1: E5M2
 __device__ __forceinline__ uint32_t fp8_pair(float a, float b) {

@@ -26,6 +26,10 @@ struct FqArgs {
 // axis: 0 rows, 1 cols.
 hipError_t launch_fwht_quant(const FqArgs& a, int in_bf16, int qt, int axis, hipStream_t st);
 
+// Wave-per-slice rows kernel: rows of L = 64 j elements with 4096 % L == 0 or 4096 <= L <= 65536.
+bool fq_rows2_supported(int64_t len, int block);
+hipError_t launch_fq_rows2(const FqArgs& a, int in_bf16, int qt, hipStream_t st);
+
 // Longest row the single-pass rows kernel takes for this block size.
 int64_t fq_rows_max_len(int block);
 

@@ -50,12 +50,15 @@ def assert_codes_close_to_fp64(gpu_q, ref_q, qtype, block, frac=1e-4):
     `frac` of the elements off by one (grid steps for FP8).  The fraction applies to rotated
     data (block >= 16); with block < 16 a bf16 input keeps its 8-bit mantissa, so values
     y * qmax / a that are exact ties in real arithmetic are common and the fp32 and fp64
-    decisions legitimately split them -- there only the +-1 bound is checked."""
+    decisions legitimately split them -- there only the +-1 bound is checked.  Two flips are
+    always allowed: on a few thousand codes one fp32-vs-fp64 split near a rounding midpoint is
+    an ordinary event, not a sign of a wrong kernel (those are caught bit-exactly against the
+    fp32-decision oracle)."""
     d = code_distance(gpu_q, ref_q, qtype)
     assert d.max(initial=0) <= 1, f"code off by {d.max()}"
     if block >= 16:
         n1 = int((d == 1).sum())
-        assert n1 <= frac * d.size, f"{n1} of {d.size} codes off by one"
+        assert n1 <= max(2.0, frac * d.size), f"{n1} of {d.size} codes off by one"
 
 
 # Accumulation of the gfx950 FP8 matrix cores (v_mfma_*_f8f6f4), measured with in-bounds

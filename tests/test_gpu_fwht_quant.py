@@ -53,6 +53,10 @@ ROW_CASES = [
     ("bf16", 4096, 4, 8192, O.E4M3),
     ("bf16", 128, 2, 16384, O.I8),         # longest row the rows kernel takes at block 128
     ("bf16", 256, 1000, 256, O.I8),        # many short rows per workgroup
+    ("bf16", 2048, 7, 2048, O.I8),         # two rows per wave, 32 lanes per block
+    ("f32", 128, 13, 512, O.E4M3),         # eight rows per wave, a partial last wave
+    ("bf16", 64, 50, 64, O.I8),            # one lane per row
+    ("f32", 4096, 3, 12288, O.E5M2),       # three waves per row
 ]
 
 
@@ -128,6 +132,26 @@ def test_zero_vectors_and_constant_rows():
     xc[:, 5] = 0
     q, s = _run(xc, H.COLS, 64, O.I8)
     assert s[5] == 0 and not q[5].any()
+
+
+@pytest.mark.parametrize("axis,block,shape", [(H.ROWS, 1, (8, 4096)), (H.ROWS, 128, (8, 4096)),
+                                               (H.ROWS, 32, (8, 96)), (H.COLS, 1, (256, 16)),
+                                               (H.COLS, 64, (256, 16))])
+def test_signed_zeros(axis, block, shape):
+    # -0 inputs, -0 blocks and exact zeros inside rotated blocks: an exactly zero value takes
+    # the +0 code whichever sign the arithmetic leaves on it, as in the oracle
+    x = _input(*shape, "bf16", seed=9)
+    x[:, ::3] = 0x8000                   # -0 in bf16
+    x[1] = 0x8000
+    x[2] = synth.bf16_bits(np.full(shape[1], -1.5, dtype=np.float32))
+    if axis == H.COLS:
+        x[:, 3] = 0x8000
+    oax = O.ROWS if axis == H.ROWS else O.COLS
+    for qt in (O.E4M3, O.E5M2, O.I8):
+        q, s = _run(x, axis, block, qt)
+        r, rs = O.fwht_quant(x, oax, block, qt, precision=32)
+        assert np.array_equal(q, r), f"{int((q != r).sum())} codes differ"
+        assert np.array_equal(s, rs)
 
 
 def test_empty_inputs():
