@@ -13,9 +13,18 @@ rotate from step to step so that no operand stays in the 256 MB Infinity Cache.
 
 Per-kernel figures are measured in the same run with HIP events on the launch stream: the
 INT8 GEMM (the dominant kernel, MFMA-bound) and the rows / columns rotation passes
-(HBM-bound).  The CPU baseline times the oracle on a bounded sample of the same step.
+(HBM-bound).  The CPU baseline times the oracle on one full step of the same layer.
+
+Other modes:
+  --kernels-only        launch each hot kernel --kernel-iters times next to a 64 MiB device
+                        copy (the counter calibration); run under rocprofv3.
+  --summarize-stats F   turn a rocprofv3 --stats kernel_stats.csv into a text summary.
+  --summarize-pmc D1 D2 turn two rocprofv3 --pmc runs of --kernels-only (FETCH_SIZE in D1,
+                        WRITE_SIZE in D2) into the per-launch HBM traffic of each kernel.
 """
 import argparse
+import csv
+import glob
 import hashlib
 import json
 import os
@@ -34,10 +43,25 @@ M = N = K = 4096
 BLOCK = 256
 N_SETS = 6                # 6 x (X, W, dY) bf16 = 576 MB > 256 MB Infinity Cache
 STEP_GOP = 3 * 2 * M * N * K / 1e9
+GEMM_OPS = 2 * M * N * K
+FQ_BYTES = M * K * (2 + 1) + 4 * M          # bf16 in, one code byte out, one fp32 scale/vector
+GEMM_BYTES = 2 * M * K + 2 * M * N + 4 * (M + N)  # both code operands, bf16 output, scales
+COPY_BYTES = 64 << 20                       # calibration copy: 64 MiB read + 64 MiB written
 KERNEL_SOURCES = ["hadamard_rotated_precision_halo_amd/csrc/gemm.hip",
                   "hadamard_rotated_precision_halo_amd/csrc/fwht_quant.hip",
                   "hadamard_rotated_precision_halo_amd/csrc/fwht_rows.hip",
                   "hadamard_rotated_precision_halo_amd/csrc/halo_device.h"]
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic_4096.json")
+
+# kernel-name patterns of each measured pass (rocprofv3 Kernel_Name substrings); a pass may
+# launch several kernels per call
+PASSES = {
+    "gemm_i8_4096": ["halo::gemm_kernel<0"],
+    "fq_rows_4096": ["halo::fq_rows2_kernel<unsigned short, 256, 0>"],
+    "fq_cols_4096": ["halo::fq_cols_kernel<unsigned short, 256, 0", "halo::fill_zero_kernel",
+                     "halo::finalize_scale_kernel", "halo::fq_cols2_kernel<unsigned short, 256, 0"],
+    "copy_64MiB": ["__amd_rocclr_copyBuffer"],
+}
 
 
 def source_hash(paths):
@@ -48,17 +72,16 @@ def source_hash(paths):
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel_key):
-    """Counter-derived HBM bytes per launch from a committed rocprofv3 summary, or None if the
-    kernels changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", "traffic_4096.json")
-    if not os.path.exists(path):
+def load_traffic(pass_key):
+    """Counter-derived HBM bytes per launch from the committed summary, or None if the kernels
+    changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_JSON):
         return None
-    with open(path) as f:
+    with open(TRAFFIC_JSON) as f:
         d = json.load(f)
     if d.get("kernel_source_hash") != source_hash(KERNEL_SOURCES):
         return None
-    return d.get("bytes_per_launch", {}).get(kernel_key)
+    return d.get("bytes_per_launch", {}).get(pass_key)
 
 
 def to_dev(a, torch):
@@ -66,7 +89,8 @@ def to_dev(a, torch):
 
 
 def time_events(fn, iters, torch):
-    """Average duration (ms) of fn() over `iters` back-to-back launches on the current stream."""
+    """Average duration (ms) of fn() over `iters` back-to-back launches on the current stream
+    (the stream the binding launches on)."""
     st = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -79,53 +103,156 @@ def time_events(fn, iters, torch):
 
 
 def cpu_baseline():
-    """The oracle (plain C, fp64/int64, OpenMP over vectors and rows) on a bounded sample of
-    one step: all six rotation passes at full size, and each of the three products on a
-    128-row slab of its output, scaled linearly to the full product."""
+    """The oracle (plain C, int64 / fp64, OpenMP over vectors and output rows) on one full
+    fwd+bwd step of the same 4096^3 layer: the six rotation + quantisation passes and the three
+    INT8 products with their dequantisation, nothing extrapolated."""
     import oracle as O
     import synth
     x, w, dy = synth.layer(M, N, K, seed=1001)
-    slab = 128
-    t_fq = t_gemm = 0.0
+    t = {"fq": 0.0, "gemm": 0.0}
+
+    def fq(a, axis):
+        t0 = time.perf_counter()
+        r = O.fwht_quant(a, axis, BLOCK, O.I8)
+        t["fq"] += time.perf_counter() - t0
+        return r
+
+    def product(qa, sa, qb, sb):
+        t0 = time.perf_counter()
+        O.dequant(O.gemm_i8(qa, qb).astype(np.float64), sa, sb)
+        t["gemm"] += time.perf_counter() - t0
+
     t0 = time.perf_counter()
-    # forward: rows of X and W along K
-    a = time.perf_counter()
-    qx, sx = O.fwht_quant(x, O.ROWS, BLOCK, O.I8)
-    qw, sw = O.fwht_quant(w, O.ROWS, BLOCK, O.I8)
-    b = time.perf_counter()
-    acc = O.gemm_i8(qx[:slab], qw)
-    O.dequant(acc.astype(np.float64), sx[:slab], sw)
-    c = time.perf_counter()
-    t_fq += b - a
-    t_gemm += (c - b) * (M / slab)
-    # dX: rows of dY along N, columns of W along N
-    a = time.perf_counter()
-    qd, sd = O.fwht_quant(dy, O.ROWS, BLOCK, O.I8)
-    qwt, swt = O.fwht_quant(w, O.COLS, BLOCK, O.I8)
-    b = time.perf_counter()
-    acc = O.gemm_i8(qd[:slab], qwt)
-    O.dequant(acc.astype(np.float64), sd[:slab], swt)
-    c = time.perf_counter()
-    t_fq += b - a
-    t_gemm += (c - b) * (M / slab)
-    # dW: columns of dY and of X along M
-    a = time.perf_counter()
-    qdt, sdt = O.fwht_quant(dy, O.COLS, BLOCK, O.I8)
-    qxt, sxt = O.fwht_quant(x, O.COLS, BLOCK, O.I8)
-    b = time.perf_counter()
-    acc = O.gemm_i8(qdt[:slab], qxt)
-    O.dequant(acc.astype(np.float64), sdt[:slab], sxt)
-    c = time.perf_counter()
-    t_fq += b - a
-    t_gemm += (c - b) * (N / slab)
+    steps = 0
+    while steps < 5 and (steps == 0 or time.perf_counter() - t0 < 10.0):
+        product(*fq(x, O.ROWS), *fq(w, O.ROWS))      # Y = X W^T, rotation along K
+        product(*fq(dy, O.ROWS), *fq(w, O.COLS))     # dX = dY W, rotation along N
+        product(*fq(dy, O.COLS), *fq(x, O.COLS))     # dW = dY^T X, rotation along M
+        steps += 1
     wall = time.perf_counter() - t0
-    est = t_fq + t_gemm
-    return {"value": round(STEP_GOP / 1e3 / est, 6), "unit": "TOP/s",
+    return {"value": round(steps * STEP_GOP / 1e3 / wall, 6), "unit": "TOP/s",
             "cores": O.num_threads(), "kind": "oracle",
-            "sample": (f"one fwd+bwd step of the 4096^3 layer: 6 rotation passes at full size "
-                       f"({t_fq:.2f} s) + the 3 INT8 products on {slab}-row slabs, scaled "
-                       f"linearly to full size ({t_gemm:.1f} s extrapolated); "
-                       f"{wall:.1f} s of CPU work measured")}
+            "sample": (f"{steps} full fwd+bwd step(s) of the 4096^3 layer (seed 1001), repeated "
+                       f"to at least 10 s: rotation passes {t['fq']:.2f} s + INT8 products with "
+                       f"dequant {t['gemm']:.2f} s = {wall:.2f} s wall")}
+
+
+def make_inputs(torch):
+    import synth
+    sets = []
+    for s in range(N_SETS):
+        x, w, dy = synth.layer(M, N, K, seed=1001 + 97 * s)
+        sets.append((to_dev(x, torch), to_dev(w, torch), to_dev(dy, torch)))
+    return sets
+
+
+def measure_kernels(H, torch, sets, iters, with_copy=False):
+    """Per-launch time (ms) of the dominant kernels, in the configuration the step launches
+    them: INT8 GEMM 4096^3 -> bf16, rows pass of X, columns pass of dY (block 256)."""
+    codes = [H.fwht_quant(X, axis=H.ROWS, block=BLOCK) for (X, _, _) in sets[:2]]
+    wcodes = [H.fwht_quant(W, axis=H.ROWS, block=BLOCK) for (_, W, _) in sets[:2]]
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
+    qbuf = torch.empty((M, K), dtype=torch.int8, device="cuda:0")
+    sbuf = torch.empty(max(M, K), dtype=torch.float32, device="cuda:0")
+
+    def gemm(i):
+        H.gemm_i8(codes[i % 2][0], codes[i % 2][1], wcodes[i % 2][0], wcodes[i % 2][1], c=y)
+
+    def rows(i):
+        H.fwht_quant(sets[i % N_SETS][0], axis=H.ROWS, block=BLOCK, q=qbuf, scale=sbuf[:M])
+
+    def cols(i):
+        H.fwht_quant(sets[i % N_SETS][2], axis=H.COLS, block=BLOCK, q=qbuf, scale=sbuf[:N])
+
+    for f in (gemm, rows, cols):
+        for i in range(3):
+            f(i)
+    out = {"gemm_i8_4096": time_events(gemm, iters, torch),
+           "fq_rows_4096": time_events(rows, iters, torch),
+           "fq_cols_4096": time_events(cols, iters, torch)}
+    if with_copy:
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0").normal_()
+        dst = torch.empty_like(src)
+        out["copy_64MiB"] = time_events(lambda i: dst.copy_(src), iters, torch)
+    return out
+
+
+def summarize_stats(path, command, last=0):
+    """rocprofv3 kernel_stats.csv -> text table (per-kernel average duration).  With `last`,
+    the kernel_trace.csv beside it also gives each pass's average over its last `last`
+    dispatches: the back-to-back launches the bench times with HIP events."""
+    with open(path) as f:
+        rows = list(csv.DictReader(f))
+    lines = [f"command: {command}", "",
+             f"{'calls':>6} {'avg us':>9} {'min us':>9} {'max us':>9} {'%':>6}  kernel"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append(f"{int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>9.2f} "
+                     f"{float(r['MinNs']) / 1e3:>9.2f} {float(r['MaxNs']) / 1e3:>9.2f} "
+                     f"{float(r['Percentage']):>6.2f}  {r['Name'][:150]}")
+    trace = path.replace("kernel_stats.csv", "kernel_trace.csv")
+    if last and os.path.exists(trace):
+        with open(trace) as f:
+            tr = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
+        lines += ["", f"per pass, last {last} calls (the event-timed measurement loop):"]
+        for key, pats in PASSES.items():
+            calls = {}
+            for r in tr:
+                if any(p in r["Kernel_Name"] for p in pats):
+                    d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                    calls.setdefault(r["Kernel_Name"], []).append(d)
+            if calls:
+                per = sum(float(np.mean(v[-last:])) for v in calls.values())
+                lines.append(f"  {key:<14} {per:>9.2f} us per call ({len(calls)} kernel(s))")
+    return "\n".join(lines) + "\n"
+
+
+def _pmc_per_call(d, counter):
+    """Average counter value (KiB) per call of each pass, from a counter_collection.csv."""
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    per_kernel = {}
+    for fn in files:
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                per_kernel.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    out = {}
+    for key, pats in PASSES.items():
+        tot = 0.0
+        found = False
+        for name, vals in per_kernel.items():
+            if any(p in name for p in pats):
+                tot += float(np.mean(vals))
+                found = True
+        out[key] = tot if found else None
+    return out
+
+
+def summarize_pmc(fetch_dir, write_dir, command):
+    fetch = _pmc_per_call(fetch_dir, "FETCH_SIZE")
+    write = _pmc_per_call(write_dir, "WRITE_SIZE")
+    # calibration: a device copy of COPY_BYTES reads and writes exactly COPY_BYTES
+    f_scale = COPY_BYTES / (fetch["copy_64MiB"] * 1024.0)
+    w_scale = COPY_BYTES / (write["copy_64MiB"] * 1024.0)
+    algo = {"gemm_i8_4096": GEMM_BYTES, "fq_rows_4096": FQ_BYTES, "fq_cols_4096": FQ_BYTES}
+    res = {"kernel_source_hash": source_hash(KERNEL_SOURCES), "command": command,
+           "fetch_scale": f_scale, "write_scale": w_scale, "bytes_per_launch": {},
+           "fetch_kib_raw": fetch, "write_kib_raw": write}
+    lines = [f"command: {command}",
+             f"calibration ({COPY_BYTES >> 20} MiB device copy): FETCH_SIZE x{f_scale:.3f}, "
+             f"WRITE_SIZE x{w_scale:.3f} -> bytes", "",
+             f"{'pass':<14} {'read MB':>9} {'write MB':>9} {'total MB':>9} {'algorithmic MB':>15}"]
+    for key in ("gemm_i8_4096", "fq_rows_4096", "fq_cols_4096"):
+        if fetch[key] is None or write[key] is None:
+            continue
+        rd = fetch[key] * 1024.0 * f_scale
+        wr = write[key] * 1024.0 * w_scale
+        res["bytes_per_launch"][key] = int(round(rd + wr))
+        lines.append(f"{key:<14} {rd / 1e6:>9.2f} {wr / 1e6:>9.2f} {(rd + wr) / 1e6:>9.2f} "
+                     f"{algo[key] / 1e6:>15.2f}")
+    return res, "\n".join(lines) + "\n"
 
 
 def main():
@@ -135,7 +262,31 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--kernel-iters", type=int, default=60)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernels-only", action="store_true")
+    ap.add_argument("--summarize-stats", metavar="CSV")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--command", default="", help="profiling command recorded in a summary")
+    ap.add_argument("--out", help="summary file to write")
+    ap.add_argument("--last", type=int, default=0, help="trace calls per pass to average")
     args = ap.parse_args()
+
+    if args.summarize_stats:
+        text = summarize_stats(args.summarize_stats, args.command, args.last)
+        if args.out:
+            with open(args.out, "w") as f:
+                f.write(text)
+        print(text, end="")
+        return
+    if args.summarize_pmc:
+        res, text = summarize_pmc(*args.summarize_pmc, args.command)
+        with open(TRAFFIC_JSON, "w") as f:
+            json.dump(res, f, indent=1)
+        if args.out:
+            with open(args.out, "w") as f:
+                f.write(text)
+        print(text, end="")
+        return
+
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -143,13 +294,16 @@ def main():
 
     import torch
     import hadamard_rotated_precision_halo_amd as H
-    import synth
 
     torch.cuda.set_device(0)
-    sets = []
-    for s in range(N_SETS):
-        x, w, dy = synth.layer(M, N, K, seed=1001 + 97 * s)
-        sets.append((to_dev(x, torch), to_dev(w, torch), to_dev(dy, torch)))
+    sets = make_inputs(torch)
+
+    if args.kernels_only:
+        t = measure_kernels(H, torch, sets, args.kernel_iters, with_copy=True)
+        print(json.dumps({k: round(v * 1e3, 3) for k, v in t.items()} | {"unit": "us"}),
+              flush=True)
+        return
+
     y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
     dx = torch.empty((M, K), dtype=torch.bfloat16, device="cuda:0")
     dw = torch.empty((N, K), dtype=torch.bfloat16, device="cuda:0")
@@ -165,33 +319,31 @@ def main():
 
     for i in range(args.warmup):
         step(i)
+    st = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        evs[i].record(st)
         step(i)
+    evs[-1].record(st)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_step = elapsed * 1e3 / args.steps
     value = STEP_GOP / (ms_step * 1e-3) / 1e3  # TOP/s
+    per_step = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
 
     # ---- per-kernel measurements (same kernels, same shapes, HIP events on the stream) ----
-    codes = [H.fwht_quant(X, axis=H.ROWS, block=BLOCK) for (X, _, _) in sets[:2]]
-    wcodes = [H.fwht_quant(W, axis=H.ROWS, block=BLOCK) for (_, W, _) in sets[:2]]
-    it = args.kernel_iters
-    for i in range(3):
-        H.gemm_i8(codes[i % 2][0], codes[i % 2][1], wcodes[i % 2][0], wcodes[i % 2][1], c=y)
-    t_gemm = time_events(lambda i: H.gemm_i8(codes[i % 2][0], codes[i % 2][1],
-                                             wcodes[i % 2][0], wcodes[i % 2][1], c=y), it, torch)
-    qbuf = torch.empty((M, K), dtype=torch.int8, device="cuda:0")
-    sbuf = torch.empty(max(M, K), dtype=torch.float32, device="cuda:0")
-    t_rows = time_events(lambda i: H.fwht_quant(sets[i % N_SETS][0], axis=H.ROWS, block=BLOCK,
-                                                q=qbuf, scale=sbuf[:M]), it, torch)
-    t_cols = time_events(lambda i: H.fwht_quant(sets[i % N_SETS][2], axis=H.COLS, block=BLOCK,
-                                                q=qbuf, scale=sbuf[:N]), it, torch)
-    gemm_tops = 2 * M * N * K / (t_gemm * 1e-3) / 1e12
-    fq_bytes = M * K * (2 + 1) + 4 * M
-    rows_gbs = fq_bytes / (t_rows * 1e-3) / 1e9
-    cols_gbs = fq_bytes / (t_cols * 1e-3) / 1e9
+    t = measure_kernels(H, torch, sets, args.kernel_iters)
+    t_gemm, t_rows, t_cols = t["gemm_i8_4096"], t["fq_rows_4096"], t["fq_cols_4096"]
+    gemm_tops = GEMM_OPS / (t_gemm * 1e-3) / 1e12
+    rows_gbs = FQ_BYTES / (t_rows * 1e-3) / 1e9
+    cols_gbs = FQ_BYTES / (t_cols * 1e-3) / 1e9
+
+    def hbm(gbs, ms, key):
+        return {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": load_traffic(key),
+                "ms_per_launch": round(ms, 5), "algorithmic_bytes": FQ_BYTES}
 
     result = {
         "metric": METRIC,
@@ -210,21 +362,16 @@ def main():
                                "bf16, INT8 codes, FWHT block 256",
                    "m": M, "n": N, "k": K, "block": BLOCK, "io": "bf16", "codes": "int8",
                    "input_sets": N_SETS},
+        "step_ms": {"p10": round(float(np.percentile(per_step, 10)), 4),
+                    "p50": round(float(np.percentile(per_step, 50)), 4),
+                    "p90": round(float(np.percentile(per_step, 90)), 4)},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 2), "peak": PEAK_INT8_TOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
                      "traffic": load_traffic("gemm_i8_4096"),
                      "kernel": "gemm_kernel<INT8, bf16 out> 4096x4096x4096",
-                     "ms_per_launch": round(t_gemm, 5)},
-        "fwht_quant": {
-            "rows": {"bound": "hbm", "achieved": round(rows_gbs, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(rows_gbs / PEAK_HBM_GBS, 4),
-                     "traffic": load_traffic("fq_rows_4096"), "ms_per_launch": round(t_rows, 5),
-                     "algorithmic_bytes": fq_bytes},
-            "cols": {"bound": "hbm", "achieved": round(cols_gbs, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(cols_gbs / PEAK_HBM_GBS, 4),
-                     "traffic": load_traffic("fq_cols_4096"), "ms_per_launch": round(t_cols, 5),
-                     "algorithmic_bytes": fq_bytes},
-        },
+                     "ms_per_launch": round(t_gemm, 5), "algorithmic_ops": GEMM_OPS},
+        "fwht_quant": {"rows": hbm(rows_gbs, t_rows, "fq_rows_4096"),
+                       "cols": hbm(cols_gbs, t_cols, "fq_cols_4096")},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline()
