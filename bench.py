@@ -49,7 +49,7 @@ GEMM_BYTES = 2 * M * K + 2 * M * N + 4 * (M + N)  # both code operands, bf16 out
 COPY_BYTES = 64 << 20                       # calibration copy: 64 MiB read + 64 MiB written
 KERNEL_SOURCES = ["hadamard_rotated_precision_halo_amd/csrc/gemm.hip",
                   "hadamard_rotated_precision_halo_amd/csrc/fwht_quant.hip",
-                  "hadamard_rotated_precision_halo_amd/csrc/fwht_rows.hip",
+                  "hadamard_rotated_precision_halo_amd/csrc/fwht_wave.hip",
                   "hadamard_rotated_precision_halo_amd/csrc/halo_device.h"]
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic_4096.json")
 
@@ -59,7 +59,7 @@ PASSES = {
     "gemm_i8_4096": ["halo::gemm_kernel<0"],
     "fq_rows_4096": ["halo::fq_rows2_kernel<unsigned short, 256, 0>"],
     "fq_cols_4096": ["halo::fq_cols_kernel<unsigned short, 256, 0", "halo::fill_zero_kernel",
-                     "halo::finalize_scale_kernel", "halo::fq_cols2_kernel<unsigned short, 256, 0"],
+                     "halo::finalize_scale_kernel", "halo::fq_cols2_kernel<256, 0>"],
     "copy_64MiB": ["__amd_rocclr_copyBuffer"],
 }
 
@@ -154,6 +154,8 @@ def measure_kernels(H, torch, sets, iters, with_copy=False):
     y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
     qbuf = torch.empty((M, K), dtype=torch.int8, device="cuda:0")
     sbuf = torch.empty(max(M, K), dtype=torch.float32, device="cuda:0")
+    wsc = torch.empty(max(H.fwht_quant_workspace_bytes(M, N, H.COLS, BLOCK), 256),
+                      dtype=torch.uint8, device="cuda:0")
 
     def gemm(i):
         H.gemm_i8(codes[i % 2][0], codes[i % 2][1], wcodes[i % 2][0], wcodes[i % 2][1], c=y)
@@ -162,7 +164,8 @@ def measure_kernels(H, torch, sets, iters, with_copy=False):
         H.fwht_quant(sets[i % N_SETS][0], axis=H.ROWS, block=BLOCK, q=qbuf, scale=sbuf[:M])
 
     def cols(i):
-        H.fwht_quant(sets[i % N_SETS][2], axis=H.COLS, block=BLOCK, q=qbuf, scale=sbuf[:N])
+        H.fwht_quant(sets[i % N_SETS][2], axis=H.COLS, block=BLOCK, q=qbuf, scale=sbuf[:N],
+                     workspace=wsc)
 
     for f in (gemm, rows, cols):
         for i in range(3):

@@ -23,8 +23,8 @@ ROWS, COLS = 0, 1
 STATUS = {0: "HALO_OK", 1: "HALO_ERR_NULL", 2: "HALO_ERR_SHAPE", 3: "HALO_ERR_BLOCK",
           4: "HALO_ERR_DTYPE", 5: "HALO_ERR_ALIGN", 6: "HALO_ERR_WORKSPACE", 7: "HALO_ERR_HIP"}
 
-EXPORTS = ("halo_fwht_quant", "halo_gemm_i8", "halo_gemm_fp8", "halo_linear_workspace_bytes",
-           "halo_linear_fwd", "halo_linear_bwd", "halo_status_str")
+EXPORTS = ("halo_fwht_quant", "halo_fwht_quant_workspace_bytes", "halo_gemm_i8", "halo_gemm_fp8",
+           "halo_linear_workspace_bytes", "halo_linear_fwd", "halo_linear_bwd", "halo_status_str")
 
 _TORCH_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.int8: I8,
                torch.float8_e4m3fn: E4M3, torch.float8_e5m2: E5M2, torch.int32: I32}
@@ -49,7 +49,9 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         i64, vp, i32, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
         e = ctypes.c_int  # enums
-        L.halo_fwht_quant.argtypes = [vp, e, i64, i64, i64, e, i32, e, vp, i64, vp, vp]
+        L.halo_fwht_quant.argtypes = [vp, e, i64, i64, i64, e, i32, e, vp, i64, vp, vp, sz, vp]
+        L.halo_fwht_quant_workspace_bytes.argtypes = [i64, i64, e, i32, e]
+        L.halo_fwht_quant_workspace_bytes.restype = sz
         L.halo_gemm_i8.argtypes = [vp, i64, vp, vp, i64, vp, i64, i64, i64, vp, e, i64, vp]
         L.halo_gemm_fp8.argtypes = [vp, e, i64, vp, vp, e, i64, vp, i64, i64, i64, vp, e, i64, vp]
         L.halo_linear_workspace_bytes.argtypes = [i64, i64, i64, e, ctypes.c_int]
@@ -102,12 +104,20 @@ def _ld(t):
     return t.stride(0)
 
 
-def fwht_quant(x, axis=ROWS, block=256, q_dtype=torch.int8, q=None, scale=None, stream=None):
+def fwht_quant_workspace_bytes(rows, cols, axis, block, x_dtype=torch.bfloat16):
+    return int(lib().halo_fwht_quant_workspace_bytes(rows, cols, axis, int(block),
+                                                     _code(x_dtype)))
+
+
+def fwht_quant(x, axis=ROWS, block=256, q_dtype=torch.int8, q=None, scale=None, workspace=None,
+               stream=None):
     """Rotate + quantise the rows (axis ROWS) or columns (axis COLS) of x.
 
     Returns (q, scale): q is [rows x cols] (ROWS) or [cols x rows] (COLS) of q_dtype
     (torch.int8 / float8_e4m3fn / float8_e5m2, or torch.float32 for the rotated values
-    themselves), scale is float32 with one entry per vector.
+    themselves), scale is float32 with one entry per vector.  `workspace` is the optional
+    scratch of the single-read columns pass: a uint8 device tensor, allocated here when None
+    and the shape can use one; pass False to run without it.
     """
     rows, cols = x.shape
     nvec, L = (rows, cols) if axis == ROWS else (cols, rows)
@@ -115,8 +125,19 @@ def fwht_quant(x, axis=ROWS, block=256, q_dtype=torch.int8, q=None, scale=None, 
         q = torch.empty((nvec, L), dtype=q_dtype, device=x.device)
     if scale is None:
         scale = torch.empty(nvec, dtype=torch.float32, device=x.device)
+    if workspace is False:
+        ws_ptr, ws_bytes = None, 0
+    else:
+        need = fwht_quant_workspace_bytes(rows, cols, axis, block, x.dtype)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        if workspace is None:
+            ws_ptr, ws_bytes = None, 0
+        else:
+            ws_ptr, ws_bytes = _ptr(workspace), workspace.numel()
     st = lib().halo_fwht_quant(_ptr(x), _code(x.dtype), rows, cols, _ld(x), axis, int(block),
-                               _code(q.dtype), _ptr(q), _ld(q), _ptr(scale), _stream(stream))
+                               _code(q.dtype), _ptr(q), _ld(q), _ptr(scale), ws_ptr, ws_bytes,
+                               _stream(stream))
     _check(st, "halo_fwht_quant")
     return q, scale
 

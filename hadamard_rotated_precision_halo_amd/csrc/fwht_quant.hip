@@ -415,8 +415,17 @@ int64_t fq_rows_max_len(int block) {
   }
 }
 
-hipError_t launch_fwht_quant(const FqArgs& a, int in_bf16, int qt, int axis, hipStream_t st) {
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwht_quant(const FqArgs& a, int in_bf16, int qt, int axis, void* ws,
+                             size_t ws_bytes, hipStream_t st) {
   if (axis == 0 && fq_rows2_supported(a.len, a.block)) return launch_fq_rows2(a, in_bf16, qt, st);
+  if (axis == 1 && fq_cols2_supported(a.len, a.nvec, a.block, in_bf16, ws_bytes))
+    return launch_fq_cols2(a, qt, ws, st);
   if (in_bf16) {
     switch (qt) {
       case 0: return dispatch_block<uint16_t, 0>(a, axis, st);

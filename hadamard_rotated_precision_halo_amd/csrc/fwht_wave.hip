@@ -1,0 +1,614 @@
+// fwht_wave.hip -- rotation + quantisation with one wave per 4096-element slice, for gfx950:
+// rows (the contiguous axis) and columns (the strided axis, codes written transposed).
+//
+// What is computed is the same as in fwht_quant.hip ("QWHA方法：基于Walsh-Hadamard变换的高效
+// 大模型微调技术" s2.1-s2.2, s3.1: natural-order butterflies over blocks of B contiguous indices
+// of each vector, one absmax scale per vector): this file only changes how the work maps onto
+// the hardware.
+//
+// Wave slice.  A wave holds 4096 elements of one or more vectors, 64 per lane, as 8 chunks of
+// 8 consecutive elements.  For B >= 64, g = B / 64 lanes share a block and chunk j of lane lo
+// sits at block offset (j * g + lo) * 8, so the 3 low index bits and the 3 high index bits of
+// a block are butterflied in registers and only log2(g) stages cross lanes; for B < 64 a lane
+// holds 64 / B whole blocks.  The two lowest lane stages are single v_fmac_f32 instructions
+// with a DPP quad permutation on the partner value (z <- z + c * z[lane ^ s], c = +1 on the
+// lower and -1 on the upper lane; the upper lane then holds the negated difference, a sign
+// folded into its quantisation multiplier); higher lane stages use ds_swizzle / permlane.
+// All stages run in increasing index-bit order with the same operand order as a sequential
+// fp32 butterfly, so the values are bit-identical to it.
+//
+// Rows kernel.  A wave reads its slice straight from HBM: 4096 / L whole rows when L <= 4096
+// (no barrier), or a workgroup of ceil(L / 4096) waves per row with one LDS exchange of wave
+// maxima.
+//
+// Columns kernel.  A workgroup of 16 waves owns a tile of C = 65536 / R columns by R rows
+// (R = 1024 for long columns): each lane loads 8 consecutive rows of 8 adjacent columns with
+// full 128-byte row segments, transposes them in registers with v_perm_b32 (8 rows of one
+// column in one 16-byte word) and writes them to LDS in the order the compute waves read them
+// (bank-conflict-free by an XOR swizzle); the waves then run the slice computation on column
+// segments of R rows.  When a column is longer than R, the P = rows / R workgroups of one
+// column strip combine their partial maxima through device-scope atomics: each max-reduces
+// its maxima into the strip's column maxima, increments the strip's arrival counter, and
+// waits until all P have arrived.  The
+// P tasks of a strip are consecutive workgroups and workgroups are dispatched in index order,
+// so the wait always ends (see the launcher); a bounded spin guards it regardless.  The input
+// is read once and the codes written once.
+#include "halo_device.h"
+#include "halo_kernels.h"
+
+#include <mutex>
+
+namespace halo {
+
+// ---------------------------------------------------------------------------
+// wave-slice helpers
+// ---------------------------------------------------------------------------
+
+// z[i] <- z[i] + c * z[i] of lane ^ (1 << S), S = 0 or 1, for 8 values: one v_fmac_f32 with a
+// DPP quad permutation of src0 each.  The leading s_nop covers the two wait states a DPP read
+// needs after a VALU write of its source; inside the block each source was written earlier.
+template <int S>
+__device__ __forceinline__ void dpp_fmac8(float* z, float c) {
+  if constexpr (S == 0) {
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %0, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %1, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %2, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %3, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %4, %4, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %5, %5, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %6, %6, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %7, %7, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
+        : "+v"(z[0]), "+v"(z[1]), "+v"(z[2]), "+v"(z[3]), "+v"(z[4]), "+v"(z[5]), "+v"(z[6]),
+          "+v"(z[7])
+        : "v"(c));
+  } else {
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %0, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %1, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %2, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %3, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %4, %4, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %5, %5, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %6, %6, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %7, %7, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
+        : "+v"(z[0]), "+v"(z[1]), "+v"(z[2]), "+v"(z[3]), "+v"(z[4]), "+v"(z[5]), "+v"(z[6]),
+          "+v"(z[7])
+        : "v"(c));
+  }
+}
+
+// Butterflies between in-register values at index distance D (the values of one lane are
+// v[j * 8 + e]; D is a power of two, the pair is (t, t + D) within groups of 2D).
+template <int D>
+__device__ __forceinline__ void reg_stage(float* v) {
+#pragma unroll
+  for (int i = 0; i < 64; i += 2 * D)
+#pragma unroll
+    for (int t = i; t < i + D; ++t) {
+      const float p = v[t], q = v[t + D];
+      v[t] = p + q;
+      v[t + D] = p - q;
+    }
+}
+
+// Lane geometry of a block of B elements inside a wave slice.
+template <int B>
+struct Slice {
+  static constexpr int G = B >= 64 ? B / 64 : 1;  // lanes per block
+  // element offset of chunk j of `lane` within the 4096-element slice
+  __device__ static __forceinline__ int off(int lane, int j) {
+    if constexpr (B >= 64) return (lane / G) * B + (j * G + lane % G) * 8;
+    else return lane * 64 + j * 8;
+  }
+  // inverse: the lane and chunk holding slice offset o (a multiple of 8)
+  __device__ static __forceinline__ void where(int o, int& lane, int& j) {
+    if constexpr (B >= 64) {
+      const int r = (o % B) / 8;
+      lane = (o / B) * G + r % G;
+      j = r / G;
+    } else {
+      lane = o / 64;
+      j = (o % 64) / 8;
+    }
+  }
+};
+
+// Rotate the 64 values of a lane in place; returns the sign the DPP stages left on them.
+template <int B>
+__device__ __forceinline__ float rotate64(float* v, int lane) {
+  constexpr int G = Slice<B>::G;
+  const int lo = lane % G;
+  if constexpr (B >= 2) reg_stage<1>(v);
+  if constexpr (B >= 4) reg_stage<2>(v);
+  if constexpr (B >= 8) reg_stage<4>(v);
+  float sgn = 1.f;
+  if constexpr (B >= 64) {
+    if constexpr (G >= 2) {
+      const float c = (lo & 1) ? -1.f : 1.f;
+#pragma unroll
+      for (int i = 0; i < 64; i += 8) dpp_fmac8<0>(&v[i], c);
+      sgn *= c;
+    }
+    if constexpr (G >= 4) {
+      const float c = (lo & 2) ? -1.f : 1.f;
+#pragma unroll
+      for (int i = 0; i < 64; i += 8) dpp_fmac8<1>(&v[i], c);
+      sgn *= c;
+    }
+    if constexpr (G >= 8) {
+      const float c = (lo & 4) ? -1.f : 1.f;
+#pragma unroll
+      for (int i = 0; i < 64; ++i) v[i] = xbutterfly<2>(v[i], c);
+    }
+    if constexpr (G >= 16) {
+      const float c = (lo & 8) ? -1.f : 1.f;
+#pragma unroll
+      for (int i = 0; i < 64; ++i) v[i] = xbutterfly<3>(v[i], c);
+    }
+    if constexpr (G >= 32) {
+      const float c = (lo & 16) ? -1.f : 1.f;
+#pragma unroll
+      for (int i = 0; i < 64; ++i) v[i] = xbutterfly<4>(v[i], c);
+    }
+    if constexpr (G >= 64) {
+      const float c = (lo & 32) ? -1.f : 1.f;
+#pragma unroll
+      for (int i = 0; i < 64; ++i) v[i] = xbutterfly<5>(v[i], c);
+    }
+    // top bits: the 8 chunks of the lane
+    reg_stage<8>(v);
+    reg_stage<16>(v);
+    reg_stage<32>(v);
+  } else {
+    // blocks of 16 or 32 elements: chunk bits inside the block
+    if constexpr (B >= 16) reg_stage<8>(v);
+    if constexpr (B >= 32) reg_stage<16>(v);
+  }
+  return sgn;
+}
+
+__device__ __forceinline__ float absmax64(const float* v) {
+  float mx = 0.f;
+#pragma unroll
+  for (int i = 0; i < 64; i += 2)
+    mx = __builtin_fmaxf(__builtin_fmaxf(mx, fabsf(v[i])), fabsf(v[i + 1]));
+  return mx;
+}
+
+// Maximum over the lanes whose low `lane_bits` lane-index bits vary (the lanes of one vector).
+__device__ __forceinline__ float lane_max(float v, int lane_bits) {
+  if (lane_bits > 0) v = xmax<0>(v);
+  if (lane_bits > 1) v = xmax<1>(v);
+  if (lane_bits > 2) v = xmax<2>(v);
+  if (lane_bits > 3) v = xmax<3>(v);
+  if (lane_bits > 4) v = xmax<4>(v);
+  if (lane_bits > 5) v = xmax<5>(v);
+  return v;
+}
+
+// Encoders for 8 consecutive values (one chunk) -> 8 bytes of codes.
+template <int QT>
+__device__ __forceinline__ uint2 encode8(const float* y, float m) {
+  uint2 w;
+  if constexpr (QT == 0) {
+    uint32_t t[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t[e] = __float_as_uint(__builtin_fmaf(y[e], m, 12582912.0f));
+    // v_perm_b32: byte 0 of each of two dwords -> bytes 0 and 1 (selector 0x0c zeroes)
+    const uint32_t p01 = __builtin_amdgcn_perm(t[1], t[0], 0x0c0c0400u);
+    const uint32_t p23 = __builtin_amdgcn_perm(t[3], t[2], 0x0c0c0400u);
+    const uint32_t p45 = __builtin_amdgcn_perm(t[5], t[4], 0x0c0c0400u);
+    const uint32_t p67 = __builtin_amdgcn_perm(t[7], t[6], 0x0c0c0400u);
+    w.x = __builtin_amdgcn_perm(p23, p01, 0x05040100u);
+    w.y = __builtin_amdgcn_perm(p67, p45, 0x05040100u);
+  } else {
+    // v_cvt_pk_{fp8,bf8}_f32 writes one 16-bit half of its destination and keeps the other
+    if constexpr (QT == 1) {
+      w.x = __builtin_amdgcn_cvt_pk_fp8_f32(mulz(y[2], m), mulz(y[3], m),
+                                            __builtin_amdgcn_cvt_pk_fp8_f32(mulz(y[0], m), mulz(y[1], m), 0, false), true);
+      w.y = __builtin_amdgcn_cvt_pk_fp8_f32(mulz(y[6], m), mulz(y[7], m),
+                                            __builtin_amdgcn_cvt_pk_fp8_f32(mulz(y[4], m), mulz(y[5], m), 0, false), true);
+    } else {
+      w.x = __builtin_amdgcn_cvt_pk_bf8_f32(mulz(y[2], m), mulz(y[3], m),
+                                            __builtin_amdgcn_cvt_pk_bf8_f32(mulz(y[0], m), mulz(y[1], m), 0, false), true);
+      w.y = __builtin_amdgcn_cvt_pk_bf8_f32(mulz(y[6], m), mulz(y[7], m),
+                                            __builtin_amdgcn_cvt_pk_bf8_f32(mulz(y[4], m), mulz(y[5], m), 0, false), true);
+    }
+  }
+  return w;
+}
+
+// Store chunk j of the lane (8 values y) at element `idx` of the code array: 8 code bytes, or
+// 8 fp32 rotated values for the value mode (QT 3).
+template <int QT>
+__device__ __forceinline__ void store_chunk8(void* q, int64_t idx, const float* y, float mul) {
+  if constexpr (QT == 3) {
+    float4* d = reinterpret_cast<float4*>(reinterpret_cast<float*>(q) + idx);
+    d[0] = make_float4(mulz(y[0], mul), mulz(y[1], mul), mulz(y[2], mul), mulz(y[3], mul));
+    d[1] = make_float4(mulz(y[4], mul), mulz(y[5], mul), mulz(y[6], mul), mulz(y[7], mul));
+  } else {
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(q) + idx) = encode8<QT>(y, mul);
+  }
+}
+
+// Quantisation multiplier and stored scale from the vector's absmax.
+template <int QT>
+__device__ __forceinline__ float quant_mul(const FqArgs& a, float mx) {
+  if constexpr (QT == 3) return a.inv_sqrt_b;
+  else return mx > 0.f ? a.qmax / mx : 0.f;
+}
+template <int QT>
+__device__ __forceinline__ float stored_scale(const FqArgs& a, float mx) {
+  return QT == 3 ? mx * a.inv_sqrt_b : mx / a.denom;
+}
+
+// ---------------------------------------------------------------------------
+// rows kernel
+// ---------------------------------------------------------------------------
+
+// QT: 0 INT8, 1 E4M3, 2 E5M2, 3 fp32 rotated values.
+// multi = 1: one row per workgroup, wave w owns columns [4096 w, 4096 (w + 1)).
+// multi = 0: 4096 % L == 0, each wave owns 4096 / L whole rows.
+template <typename Tin, int B, int QT>
+__global__ __launch_bounds__(1024) void fq_rows2_kernel(FqArgs a, int multi) {
+  using S = Slice<B>;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+
+  int64_t row;
+  int col0;  // column of the slice start within the row
+  int row_lanes_log2;
+  bool valid;
+  if (multi) {
+    row = blockIdx.x;
+    col0 = w * 4096;
+    row_lanes_log2 = 6;
+    valid = col0 + S::off(lane, 0) < a.len;  // lanes past the row end idle (a whole lane or none)
+  } else {
+    const int L = (int)a.len;
+    const int rpw = 4096 / L;              // rows per wave
+    const int first = (blockIdx.x * nw + w) * rpw;
+    const int r_in_wave = S::off(lane, 0) / L;
+    row = (int64_t)first + r_in_wave;
+    col0 = -r_in_wave * L;                 // so that col0 + off(lane, j) is the column
+    row_lanes_log2 = 31 - __builtin_clz((unsigned)(L / 64));
+    valid = row < a.nvec;
+  }
+  const Tin* __restrict__ xin = reinterpret_cast<const Tin*>(a.x);
+  // idle lanes (past the row end, or past the last row) read the first chunk of row 0
+  const Tin* rp = xin + (valid ? row : 0) * a.ldx;
+
+  float v[64];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int c = valid ? col0 + S::off(lane, j) : 0;
+    load8<Tin>(rp + c, &v[j * 8]);
+  }
+  const float sgn = rotate64<B>(v, lane);
+
+  float mx = valid ? absmax64(v) : 0.f;
+  mx = lane_max(mx, row_lanes_log2);
+  if (multi && nw > 1) {
+    __shared__ float s_wmax[16];
+    if (lane == 0) s_wmax[w] = mx;
+    __syncthreads();
+    mx = 0.f;
+    for (int i = 0; i < nw; ++i) mx = __builtin_fmaxf(mx, s_wmax[i]);
+  }
+
+  const bool writer = multi ? (w == 0 && lane == 0) : ((lane & ((1 << row_lanes_log2) - 1)) == 0);
+  if (valid && writer) a.scale[row] = stored_scale<QT>(a, mx);
+  if (!valid) return;
+  const float mul = quant_mul<QT>(a, mx) * sgn;
+  const int64_t base = row * a.ldq + col0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) store_chunk8<QT>(a.q, base + S::off(lane, j), &v[j * 8], mul);
+}
+
+template <typename Tin, int B, int QT>
+static hipError_t launch_rows2_t(const FqArgs& a, hipStream_t st) {
+  const int64_t L = a.len;
+  if (a.nvec == 0) return hipSuccess;
+  if (L >= 4096) {
+    const int nw = (int)((L + 4095) / 4096);
+    hipLaunchKernelGGL((fq_rows2_kernel<Tin, B, QT>), dim3((unsigned)a.nvec), dim3(64 * nw), 0, st,
+                       a, 1);
+  } else {
+    const int64_t rpw = 4096 / L;
+    const int64_t waves = (a.nvec + rpw - 1) / rpw;
+    const int nw = 4;
+    hipLaunchKernelGGL((fq_rows2_kernel<Tin, B, QT>), dim3((unsigned)((waves + nw - 1) / nw)),
+                       dim3(64 * nw), 0, st, a, 0);
+  }
+  return hipGetLastError();
+}
+
+bool fq_rows2_supported(int64_t len, int block) {
+  if (len <= 0 || len % 64 != 0 || len > 16 * 4096) return false;
+  if (len < 4096 && 4096 % len != 0) return false;
+  return block >= 1 && block <= 4096 && len % block == 0;
+}
+
+// ---------------------------------------------------------------------------
+// columns kernel
+// ---------------------------------------------------------------------------
+
+constexpr int kColsLdsBytes = 16 * 512 * 16;  // 16 waves x 512 chunks of 16 bytes
+
+// LDS chunk (16-byte slot) of chunk j of `lane` in wave w: lane-major per wave, so the compute
+// reads are contiguous; the XOR on the low 4 lane bits spreads the transposing writes over all
+// 64 banks.
+template <int B>
+__device__ __forceinline__ int lds_slot(int w, int lane, int j) {
+  constexpr int JA = B >= 64 ? B / 64 : 1;
+  return w * 512 + j * 64 + (lane ^ (((j * JA) ^ w) & 15));
+}
+
+// Columns-axis plan: R rows per task (the slice length of a wave's column segment), P tasks
+// per column strip of C = 65536 / R columns.
+struct ColsGeo {
+  int R, P, C;
+  int64_t strips;
+};
+
+__device__ __forceinline__ uint32_t bf16_pair(uint32_t lo_word, uint32_t hi_word, int half) {
+  // column `half` (0: low 16 bits, 1: high 16 bits) of two rows -> one dword, lower row first
+  return __builtin_amdgcn_perm(hi_word, lo_word, half ? 0x07060302u : 0x05040100u);
+}
+
+template <int B, int QT>
+__global__ __launch_bounds__(1024) void fq_cols2_kernel(FqArgs a, int R, int P, int C,
+                                                        int64_t tasks, float* colmax,
+                                                        uint32_t* arrive) {
+  extern __shared__ __attribute__((aligned(16))) uint4 lds[];
+  using S = Slice<B>;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int64_t ncols = a.nvec;
+  const int CC = C / 8;                      // 16-byte column chunks per row of the tile
+  const int cpw = 4096 / R;                  // column segments per wave
+  const int cc = t % CC, rg = t / CC;        // loader: column chunk, group of 8 rows
+  const int row_lanes_log2 = 31 - __builtin_clz((unsigned)(R / 64));
+  const uint16_t* __restrict__ xin = reinterpret_cast<const uint16_t*>(a.x);
+
+  for (int64_t task = blockIdx.x; task < tasks; task += gridDim.x) {
+    const int64_t strip = task / P;
+    const int part = (int)(task % P);
+    const int64_t c0 = strip * C;
+
+    // ---- load 8 rows x 8 columns, transpose, write to LDS ------------------------------
+    {
+      const int64_t col = c0 + cc * 8;
+      const bool cvalid = col < ncols;
+      const uint16_t* p = xin + ((int64_t)part * R + rg * 8) * a.ldx + (cvalid ? col : 0);
+      uint4 raw[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) raw[i] = *reinterpret_cast<const uint4*>(p + i * a.ldx);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int cl = cc * 8 + e;             // column within the tile
+        const int wr = cl / cpw, ciw = cl % cpw;
+        int ln, j;
+        S::where(ciw * R + rg * 8, ln, j);
+        uint32_t d0, d1, d2, d3;
+        if ((e >> 1) == 0) {
+          d0 = bf16_pair(raw[0].x, raw[1].x, e & 1); d1 = bf16_pair(raw[2].x, raw[3].x, e & 1);
+          d2 = bf16_pair(raw[4].x, raw[5].x, e & 1); d3 = bf16_pair(raw[6].x, raw[7].x, e & 1);
+        } else if ((e >> 1) == 1) {
+          d0 = bf16_pair(raw[0].y, raw[1].y, e & 1); d1 = bf16_pair(raw[2].y, raw[3].y, e & 1);
+          d2 = bf16_pair(raw[4].y, raw[5].y, e & 1); d3 = bf16_pair(raw[6].y, raw[7].y, e & 1);
+        } else if ((e >> 1) == 2) {
+          d0 = bf16_pair(raw[0].z, raw[1].z, e & 1); d1 = bf16_pair(raw[2].z, raw[3].z, e & 1);
+          d2 = bf16_pair(raw[4].z, raw[5].z, e & 1); d3 = bf16_pair(raw[6].z, raw[7].z, e & 1);
+        } else {
+          d0 = bf16_pair(raw[0].w, raw[1].w, e & 1); d1 = bf16_pair(raw[2].w, raw[3].w, e & 1);
+          d2 = bf16_pair(raw[4].w, raw[5].w, e & 1); d3 = bf16_pair(raw[6].w, raw[7].w, e & 1);
+        }
+        lds[lds_slot<B>(wr, ln, j)] = make_uint4(d0, d1, d2, d3);
+      }
+    }
+    __syncthreads();
+
+    // ---- rotate the wave's column segments ------------------------------------------------
+    float v[64];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) unpack_bf16x8(lds[lds_slot<B>(w, lane, j)], &v[j * 8]);
+    const float sgn = rotate64<B>(v, lane);
+    const int seg = S::off(lane, 0) / R;       // column segment of this lane within the wave
+    const int64_t col = c0 + w * cpw + seg;
+    const bool valid = col < ncols;
+    float mx = lane_max(absmax64(v), row_lanes_log2);
+    const bool writer = (lane & ((1 << row_lanes_log2) - 1)) == 0;
+
+    // ---- column maxima of a strip split over P tasks ---------------------------------------
+    // Device-scope atomics only (they are performed at the device's coherence point, across
+    // XCDs): each task max-reduces its partial maxima into colmax (non-negative floats order
+    // like their bit patterns) with returning atomics, so they have been performed before the
+    // barrier; one thread then counts the task in, waits for all P, and every lane reads the
+    // column maxima back with atomic loads.  No cache-wide fence is needed.
+    if (P > 1) {
+      uint32_t* cm = reinterpret_cast<uint32_t*>(colmax);
+      uint32_t seen = 0;
+      if (valid && writer)
+        seen = __hip_atomic_fetch_max(&cm[col], __float_as_uint(mx), __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+      // the returned value is consumed, so the atomic has completed before the barrier
+      if (__builtin_expect(seen == 0xffffffffu, 0)) mx = __uint_as_float(seen);
+      __syncthreads();
+      if (t == 0) {
+        __hip_atomic_fetch_add(&arrive[strip], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // the other tasks of this strip are dispatched (workgroups start in index order), so
+        // the count reaches P; the bound only guards against a broken launch
+        for (uint32_t it = 0; it < (1u << 20); ++it) {
+          if (__hip_atomic_load(&arrive[strip], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >=
+              (uint32_t)P)
+            break;
+          __builtin_amdgcn_s_sleep(2);
+        }
+      }
+      __syncthreads();
+      if (valid)
+        mx = __uint_as_float(__hip_atomic_load(&cm[col], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    }
+
+    // ---- quantise and store the transposed codes ------------------------------------------
+    if (valid) {
+      if (part == 0 && writer) a.scale[col] = stored_scale<QT>(a, mx);
+      const float mul = quant_mul<QT>(a, mx) * sgn;
+      const int64_t base = col * a.ldq + (int64_t)part * R - (int64_t)seg * R;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) store_chunk8<QT>(a.q, base + S::off(lane, j), &v[j * 8], mul);
+    }
+    __syncthreads();  // the next task overwrites the LDS tile
+  }
+}
+
+// Rows per task for a column of `rows` elements; 0 when the shape is not covered.
+static int cols2_rows_per_task(int64_t rows, int block) {
+  int R;
+  if (block > 1024) R = block;
+  else if (rows >= 1024) R = 1024;
+  else R = (int)rows;
+  if (R < 64 || R > 4096 || (R & (R - 1)) != 0) return 0;
+  if (rows % R != 0 || R % block != 0) return 0;
+  return R;
+}
+
+size_t fq_cols2_ws_bytes(int64_t rows, int64_t cols, int block, int in_bf16) {
+  if (!in_bf16) return 0;
+  const int R = cols2_rows_per_task(rows, block);
+  if (R == 0) return 0;
+  const int64_t P = rows / R;
+  if (P <= 1) return 0;
+  const int64_t C = 65536 / R;
+  const int64_t strips = (cols + C - 1) / C;
+  const size_t cnt = ((size_t)strips * 4 + 255) & ~(size_t)255;
+  return cnt + (size_t)cols * 4;
+}
+
+bool fq_cols2_supported(int64_t rows, int64_t cols, int block, int in_bf16, size_t ws_bytes) {
+  if (!in_bf16 || rows <= 0 || cols <= 0) return false;
+  const int R = cols2_rows_per_task(rows, block);
+  if (R == 0) return false;
+  return rows / R == 1 || ws_bytes >= fq_cols2_ws_bytes(rows, cols, block, in_bf16);
+}
+
+// Workgroups that can be resident at once (one per compute unit: the tile takes 128 KB of
+// LDS), queried once per device.
+static int cols2_capacity(const void* fn) {
+  static int cap[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cap[dev] > 0) return cap[dev];
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 1024, kColsLdsBytes) != hipSuccess)
+    return 0;
+  cap[dev] = cus * per_cu;
+  return cap[dev];
+}
+
+template <int B, int QT>
+static hipError_t launch_cols2_t(const FqArgs& a, void* ws, hipStream_t st) {
+  const int64_t rows = a.len, ncols = a.nvec;
+  if (ncols == 0 || rows == 0) return hipSuccess;
+  const int R = cols2_rows_per_task(rows, a.block);
+  const int P = (int)(rows / R), C = 65536 / R;
+  const int64_t strips = (ncols + C - 1) / C, tasks = strips * P;
+  const void* fn = reinterpret_cast<const void*>(&fq_cols2_kernel<B, QT>);
+  static std::once_flag once;
+  static hipError_t attr_err = hipSuccess;
+  std::call_once(once, [fn] {
+    attr_err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kColsLdsBytes);
+  });
+  if (attr_err != hipSuccess) return attr_err;
+  FqArgs args = a;
+  int Ra = R, Pa = P, Ca = C;
+  int64_t ta = tasks;
+  float* colmax = nullptr;
+  uint32_t* arrive = nullptr;
+  if (P == 1) {
+    hipLaunchKernelGGL((fq_cols2_kernel<B, QT>), dim3((unsigned)tasks), dim3(1024), kColsLdsBytes,
+                       st, args, Ra, Pa, Ca, ta, colmax, arrive);
+    return hipGetLastError();
+  }
+  // one task per workgroup; the P tasks of a strip are consecutive workgroups.  A waiting
+  // workgroup only waits for the other members of its own group, and the hardware dispatches
+  // workgroups in index order on each XCD: every group below the lowest undispatched
+  // workgroup is fully dispatched and finishes, freeing room for the rest, so every wait ends
+  // as long as one group fits on the device at once.
+  const int cap = cols2_capacity(fn);
+  if (cap < P) return hipErrorInvalidConfiguration;
+  // scratch: arrival counters (padded to 256 bytes), then the column maxima; both start at 0
+  arrive = reinterpret_cast<uint32_t*>(ws);
+  const size_t cnt = ((size_t)strips * 4 + 255) & ~(size_t)255;
+  colmax = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + cnt);
+  hipError_t e = launch_fill_zero(reinterpret_cast<float*>(ws), (int64_t)(cnt / 4) + ncols, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((fq_cols2_kernel<B, QT>), dim3((unsigned)tasks), dim3(1024), kColsLdsBytes,
+                     st, args, Ra, Pa, Ca, ta, colmax, arrive);
+  return hipGetLastError();
+}
+
+template <int QT>
+static hipError_t cols2_block(const FqArgs& a, void* ws, hipStream_t st) {
+#define HALO_C2_CASE(BB) \
+  case BB: return launch_cols2_t<BB, QT>(a, ws, st);
+  switch (a.block) {
+    HALO_C2_CASE(1) HALO_C2_CASE(2) HALO_C2_CASE(4) HALO_C2_CASE(8) HALO_C2_CASE(16)
+    HALO_C2_CASE(32) HALO_C2_CASE(64) HALO_C2_CASE(128) HALO_C2_CASE(256) HALO_C2_CASE(512)
+    HALO_C2_CASE(1024) HALO_C2_CASE(2048) HALO_C2_CASE(4096)
+    default: return hipErrorInvalidValue;
+  }
+#undef HALO_C2_CASE
+}
+
+hipError_t launch_fq_cols2(const FqArgs& a, int qt, void* ws, hipStream_t st) {
+  switch (qt) {
+    case 0: return cols2_block<0>(a, ws, st);
+    case 1: return cols2_block<1>(a, ws, st);
+    case 2: return cols2_block<2>(a, ws, st);
+    case 3: return cols2_block<3>(a, ws, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
+// rows dispatch
+// ---------------------------------------------------------------------------
+
+template <typename Tin, int QT>
+static hipError_t rows2_block(const FqArgs& a, hipStream_t st) {
+#define HALO_R2_CASE(BB) \
+  case BB: return launch_rows2_t<Tin, BB, QT>(a, st);
+  switch (a.block) {
+    HALO_R2_CASE(1) HALO_R2_CASE(2) HALO_R2_CASE(4) HALO_R2_CASE(8) HALO_R2_CASE(16)
+    HALO_R2_CASE(32) HALO_R2_CASE(64) HALO_R2_CASE(128) HALO_R2_CASE(256) HALO_R2_CASE(512)
+    HALO_R2_CASE(1024) HALO_R2_CASE(2048) HALO_R2_CASE(4096)
+    default: return hipErrorInvalidValue;
+  }
+#undef HALO_R2_CASE
+}
+
+hipError_t launch_fq_rows2(const FqArgs& a, int in_bf16, int qt, hipStream_t st) {
+  if (in_bf16) {
+    switch (qt) {
+      case 0: return rows2_block<uint16_t, 0>(a, st);
+      case 1: return rows2_block<uint16_t, 1>(a, st);
+      case 2: return rows2_block<uint16_t, 2>(a, st);
+      case 3: return rows2_block<uint16_t, 3>(a, st);
+    }
+  } else {
+    switch (qt) {
+      case 0: return rows2_block<float, 0>(a, st);
+      case 1: return rows2_block<float, 1>(a, st);
+      case 2: return rows2_block<float, 2>(a, st);
+      case 3: return rows2_block<float, 3>(a, st);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace halo

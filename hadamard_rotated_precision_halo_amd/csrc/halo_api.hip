@@ -75,7 +75,7 @@ halo_status check_fq(const void* x, halo_dtype xt, int64_t rows, int64_t cols, i
 
 halo_status run_fq(const void* x, halo_dtype xt, int64_t rows, int64_t cols, int64_t ldx,
                    halo_axis axis, int32_t block, halo_dtype qt, void* q, int64_t ldq,
-                   float* scale, hipStream_t st) {
+                   float* scale, void* ws, size_t ws_bytes, hipStream_t st) {
   FqArgs a{};
   a.x = x;
   a.ldx = ldx;
@@ -88,7 +88,14 @@ halo_status run_fq(const void* x, halo_dtype xt, int64_t rows, int64_t cols, int
   a.qmax = qmax_of(qt);
   a.denom = (float)((double)a.qmax * std::sqrt((double)block));
   a.inv_sqrt_b = (float)(1.0 / std::sqrt((double)block));
-  return from_hip(launch_fwht_quant(a, xt == HALO_BF16 ? 1 : 0, qt_index(qt), (int)axis, st));
+  return from_hip(launch_fwht_quant(a, xt == HALO_BF16 ? 1 : 0, qt_index(qt), (int)axis, ws,
+                                    ws ? ws_bytes : 0, st));
+}
+
+// Scratch of one rotation pass (the single-read columns kernel's partial maxima and counters).
+size_t fq_ws_bytes(int64_t rows, int64_t cols, halo_axis axis, int32_t block, halo_dtype xt) {
+  if (axis != HALO_ALONG_COLS) return 0;
+  return fq_cols2_ws_bytes(rows, cols, block, xt == HALO_BF16 ? 1 : 0);
 }
 
 halo_status check_gemm(const void* a, int64_t lda, const void* b, int64_t ldb, int64_t m,
@@ -108,15 +115,17 @@ halo_status check_gemm(const void* a, int64_t lda, const void* b, int64_t ldb, i
 
 size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
 
-// Region sizes of the layer workspace, in carve order.
+// Region sizes of the layer workspace, in carve order; the last region is the scratch the
+// columns passes share (they run one after another on the caller's stream).
 struct WsPlan {
-  size_t off[8];
+  size_t off[9];
   size_t total;
+  size_t scratch_off, scratch_bytes;
 };
 
-WsPlan plan_ws(int64_t m, int64_t n, int64_t k, int backward) {
+WsPlan plan_ws(int64_t m, int64_t n, int64_t k, int backward, int32_t block, halo_dtype io) {
   WsPlan p{};
-  size_t sizes[8];
+  size_t sizes[9];
   int cnt = 0;
   if (!backward) {
     sizes[cnt++] = (size_t)m * k;      // X codes   [m x k]
@@ -138,7 +147,17 @@ WsPlan plan_ws(int64_t m, int64_t n, int64_t k, int backward) {
     p.off[i] = o;
     o += round256(sizes[i]);
   }
-  p.total = o;
+  size_t scratch = 0;
+  if (backward) {
+    scratch = fq_ws_bytes(n, k, HALO_ALONG_COLS, block, io);        // W columns along n
+    const size_t s2 = fq_ws_bytes(m, n, HALO_ALONG_COLS, block, io);  // dY columns along m
+    const size_t s3 = fq_ws_bytes(m, k, HALO_ALONG_COLS, block, io);  // X columns along m
+    if (s2 > scratch) scratch = s2;
+    if (s3 > scratch) scratch = s3;
+  }
+  p.scratch_off = o;
+  p.scratch_bytes = round256(scratch);
+  p.total = o + p.scratch_bytes;
   return p;
 }
 
@@ -171,12 +190,21 @@ const char* halo_status_str(halo_status s) {
   return "unknown status";
 }
 
+size_t halo_fwht_quant_workspace_bytes(int64_t rows, int64_t cols, halo_axis axis,
+                                       int32_t block, halo_dtype x_type) {
+  if (rows < 0 || cols < 0 || rows >= kMaxDim || cols >= kMaxDim || !valid_block(block))
+    return 0;
+  return fq_ws_bytes(rows, cols, axis, block, x_type);
+}
+
 halo_status halo_fwht_quant(const void* x, halo_dtype x_type, int64_t rows, int64_t cols,
                             int64_t ldx, halo_axis axis, int32_t block, halo_dtype q_type,
-                            void* q, int64_t ldq, float* scale, void* stream) {
+                            void* q, int64_t ldq, float* scale, void* ws, size_t ws_bytes,
+                            void* stream) {
   halo_status s = check_fq(x, x_type, rows, cols, ldx, axis, block, q_type, q, ldq, scale);
   if (s != HALO_OK) return s;
-  return run_fq(x, x_type, rows, cols, ldx, axis, block, q_type, q, ldq, scale,
+  if (ws && !aligned16(ws)) return HALO_ERR_ALIGN;
+  return run_fq(x, x_type, rows, cols, ldx, axis, block, q_type, q, ldq, scale, ws, ws_bytes,
                 (hipStream_t)stream);
 }
 
@@ -209,7 +237,14 @@ size_t halo_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, halo_dtype q
                                    int backward) {
   if (m < 0 || n < 0 || k < 0 || m >= kMaxDim || n >= kMaxDim || k >= kMaxDim) return 0;
   if (q_type != HALO_I8 && q_type != HALO_E4M3) return 0;
-  return plan_ws(m, n, k, backward ? 1 : 0).total;
+  // the block and the input type decide the columns passes' scratch: size it for the most
+  // demanding case (bf16 input, the block that needs the most partial maxima)
+  size_t most = 0;
+  for (int32_t b = 1; b <= 4096; b *= 2) {
+    const size_t t = plan_ws(m, n, k, backward ? 1 : 0, b, HALO_BF16).total;
+    if (t > most) most = t;
+  }
+  return most;
 }
 
 halo_status halo_linear_fwd(const void* x, const void* w, halo_dtype io_type, int64_t m,
@@ -226,7 +261,7 @@ halo_status halo_linear_fwd(const void* x, const void* w, halo_dtype io_type, in
   if (k > fq_rows_max_len(block)) return HALO_ERR_SHAPE;
   if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return HALO_ERR_ALIGN;
   if ((n * esize(y_type)) % 16 != 0) return HALO_ERR_ALIGN;
-  const WsPlan p = plan_ws(m, n, k, 0);
+  const WsPlan p = plan_ws(m, n, k, 0, block, io_type);
   if (!ws || ws_bytes < p.total) return HALO_ERR_WORKSPACE;
   if (!aligned16(ws)) return HALO_ERR_ALIGN;
   char* base = static_cast<char*>(ws);
@@ -235,8 +270,10 @@ halo_status halo_linear_fwd(const void* x, const void* w, halo_dtype io_type, in
   void* qw = base + p.off[2];
   float* sw = reinterpret_cast<float*>(base + p.off[3]);
   hipStream_t st = (hipStream_t)stream;
-  halo_status s = run_fq(x, io_type, m, k, k, HALO_ALONG_ROWS, block, q_type, qx, k, sx, st);
-  if (s == HALO_OK) s = run_fq(w, io_type, n, k, k, HALO_ALONG_ROWS, block, q_type, qw, k, sw, st);
+  halo_status s =
+      run_fq(x, io_type, m, k, k, HALO_ALONG_ROWS, block, q_type, qx, k, sx, nullptr, 0, st);
+  if (s == HALO_OK)
+    s = run_fq(w, io_type, n, k, k, HALO_ALONG_ROWS, block, q_type, qw, k, sw, nullptr, 0, st);
   if (s == HALO_OK) s = gemm_any(qx, q_type, k, sx, qw, q_type, k, sw, m, n, k, y, y_type, n, st);
   return s;
 }
@@ -261,10 +298,12 @@ halo_status halo_linear_bwd(const void* dy, const void* x, const void* w, halo_d
   if (dx && n > fq_rows_max_len(block)) return HALO_ERR_SHAPE;
   if (!aligned16(dy) || !aligned16(x) || !aligned16(w)) return HALO_ERR_ALIGN;
   if ((dx && !aligned16(dx)) || (dw && !aligned16(dw))) return HALO_ERR_ALIGN;
-  const WsPlan p = plan_ws(m, n, k, 1);
+  const WsPlan p = plan_ws(m, n, k, 1, block, io_type);
   if (!ws || ws_bytes < p.total) return HALO_ERR_WORKSPACE;
   if (!aligned16(ws)) return HALO_ERR_ALIGN;
   char* base = static_cast<char*>(ws);
+  void* scr = base + p.scratch_off;
+  const size_t scr_bytes = p.scratch_bytes;
   hipStream_t st = (hipStream_t)stream;
   halo_status s = HALO_OK;
   if (dx) {  // dX[m x k] = dY W: contraction over n
@@ -272,9 +311,11 @@ halo_status halo_linear_bwd(const void* dy, const void* x, const void* w, halo_d
     float* sdy = reinterpret_cast<float*>(base + p.off[1]);
     void* qwt = base + p.off[2];
     float* swt = reinterpret_cast<float*>(base + p.off[3]);
-    s = run_fq(dy, io_type, m, n, n, HALO_ALONG_ROWS, block, grad_q_type, qdy, n, sdy, st);
+    s = run_fq(dy, io_type, m, n, n, HALO_ALONG_ROWS, block, grad_q_type, qdy, n, sdy, nullptr,
+               0, st);
     if (s == HALO_OK)
-      s = run_fq(w, io_type, n, k, k, HALO_ALONG_COLS, block, q_type, qwt, n, swt, st);
+      s = run_fq(w, io_type, n, k, k, HALO_ALONG_COLS, block, q_type, qwt, n, swt, scr, scr_bytes,
+                 st);
     if (s == HALO_OK)
       s = gemm_any(qdy, grad_q_type, n, sdy, qwt, q_type, n, swt, m, k, n, dx, io_type, k, st);
   }
@@ -283,9 +324,11 @@ halo_status halo_linear_bwd(const void* dy, const void* x, const void* w, halo_d
     float* sdyt = reinterpret_cast<float*>(base + p.off[5]);
     void* qxt = base + p.off[6];
     float* sxt = reinterpret_cast<float*>(base + p.off[7]);
-    s = run_fq(dy, io_type, m, n, n, HALO_ALONG_COLS, block, grad_q_type, qdyt, m, sdyt, st);
+    s = run_fq(dy, io_type, m, n, n, HALO_ALONG_COLS, block, grad_q_type, qdyt, m, sdyt, scr,
+               scr_bytes, st);
     if (s == HALO_OK)
-      s = run_fq(x, io_type, m, k, k, HALO_ALONG_COLS, block, q_type, qxt, m, sxt, st);
+      s = run_fq(x, io_type, m, k, k, HALO_ALONG_COLS, block, q_type, qxt, m, sxt, scr, scr_bytes,
+                 st);
     if (s == HALO_OK)
       s = gemm_any(qdyt, grad_q_type, m, sdyt, qxt, q_type, m, sxt, n, k, m, dw, io_type, k, st);
   }

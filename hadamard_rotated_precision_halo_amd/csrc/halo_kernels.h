@@ -23,8 +23,19 @@ struct FqArgs {
 };
 
 // in_bf16: 1 for bf16 input, 0 for fp32.  qt: 0 INT8, 1 E4M3, 2 E5M2, 3 fp32 values.
-// axis: 0 rows, 1 cols.
-hipError_t launch_fwht_quant(const FqArgs& a, int in_bf16, int qt, int axis, hipStream_t st);
+// axis: 0 rows, 1 cols.  ws / ws_bytes: scratch for the single-read columns kernel (may be
+// NULL / 0: the columns pass then reads its input twice).
+hipError_t launch_fwht_quant(const FqArgs& a, int in_bf16, int qt, int axis, void* ws,
+                             size_t ws_bytes, hipStream_t st);
+
+// Scratch bytes the single-read columns kernel needs for columns of `rows` elements (0 when
+// it needs none or does not cover the shape).
+size_t fq_cols2_ws_bytes(int64_t rows, int64_t cols, int block, int in_bf16);
+bool fq_cols2_supported(int64_t rows, int64_t cols, int block, int in_bf16, size_t ws_bytes);
+hipError_t launch_fq_cols2(const FqArgs& a, int qt, void* ws, hipStream_t st);
+
+// Zero n floats (also used for 32-bit counters).
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 
 // Wave-per-slice rows kernel: rows of L = 64 j elements with 4096 % L == 0 or 4096 <= L <= 65536.
 bool fq_rows2_supported(int64_t len, int block);

@@ -87,13 +87,27 @@ typedef enum {
  *            HALO_F32: test mode, q receives the rotated values themselves (fp32) and scale
  *            the absmax of each rotated vector.
  *   ldq      leading dimension of q in elements.
+ *   ws       optional device scratch of ws_bytes >= halo_fwht_quant_workspace_bytes(...)
+ *            bytes (16-byte aligned), caller-owned; its contents on entry do not matter and
+ *            are clobbered.  With it, a columns-axis pass over long bf16 columns reads its
+ *            input once; with ws NULL (or too small) the pass reads its input twice and gives
+ *            the same codes and scales.  Calls that share one scratch must be ordered on one
+ *            stream.
  * Rows-axis vectors are limited to L <= 16384 elements (one workgroup holds a whole row).
  * Codes are decided in fp32: m = qmax / max|b| with b the un-normalised butterfly output and
  * code = round(b * m); the 1/sqrt(block) factor cancels between b and max|b|.
  */
 halo_status halo_fwht_quant(const void* x, halo_dtype x_type, int64_t rows, int64_t cols,
                             int64_t ldx, halo_axis axis, int32_t block, halo_dtype q_type,
-                            void* q, int64_t ldq, float* scale, void* stream);
+                            void* q, int64_t ldq, float* scale, void* ws, size_t ws_bytes,
+                            void* stream);
+
+/*
+ * Scratch bytes halo_fwht_quant can use for this shape (0 when it needs none: rows axis,
+ * fp32 input, or columns short enough for one workgroup).  Invalid arguments give 0.
+ */
+size_t halo_fwht_quant_workspace_bytes(int64_t rows, int64_t cols, halo_axis axis,
+                                       int32_t block, halo_dtype x_type);
 
 /*
  * INT8 product with wide accumulation and a fused scale dequant ("HALO: Hadamard-Assisted

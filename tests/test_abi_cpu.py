@@ -61,8 +61,8 @@ def test_status_strings(L):
 
 
 def fq(L, x=P, xt=BF16, rows=64, cols=256, ldx=256, axis=0, block=256, qt=I8, q=P2, ldq=256,
-       scale=P3):
-    return L.halo_fwht_quant(x, xt, rows, cols, ldx, axis, block, qt, q, ldq, scale, None)
+       scale=P3, ws=None, wsb=0):
+    return L.halo_fwht_quant(x, xt, rows, cols, ldx, axis, block, qt, q, ldq, scale, ws, wsb, None)
 
 
 def test_fwht_quant_validation(L):
@@ -89,6 +89,22 @@ def test_fwht_quant_validation(L):
     assert fq(L, q=BAD) == ALIGN
     assert fq(L, ldx=260, cols=256) == ALIGN  # 520 bytes per bf16 row
     assert fq(L, ldq=260) == ALIGN
+    assert fq(L, ws=BAD, wsb=4096) == ALIGN
+
+
+def test_fwht_quant_workspace_bytes(L):
+    # single-read columns pass: per-strip arrival counters (64 strips of 64 columns, padded to
+    # 256 bytes) + one maximum per column
+    W = L.halo_fwht_quant_workspace_bytes
+    assert W(4096, 4096, 1, 256, BF16) == 256 + 4096 * 4
+    assert W(8192, 4096, 1, 128, BF16) == 256 + 4096 * 4
+    assert W(16384, 14336, 1, 512, BF16) == 1024 + 14336 * 4
+    assert W(8192, 4096, 1, 4096, BF16) == 1024 + 4096 * 4      # 16-column strips of 4096 rows
+    assert W(1024, 4096, 1, 256, BF16) == 0      # one part per column: no exchange
+    assert W(4096, 4096, 0, 256, BF16) == 0      # rows axis
+    assert W(4096, 4096, 1, 256, F32) == 0       # fp32 input takes the two-read path
+    assert W(4096, 4096, 1, 3, BF16) == 0
+    assert W(-1, 4096, 1, 256, BF16) == 0
 
 
 def gi8(L, a=P, lda=128, sa=P2, b=P3, ldb=128, sb=P2, m=64, n=64, k=128, c=P, ct=BF16, ldc=64):
@@ -132,6 +148,11 @@ def test_workspace_bytes(L):
     assert L.halo_linear_workspace_bytes(m, n, k, I8, 0) == r(m * k) + r(4 * m) + r(n * k) + r(4 * n)
     want = (r(m * n) + r(4 * m) + r(k * n) + r(4 * k) + r(n * m) + r(4 * n) + r(k * m) + r(4 * k))
     assert L.halo_linear_workspace_bytes(m, n, k, E4M3, 1) == want
+    # 4096^3 backward: the code matrices plus the columns passes' shared scratch
+    big = 4096
+    codes = 4 * (r(big * big) + r(4 * big))
+    # (sized for every block; block 2048 needs the most: 128 strips of 32 columns, 2 parts)
+    assert L.halo_linear_workspace_bytes(big, big, big, I8, 1) == codes + r(512 + 4096 * 4)
     assert L.halo_linear_workspace_bytes(-1, n, k, I8, 0) == 0
     assert L.halo_linear_workspace_bytes(m, n, k, BF16, 0) == 0
 

@@ -88,6 +88,12 @@ COL_CASES = [
     ("bf16", 1024, 2048, 16, O.I8),
     ("bf16", 2048, 4096, 8, O.E4M3),
     ("bf16", 4096, 8192, 8, O.I8),
+    ("bf16", 256, 4096, 520, O.I8),       # 4 tasks per strip, partial last strip
+    ("bf16", 128, 8192, 72, O.E4M3),      # 8 tasks per strip
+    ("bf16", 512, 512, 136, O.E5M2),      # 512-row tiles of 128 columns
+    ("bf16", 64, 256, 1032, O.I8),        # 256-row tiles, 5 strips
+    ("bf16", 1024, 3072, 64, O.I8),       # 3 tasks per strip
+    ("bf16", 256, 4096, 5120, O.I8),      # 320 tasks: more than one round of the persistent grid
 ]
 
 
@@ -102,6 +108,24 @@ def test_cols_match_oracle(io, block, rows, cols, qtype):
     r64, s64 = O.fwht_quant(x, O.COLS, block, qtype, precision=64)
     assert_codes_close_to_fp64(q, r64, qtype, block)
     np.testing.assert_allclose(s, s64, rtol=1e-5)
+
+
+def test_cols_single_read_matches_two_read_path():
+    # the same pass with and without scratch (one input read vs two), repeated on one scratch
+    # buffer and on a second stream: identical codes and scales every time
+    x = to_dev(_input(8192, 200, "bf16", seed=77, kind="grad"))
+    ref_q, ref_s = H.fwht_quant(x, axis=H.COLS, block=256, workspace=False)
+    ws = torch.empty(H.fwht_quant_workspace_bytes(8192, 200, H.COLS, 256), dtype=torch.uint8,
+                     device="cuda")
+    assert ws.numel() > 0
+    for _ in range(3):
+        q, s = H.fwht_quant(x, axis=H.COLS, block=256, workspace=ws)
+        assert torch.equal(q, ref_q) and torch.equal(s, ref_s)
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        q, s = H.fwht_quant(x, axis=H.COLS, block=256, workspace=ws)
+    st.synchronize()
+    assert torch.equal(q, ref_q) and torch.equal(s, ref_s)
 
 
 @pytest.mark.parametrize("axis,block,rows,cols", [(H.ROWS, 256, 24, 1024), (H.ROWS, 128, 6, 11008),
