@@ -252,24 +252,34 @@ __device__ __forceinline__ float stored_scale(const FqArgs& a, float mx) {
 // QT: 0 INT8, 1 E4M3, 2 E5M2, 3 fp32 rotated values.
 // multi = 1: one row per workgroup, wave w owns columns [4096 w, 4096 (w + 1)).
 // multi = 0: 4096 % L == 0, each wave owns 4096 / L whole rows.
+// One launch serves up to two passes of the same geometry (workgroups below pp.split run the
+// first), and can clear a scratch range for the column passes that follow it on the stream.
 template <typename Tin, int B, int QT>
-__global__ __launch_bounds__(1024) void fq_rows2_kernel(FqArgs a, int multi) {
+__global__ __launch_bounds__(1024) void fq_rows2_kernel(FqPair pp, int multi) {
   using S = Slice<B>;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  if (pp.zero) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < pp.nzero; i += stride)
+      pp.zero[i] = 0u;
+  }
+  const bool second = (int64_t)blockIdx.x >= pp.split;
+  const FqArgs a = second ? pp.p1 : pp.p0;
+  const int bid = (int)(blockIdx.x - (second ? pp.split : 0));
 
   int64_t row;
   int col0;  // column of the slice start within the row
   int row_lanes_log2;
   bool valid;
   if (multi) {
-    row = blockIdx.x;
+    row = bid;
     col0 = w * 4096;
     row_lanes_log2 = 6;
     valid = col0 + S::off(lane, 0) < a.len;  // lanes past the row end idle (a whole lane or none)
   } else {
     const int L = (int)a.len;
     const int rpw = 4096 / L;              // rows per wave
-    const int first = (blockIdx.x * nw + w) * rpw;
+    const int first = (bid * nw + w) * rpw;
     const int r_in_wave = S::off(lane, 0) / L;
     row = (int64_t)first + r_in_wave;
     col0 = -r_in_wave * L;                 // so that col0 + off(lane, j) is the column
@@ -307,21 +317,29 @@ __global__ __launch_bounds__(1024) void fq_rows2_kernel(FqArgs a, int multi) {
   for (int j = 0; j < 8; ++j) store_chunk8<QT>(a.q, base + S::off(lane, j), &v[j * 8], mul);
 }
 
+// Workgroups of one rows pass (0 for an empty one).
+static int64_t rows2_grid(const FqArgs& a) {
+  if (a.nvec == 0) return 0;
+  if (a.len >= 4096) return a.nvec;
+  const int64_t rpw = 4096 / a.len;
+  const int64_t waves = (a.nvec + rpw - 1) / rpw;
+  return (waves + 3) / 4;
+}
+
 template <typename Tin, int B, int QT>
-static hipError_t launch_rows2_t(const FqArgs& a, hipStream_t st) {
-  const int64_t L = a.len;
-  if (a.nvec == 0) return hipSuccess;
-  if (L >= 4096) {
-    const int nw = (int)((L + 4095) / 4096);
-    hipLaunchKernelGGL((fq_rows2_kernel<Tin, B, QT>), dim3((unsigned)a.nvec), dim3(64 * nw), 0, st,
-                       a, 1);
-  } else {
-    const int64_t rpw = 4096 / L;
-    const int64_t waves = (a.nvec + rpw - 1) / rpw;
-    const int nw = 4;
-    hipLaunchKernelGGL((fq_rows2_kernel<Tin, B, QT>), dim3((unsigned)((waves + nw - 1) / nw)),
-                       dim3(64 * nw), 0, st, a, 0);
+static hipError_t launch_rows2_t(FqPair pp, hipStream_t st) {
+  const int64_t L = pp.p0.len;
+  const int64_t g0 = rows2_grid(pp.p0), g1 = pp.has1 ? rows2_grid(pp.p1) : 0;
+  pp.split = g0;
+  const int64_t grid = g0 + g1;
+  if (grid == 0) {
+    if (pp.zero && pp.nzero > 0) return launch_fill_zero(reinterpret_cast<float*>(pp.zero), pp.nzero, st);
+    return hipSuccess;
   }
+  const int multi = L >= 4096 ? 1 : 0;
+  const int nw = multi ? (int)((L + 4095) / 4096) : 4;
+  hipLaunchKernelGGL((fq_rows2_kernel<Tin, B, QT>), dim3((unsigned)grid), dim3(64 * nw), 0, st, pp,
+                     multi);
   return hipGetLastError();
 }
 
@@ -346,35 +364,47 @@ __device__ __forceinline__ int lds_slot(int w, int lane, int j) {
   return w * 512 + j * 64 + (lane ^ (((j * JA) ^ w) & 15));
 }
 
-// Columns-axis plan: R rows per task (the slice length of a wave's column segment), P tasks
-// per column strip of C = 65536 / R columns.
-struct ColsGeo {
-  int R, P, C;
-  int64_t strips;
-};
-
 __device__ __forceinline__ uint32_t bf16_pair(uint32_t lo_word, uint32_t hi_word, int half) {
   // column `half` (0: low 16 bits, 1: high 16 bits) of two rows -> one dword, lower row first
   return __builtin_amdgcn_perm(hi_word, lo_word, half ? 0x07060302u : 0x05040100u);
 }
 
+// One column pass of a launch: its arguments and its scratch (column maxima and per-strip
+// arrival counters, both zero at launch; unused when P == 1).
+struct Cols2Prob {
+  FqArgs a;
+  float* colmax;
+  uint32_t* arrive;
+};
+// Up to two passes over columns of the same length (tasks below `split` run the first).
+struct Cols2Pair {
+  Cols2Prob p0, p1;
+  int64_t split, tasks;
+  int R, P, C;
+};
+
 template <int B, int QT>
-__global__ __launch_bounds__(1024) void fq_cols2_kernel(FqArgs a, int R, int P, int C,
-                                                        int64_t tasks, float* colmax,
-                                                        uint32_t* arrive) {
+__global__ __launch_bounds__(1024) void fq_cols2_kernel(Cols2Pair cp) {
   extern __shared__ __attribute__((aligned(16))) uint4 lds[];
   using S = Slice<B>;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int64_t ncols = a.nvec;
+  const int R = cp.R, P = cp.P, C = cp.C;
   const int CC = C / 8;                      // 16-byte column chunks per row of the tile
   const int cpw = 4096 / R;                  // column segments per wave
   const int cc = t % CC, rg = t / CC;        // loader: column chunk, group of 8 rows
   const int row_lanes_log2 = 31 - __builtin_clz((unsigned)(R / 64));
-  const uint16_t* __restrict__ xin = reinterpret_cast<const uint16_t*>(a.x);
 
-  for (int64_t task = blockIdx.x; task < tasks; task += gridDim.x) {
-    const int64_t strip = task / P;
-    const int part = (int)(task % P);
+  for (int64_t task = blockIdx.x; task < cp.tasks; task += gridDim.x) {
+    const bool second = task >= cp.split;
+    const Cols2Prob pr = second ? cp.p1 : cp.p0;
+    const FqArgs& a = pr.a;
+    float* colmax = pr.colmax;
+    uint32_t* arrive = pr.arrive;
+    const int64_t ncols = a.nvec;
+    const uint16_t* __restrict__ xin = reinterpret_cast<const uint16_t*>(a.x);
+    const int64_t ltask = task - (second ? cp.split : 0);
+    const int64_t strip = ltask / P;
+    const int part = (int)(ltask % P);
     const int64_t c0 = strip * C;
 
     // ---- load 8 rows x 8 columns, transpose, write to LDS ------------------------------
@@ -510,13 +540,21 @@ static int cols2_capacity(const void* fn) {
   return cap[dev];
 }
 
+// Scratch layout of one pass: arrival counters (padded to 256 bytes), then the column maxima.
+static void cols2_scratch(void* ws, int64_t strips, float** colmax, uint32_t** arrive,
+                          int64_t* words) {
+  const size_t cnt = ((size_t)strips * 4 + 255) & ~(size_t)255;
+  *arrive = reinterpret_cast<uint32_t*>(ws);
+  *colmax = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + cnt);
+  *words = (int64_t)(cnt / 4);
+}
+
 template <int B, int QT>
-static hipError_t launch_cols2_t(const FqArgs& a, void* ws, hipStream_t st) {
-  const int64_t rows = a.len, ncols = a.nvec;
-  if (ncols == 0 || rows == 0) return hipSuccess;
-  const int R = cols2_rows_per_task(rows, a.block);
+static hipError_t launch_cols2_t(const FqArgs& a0, void* ws0, const FqArgs* a1, void* ws1,
+                                 int prezeroed, hipStream_t st) {
+  const int64_t rows = a0.len;
+  const int R = cols2_rows_per_task(rows, a0.block);
   const int P = (int)(rows / R), C = 65536 / R;
-  const int64_t strips = (ncols + C - 1) / C, tasks = strips * P;
   const void* fn = reinterpret_cast<const void*>(&fq_cols2_kernel<B, QT>);
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
@@ -524,39 +562,54 @@ static hipError_t launch_cols2_t(const FqArgs& a, void* ws, hipStream_t st) {
     attr_err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kColsLdsBytes);
   });
   if (attr_err != hipSuccess) return attr_err;
-  FqArgs args = a;
-  int Ra = R, Pa = P, Ca = C;
-  int64_t ta = tasks;
-  float* colmax = nullptr;
-  uint32_t* arrive = nullptr;
-  if (P == 1) {
-    hipLaunchKernelGGL((fq_cols2_kernel<B, QT>), dim3((unsigned)tasks), dim3(1024), kColsLdsBytes,
-                       st, args, Ra, Pa, Ca, ta, colmax, arrive);
-    return hipGetLastError();
+  Cols2Pair cp{};
+  cp.R = R;
+  cp.P = P;
+  cp.C = C;
+  const FqArgs* probs[2] = {&a0, a1};
+  void* wss[2] = {ws0, ws1};
+  Cols2Prob* dst[2] = {&cp.p0, &cp.p1};
+  int64_t tasks[2] = {0, 0};
+  for (int i = 0; i < 2; ++i) {
+    if (!probs[i] || probs[i]->nvec == 0 || rows == 0) continue;
+    const int64_t strips = (probs[i]->nvec + C - 1) / C;
+    tasks[i] = strips * P;
+    dst[i]->a = *probs[i];
+    if (P > 1) {
+      int64_t words = 0;
+      cols2_scratch(wss[i], strips, &dst[i]->colmax, &dst[i]->arrive, &words);
+      if (!prezeroed) {
+        const hipError_t e = launch_fill_zero(reinterpret_cast<float*>(wss[i]),
+                                              words + probs[i]->nvec, st);
+        if (e != hipSuccess) return e;
+      }
+    }
   }
+  if (tasks[0] == 0) {  // keep the first slot filled: the kernel picks by task index
+    cp.p0 = cp.p1;
+    tasks[0] = tasks[1];
+    tasks[1] = 0;
+  }
+  cp.split = tasks[0];
+  cp.tasks = tasks[0] + tasks[1];
+  if (cp.tasks == 0) return hipSuccess;
   // one task per workgroup; the P tasks of a strip are consecutive workgroups.  A waiting
   // workgroup only waits for the other members of its own group, and the hardware dispatches
   // workgroups in index order on each XCD: every group below the lowest undispatched
   // workgroup is fully dispatched and finishes, freeing room for the rest, so every wait ends
   // as long as one group fits on the device at once.
-  const int cap = cols2_capacity(fn);
-  if (cap < P) return hipErrorInvalidConfiguration;
-  // scratch: arrival counters (padded to 256 bytes), then the column maxima; both start at 0
-  arrive = reinterpret_cast<uint32_t*>(ws);
-  const size_t cnt = ((size_t)strips * 4 + 255) & ~(size_t)255;
-  colmax = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + cnt);
-  hipError_t e = launch_fill_zero(reinterpret_cast<float*>(ws), (int64_t)(cnt / 4) + ncols, st);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((fq_cols2_kernel<B, QT>), dim3((unsigned)tasks), dim3(1024), kColsLdsBytes,
-                     st, args, Ra, Pa, Ca, ta, colmax, arrive);
+  if (P > 1 && cols2_capacity(fn) < P) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((fq_cols2_kernel<B, QT>), dim3((unsigned)cp.tasks), dim3(1024), kColsLdsBytes,
+                     st, cp);
   return hipGetLastError();
 }
 
 template <int QT>
-static hipError_t cols2_block(const FqArgs& a, void* ws, hipStream_t st) {
+static hipError_t cols2_block(const FqArgs& a0, void* ws0, const FqArgs* a1, void* ws1,
+                              int prezeroed, hipStream_t st) {
 #define HALO_C2_CASE(BB) \
-  case BB: return launch_cols2_t<BB, QT>(a, ws, st);
-  switch (a.block) {
+  case BB: return launch_cols2_t<BB, QT>(a0, ws0, a1, ws1, prezeroed, st);
+  switch (a0.block) {
     HALO_C2_CASE(1) HALO_C2_CASE(2) HALO_C2_CASE(4) HALO_C2_CASE(8) HALO_C2_CASE(16)
     HALO_C2_CASE(32) HALO_C2_CASE(64) HALO_C2_CASE(128) HALO_C2_CASE(256) HALO_C2_CASE(512)
     HALO_C2_CASE(1024) HALO_C2_CASE(2048) HALO_C2_CASE(4096)
@@ -565,14 +618,19 @@ static hipError_t cols2_block(const FqArgs& a, void* ws, hipStream_t st) {
 #undef HALO_C2_CASE
 }
 
-hipError_t launch_fq_cols2(const FqArgs& a, int qt, void* ws, hipStream_t st) {
+hipError_t launch_fq_cols2_pair(const FqArgs& a0, void* ws0, const FqArgs* a1, void* ws1, int qt,
+                                int prezeroed, hipStream_t st) {
   switch (qt) {
-    case 0: return cols2_block<0>(a, ws, st);
-    case 1: return cols2_block<1>(a, ws, st);
-    case 2: return cols2_block<2>(a, ws, st);
-    case 3: return cols2_block<3>(a, ws, st);
+    case 0: return cols2_block<0>(a0, ws0, a1, ws1, prezeroed, st);
+    case 1: return cols2_block<1>(a0, ws0, a1, ws1, prezeroed, st);
+    case 2: return cols2_block<2>(a0, ws0, a1, ws1, prezeroed, st);
+    case 3: return cols2_block<3>(a0, ws0, a1, ws1, prezeroed, st);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_fq_cols2(const FqArgs& a, int qt, void* ws, hipStream_t st) {
+  return launch_fq_cols2_pair(a, ws, nullptr, nullptr, qt, 0, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -580,10 +638,10 @@ hipError_t launch_fq_cols2(const FqArgs& a, int qt, void* ws, hipStream_t st) {
 // ---------------------------------------------------------------------------
 
 template <typename Tin, int QT>
-static hipError_t rows2_block(const FqArgs& a, hipStream_t st) {
+static hipError_t rows2_block(const FqPair& a, hipStream_t st) {
 #define HALO_R2_CASE(BB) \
   case BB: return launch_rows2_t<Tin, BB, QT>(a, st);
-  switch (a.block) {
+  switch (a.p0.block) {
     HALO_R2_CASE(1) HALO_R2_CASE(2) HALO_R2_CASE(4) HALO_R2_CASE(8) HALO_R2_CASE(16)
     HALO_R2_CASE(32) HALO_R2_CASE(64) HALO_R2_CASE(128) HALO_R2_CASE(256) HALO_R2_CASE(512)
     HALO_R2_CASE(1024) HALO_R2_CASE(2048) HALO_R2_CASE(4096)
@@ -593,6 +651,12 @@ static hipError_t rows2_block(const FqArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_fq_rows2(const FqArgs& a, int in_bf16, int qt, hipStream_t st) {
+  FqPair pp{};
+  pp.p0 = a;
+  return launch_fq_rows2_pair(pp, in_bf16, qt, st);
+}
+
+hipError_t launch_fq_rows2_pair(const FqPair& a, int in_bf16, int qt, hipStream_t st) {
   if (in_bf16) {
     switch (qt) {
       case 0: return rows2_block<uint16_t, 0>(a, st);

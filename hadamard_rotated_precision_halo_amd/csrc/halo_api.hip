@@ -73,6 +73,23 @@ halo_status check_fq(const void* x, halo_dtype xt, int64_t rows, int64_t cols, i
   return HALO_OK;
 }
 
+FqArgs make_fq(const void* x, int64_t rows, int64_t cols, int64_t ldx, halo_axis axis,
+               int32_t block, halo_dtype qt, void* q, int64_t ldq, float* scale) {
+  FqArgs a{};
+  a.x = x;
+  a.ldx = ldx;
+  a.nvec = axis == HALO_ALONG_ROWS ? rows : cols;
+  a.len = axis == HALO_ALONG_ROWS ? cols : rows;
+  a.q = q;
+  a.ldq = ldq;
+  a.scale = scale;
+  a.block = block;
+  a.qmax = qmax_of(qt);
+  a.denom = (float)((double)a.qmax * std::sqrt((double)block));
+  a.inv_sqrt_b = (float)(1.0 / std::sqrt((double)block));
+  return a;
+}
+
 halo_status run_fq(const void* x, halo_dtype xt, int64_t rows, int64_t cols, int64_t ldx,
                    halo_axis axis, int32_t block, halo_dtype qt, void* q, int64_t ldq,
                    float* scale, void* ws, size_t ws_bytes, hipStream_t st) {
@@ -115,12 +132,14 @@ halo_status check_gemm(const void* a, int64_t lda, const void* b, int64_t ldb, i
 
 size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
 
-// Region sizes of the layer workspace, in carve order; the last region is the scratch the
-// columns passes share (they run one after another on the caller's stream).
+// Region sizes of the layer workspace, in carve order; the backward's last region is the
+// scratch of its three column passes (W, dY, X: one sub-region each, cleared together by the
+// first kernel of the call).
 struct WsPlan {
   size_t off[9];
   size_t total;
   size_t scratch_off, scratch_bytes;
+  size_t scr_w, scr_dy, scr_x;  // sub-region sizes, in this order
 };
 
 WsPlan plan_ws(int64_t m, int64_t n, int64_t k, int backward, int32_t block, halo_dtype io) {
@@ -147,16 +166,13 @@ WsPlan plan_ws(int64_t m, int64_t n, int64_t k, int backward, int32_t block, hal
     p.off[i] = o;
     o += round256(sizes[i]);
   }
-  size_t scratch = 0;
   if (backward) {
-    scratch = fq_ws_bytes(n, k, HALO_ALONG_COLS, block, io);        // W columns along n
-    const size_t s2 = fq_ws_bytes(m, n, HALO_ALONG_COLS, block, io);  // dY columns along m
-    const size_t s3 = fq_ws_bytes(m, k, HALO_ALONG_COLS, block, io);  // X columns along m
-    if (s2 > scratch) scratch = s2;
-    if (s3 > scratch) scratch = s3;
+    p.scr_w = round256(fq_ws_bytes(n, k, HALO_ALONG_COLS, block, io));   // W columns along n
+    p.scr_dy = round256(fq_ws_bytes(m, n, HALO_ALONG_COLS, block, io));  // dY columns along m
+    p.scr_x = round256(fq_ws_bytes(m, k, HALO_ALONG_COLS, block, io));   // X columns along m
   }
   p.scratch_off = o;
-  p.scratch_bytes = round256(scratch);
+  p.scratch_bytes = p.scr_w + p.scr_dy + p.scr_x;
   p.total = o + p.scratch_bytes;
   return p;
 }
@@ -270,10 +286,18 @@ halo_status halo_linear_fwd(const void* x, const void* w, halo_dtype io_type, in
   void* qw = base + p.off[2];
   float* sw = reinterpret_cast<float*>(base + p.off[3]);
   hipStream_t st = (hipStream_t)stream;
-  halo_status s =
-      run_fq(x, io_type, m, k, k, HALO_ALONG_ROWS, block, q_type, qx, k, sx, nullptr, 0, st);
-  if (s == HALO_OK)
-    s = run_fq(w, io_type, n, k, k, HALO_ALONG_ROWS, block, q_type, qw, k, sw, nullptr, 0, st);
+  halo_status s = HALO_OK;
+  if (fq_rows2_supported(k, block)) {  // X and W rows in one launch
+    FqPair pp{};
+    pp.p0 = make_fq(x, m, k, k, HALO_ALONG_ROWS, block, q_type, qx, k, sx);
+    pp.p1 = make_fq(w, n, k, k, HALO_ALONG_ROWS, block, q_type, qw, k, sw);
+    pp.has1 = 1;
+    s = from_hip(launch_fq_rows2_pair(pp, io_type == HALO_BF16 ? 1 : 0, qt_index(q_type), st));
+  } else {
+    s = run_fq(x, io_type, m, k, k, HALO_ALONG_ROWS, block, q_type, qx, k, sx, nullptr, 0, st);
+    if (s == HALO_OK)
+      s = run_fq(w, io_type, n, k, k, HALO_ALONG_ROWS, block, q_type, qw, k, sw, nullptr, 0, st);
+  }
   if (s == HALO_OK) s = gemm_any(qx, q_type, k, sx, qw, q_type, k, sw, m, n, k, y, y_type, n, st);
   return s;
 }
@@ -302,20 +326,53 @@ halo_status halo_linear_bwd(const void* dy, const void* x, const void* w, halo_d
   if (!ws || ws_bytes < p.total) return HALO_ERR_WORKSPACE;
   if (!aligned16(ws)) return HALO_ERR_ALIGN;
   char* base = static_cast<char*>(ws);
-  void* scr = base + p.scratch_off;
-  const size_t scr_bytes = p.scratch_bytes;
+  char* scr = base + p.scratch_off;
+  void* scr_w = scr;
+  void* scr_dy = scr + p.scr_w;
+  void* scr_x = scr + p.scr_w + p.scr_dy;
+  const int inb = io_type == HALO_BF16 ? 1 : 0;
   hipStream_t st = (hipStream_t)stream;
   halo_status s = HALO_OK;
+  // the single-read column passes need their scratch cleared: folded into the first kernel
+  // when that is a rows pass, else one fill
+  bool zero_pending = p.scratch_bytes > 0;
+  auto clear_scratch = [&]() {
+    if (!zero_pending || s != HALO_OK) return;
+    s = from_hip(launch_fill_zero(reinterpret_cast<float*>(scr), (int64_t)(p.scratch_bytes / 4), st));
+    zero_pending = false;
+  };
+  // one column pass along the rows of x (length `rows`): single-read when covered
+  auto cols_pass = [&](const void* xx, int64_t rows, int64_t cols, halo_dtype qt, void* q,
+                       float* sc, void* sws, size_t sbytes) {
+    if (s != HALO_OK) return;
+    if (fq_cols2_supported(rows, cols, block, inb, sbytes)) {
+      const FqArgs a = make_fq(xx, rows, cols, cols, HALO_ALONG_COLS, block, qt, q, rows, sc);
+      s = from_hip(launch_fq_cols2_pair(a, sws, nullptr, nullptr, qt_index(qt), 1, st));
+    } else {
+      s = run_fq(xx, io_type, rows, cols, cols, HALO_ALONG_COLS, block, qt, q, rows, sc, nullptr,
+                 0, st);
+    }
+  };
   if (dx) {  // dX[m x k] = dY W: contraction over n
     void* qdy = base + p.off[0];
     float* sdy = reinterpret_cast<float*>(base + p.off[1]);
     void* qwt = base + p.off[2];
     float* swt = reinterpret_cast<float*>(base + p.off[3]);
-    s = run_fq(dy, io_type, m, n, n, HALO_ALONG_ROWS, block, grad_q_type, qdy, n, sdy, nullptr,
-               0, st);
-    if (s == HALO_OK)
-      s = run_fq(w, io_type, n, k, k, HALO_ALONG_COLS, block, q_type, qwt, n, swt, scr, scr_bytes,
-                 st);
+    if (fq_rows2_supported(n, block)) {
+      FqPair pp{};
+      pp.p0 = make_fq(dy, m, n, n, HALO_ALONG_ROWS, block, grad_q_type, qdy, n, sdy);
+      if (zero_pending) {
+        pp.zero = reinterpret_cast<uint32_t*>(scr);
+        pp.nzero = (int64_t)(p.scratch_bytes / 4);
+        zero_pending = false;
+      }
+      s = from_hip(launch_fq_rows2_pair(pp, inb, qt_index(grad_q_type), st));
+    } else {
+      s = run_fq(dy, io_type, m, n, n, HALO_ALONG_ROWS, block, grad_q_type, qdy, n, sdy, nullptr,
+                 0, st);
+    }
+    clear_scratch();
+    cols_pass(w, n, k, q_type, qwt, swt, scr_w, p.scr_w);
     if (s == HALO_OK)
       s = gemm_any(qdy, grad_q_type, n, sdy, qwt, q_type, n, swt, m, k, n, dx, io_type, k, st);
   }
@@ -324,11 +381,17 @@ halo_status halo_linear_bwd(const void* dy, const void* x, const void* w, halo_d
     float* sdyt = reinterpret_cast<float*>(base + p.off[5]);
     void* qxt = base + p.off[6];
     float* sxt = reinterpret_cast<float*>(base + p.off[7]);
-    s = run_fq(dy, io_type, m, n, n, HALO_ALONG_COLS, block, grad_q_type, qdyt, m, sdyt, scr,
-               scr_bytes, st);
-    if (s == HALO_OK)
-      s = run_fq(x, io_type, m, k, k, HALO_ALONG_COLS, block, q_type, qxt, m, sxt, scr, scr_bytes,
-                 st);
+    clear_scratch();
+    const bool c1 = fq_cols2_supported(m, n, block, inb, p.scr_dy);
+    const bool c2 = fq_cols2_supported(m, k, block, inb, p.scr_x);
+    if (s == HALO_OK && c1 && c2 && grad_q_type == q_type) {  // dY and X columns in one launch
+      const FqArgs a0 = make_fq(dy, m, n, n, HALO_ALONG_COLS, block, grad_q_type, qdyt, m, sdyt);
+      const FqArgs a1 = make_fq(x, m, k, k, HALO_ALONG_COLS, block, q_type, qxt, m, sxt);
+      s = from_hip(launch_fq_cols2_pair(a0, scr_dy, &a1, scr_x, qt_index(q_type), 1, st));
+    } else {
+      cols_pass(dy, m, n, grad_q_type, qdyt, sdyt, scr_dy, p.scr_dy);
+      cols_pass(x, m, k, q_type, qxt, sxt, scr_x, p.scr_x);
+    }
     if (s == HALO_OK)
       s = gemm_any(qdyt, grad_q_type, m, sdyt, qxt, q_type, m, sxt, n, k, m, dw, io_type, k, st);
   }

@@ -41,6 +41,22 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 bool fq_rows2_supported(int64_t len, int block);
 hipError_t launch_fq_rows2(const FqArgs& a, int in_bf16, int qt, hipStream_t st);
 
+// Two rows passes of the same row length, block, input and code type in one launch (p1 is
+// used when has1 != 0), which also clears `nzero` 32-bit words at `zero` (may be NULL).
+struct FqPair {
+  FqArgs p0, p1;
+  int has1;
+  int64_t split;  // set by the launcher
+  uint32_t* zero;
+  int64_t nzero;
+};
+hipError_t launch_fq_rows2_pair(const FqPair& a, int in_bf16, int qt, hipStream_t st);
+
+// Up to two single-read column passes over columns of the same length, block and code type in
+// one launch (a1 may be NULL).  prezeroed: the scratch of both was cleared earlier on st.
+hipError_t launch_fq_cols2_pair(const FqArgs& a0, void* ws0, const FqArgs* a1, void* ws1, int qt,
+                                int prezeroed, hipStream_t st);
+
 // Longest row the single-pass rows kernel takes for this block size.
 int64_t fq_rows_max_len(int block);
 

@@ -151,8 +151,9 @@ def test_workspace_bytes(L):
     # 4096^3 backward: the code matrices plus the columns passes' shared scratch
     big = 4096
     codes = 4 * (r(big * big) + r(4 * big))
-    # (sized for every block; block 2048 needs the most: 128 strips of 32 columns, 2 parts)
-    assert L.halo_linear_workspace_bytes(big, big, big, I8, 1) == codes + r(512 + 4096 * 4)
+    # (one scratch per column pass: W, dY, X; sized for every block, and block 2048 needs the
+    # most: 128 strips of 32 columns, 2 parts)
+    assert L.halo_linear_workspace_bytes(big, big, big, I8, 1) == codes + 3 * r(512 + 4096 * 4)
     assert L.halo_linear_workspace_bytes(-1, n, k, I8, 0) == 0
     assert L.halo_linear_workspace_bytes(m, n, k, BF16, 0) == 0
 

@@ -72,6 +72,8 @@ BWD = [  # m, n, k, block, io, q, gq
     (1024, 512, 256, 512, synth.BF16, "e4m3", "e5m2"),
     (256, 256, 128, 64, synth.F32, "i8", "i8"),
     (512, 512, 256, 256, synth.BF16, "e4m3", "e4m3"),
+    (2048, 2048, 256, 256, synth.BF16, "i8", "i8"),    # every column pass split over 2 tasks
+    (2048, 512, 256, 512, synth.BF16, "e4m3", "e5m2"),  # split dY / X passes, separate launches
 ]
 
 
@@ -104,6 +106,17 @@ def test_linear_bwd_single_outputs():
     assert dxb is None
     dx, dw = H.linear_bwd(to_dev(dy), to_dev(x), to_dev(w), b)
     assert torch.equal(dx, dxo) and torch.equal(dw, dwb)
+
+
+def test_linear_bwd_dw_only_long_columns():
+    # no rows pass precedes the column passes: their scratch is cleared by a fill of its own
+    m, n, k, b = 4096, 256, 128, 256
+    x, w, dy = synth.layer(m, n, k, seed=13)
+    _, dw = H.linear_bwd(to_dev(dy), to_dev(x), to_dev(w), b, want_dx=False)
+    _, dw_ref = H.linear_bwd(to_dev(dy), to_dev(x), to_dev(w), b)
+    assert torch.equal(dw, dw_ref)
+    r64 = O.linear_bwd(dy, x, w, b, O.I8, O.I8, precision=64)
+    assert rel_fro(_np(dw), r64[1]) <= 1e-2
 
 
 def test_rotation_beats_no_rotation_on_outliers():
