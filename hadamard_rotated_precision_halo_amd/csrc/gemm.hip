@@ -24,8 +24,9 @@
 // loads the global chunk that belongs in its physical slot.
 //
 // The product is formed transposed (the MFMA's first operand is the b tile).  The epilogue
-// stages each wave's accumulators in LDS and reads them back row-contiguous, so the stores
-// are full 256- or 512-byte row runs; the scales sa, sb were loaded into LDS at kernel start.
+// stages each wave's results in LDS and reads them back row-contiguous, so the stores are
+// full 256- or 512-byte row runs (bf16 output is dequantised and rounded before staging,
+// halving the staged bytes); the scales sa, sb were loaded into LDS at kernel start.
 // Workgroups are numbered so that each of the 8 XCDs (workgroup i runs on XCD i % 8) gets a
 // contiguous run of tiles, rastered in groups of 4 tile rows, for L2 reuse of both operands.
 #include "halo_device.h"
@@ -287,12 +288,66 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
   __builtin_amdgcn_s_waitcnt(HALO_VMCNT(0));  // no LDS write may outlive the workgroup
 
   // ---- epilogue -----------------------------------------------------------------------
-  // Each wave stages its accumulators in LDS, 32 output rows at a time (row pitch 132 words:
-  // the 16-byte writes of 16 consecutive rows fall in 16 different bank groups), and reads
-  // them back row-contiguous: 32 lanes cover one 128-column row, so stores are 256-byte (bf16)
-  // or 512-byte (fp32, int32) runs.  The dequant (acc * sa[row]) * sb[col] is applied after the
-  // read-back, where each lane owns 4 fixed columns.
   __syncthreads();  // every wave is done with the K slabs
+  if constexpr (OUT == 2) {
+    // bf16 output: the dequant (acc * sa[row]) * sb[col] and the rounding to bf16 happen in
+    // the accumulator layout (lane (fr, fh) of tile (i, j) holds output row j * 32 + fr and
+    // columns i * 32 + g * 8 + fh * 4 + [0, 4), g = 0..3); the packed bf16 are staged in LDS
+    // 32 rows at a time (pitch 264 bytes: the 8-byte writes of 32 consecutive rows cover all
+    // 64 banks) and read back row-contiguous, 16 bytes per lane, 16 lanes per 128-column row.
+    constexpr int BPITCH = 132;  // row pitch in bf16 elements (264 bytes)
+    uint16_t* btile = reinterpret_cast<uint16_t*>(smem) + wave * (32 * BPITCH);
+    float4 sbq[4][4];  // sb of the lane's columns, per (i, g)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq)
+        sbq[i][gq] = *reinterpret_cast<const float4*>(s_sb + wn * 128 + i * 32 + gq * 8 + fh * 4);
+    const int rrow = lane >> 4, rcol = (lane & 15) * 8;  // read-back position
+    const int64_t col0 = n0 + wn * 128 + rcol;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float sar = s_sa[wm * 128 + j * 32 + fr];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          float a[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if constexpr (KIND == 0) a[e] = (float)acc[i][j][gq * 4 + e];
+            else a[e] = acc[i][j][gq * 4 + e];
+          }
+          const float4 sbv = sbq[i][gq];
+          uint2 w;
+          w.x = pack_bf16x2((a[0] * sar) * sbv.x, (a[1] * sar) * sbv.y);
+          w.y = pack_bf16x2((a[2] * sar) * sbv.z, (a[3] * sar) * sbv.w);
+          *reinterpret_cast<uint2*>(btile + fr * BPITCH + i * 32 + gq * 8 + fh * 4) = w;
+        }
+      // the wave reads back only what it wrote: program order plus the LDS wait suffice
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int r = t * 4 + rrow;
+        const int64_t row = m0 + wm * 128 + j * 32 + r;
+        const uint4 w = *reinterpret_cast<const uint4*>(btile + r * BPITCH + rcol);
+        if (row >= g.m || col0 >= g.n) continue;
+        uint16_t* dst = reinterpret_cast<uint16_t*>(g.c) + row * g.ldc + col0;
+        if (col0 + 7 < g.n) {
+          *reinterpret_cast<uint4*>(dst) = w;
+        } else {
+          const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+          for (int e = 0; e < 8 && col0 + e < g.n; ++e)
+            dst[e] = (uint16_t)(wv[e >> 1] >> ((e & 1) * 16));
+        }
+      }
+    }
+    return;
+  }
+  // int32 / fp32 output: each wave stages its raw accumulators in LDS, 32 output rows at a
+  // time (row pitch 132 words: the 16-byte writes of 16 consecutive rows fall in 16 different
+  // bank groups), and reads them back row-contiguous: 32 lanes cover one 128-column row, so
+  // stores are 512-byte runs.  The dequant (acc * sa[row]) * sb[col] is applied after the
+  // read-back, where each lane owns 4 fixed columns.
   constexpr int PITCH = 132;
   uint32_t* stile = reinterpret_cast<uint32_t*>(smem) + wave * (32 * PITCH);
   const int ecol = (lane & 31) * 4;  // 4 consecutive columns of this lane after read-back
