@@ -37,6 +37,9 @@
 namespace halo {
 
 constexpr int BM = 256, BN = 256;
+#ifndef HALO_GEMM_ORDERED
+#define HALO_GEMM_ORDERED 1
+#endif
 constexpr int RING_BYTES = 128 * 1024;          // K-slab ring; the scales follow it
 constexpr int LDS_BYTES = RING_BYTES + 2 * 256 * 4;
 
@@ -164,18 +167,22 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
   // Stage slab kt into ring slot kt % NSTAGE: always 2 * INST direct-to-LDS loads per thread,
   // so the vmcnt arithmetic is uniform.  Slabs past the end reload the last slab (never read)
   // and chunks past k read the row's last chunk instead; their fragments are masked to zero.
-  auto stage = [&](int kt) __attribute__((always_inline)) {
+  // loads [q0, q1) of the slab: load q is operand q % 2, row group q / 2
+  auto stage_part = [&](int kt, int q0, int q1) __attribute__((always_inline)) {
     char* sa = smem + (kt % NSTAGE) * SL::STAGE;
     char* sb = sa + SL::OPER;
     const uint32_t kb = (uint32_t)min(kt, nk - 1) * BK;
 #pragma unroll
-    for (int i = 0; i < INST; ++i) {
+    for (int q = 0; q < 2 * INST; ++q) {
+      if (q < q0 || q >= q1) continue;
+      const int i = q >> 1;
       uint32_t kc = kb + cbo[i];
       if constexpr (MASK) kc = min(kc, klast);
-      dma16(A + aoff[i] + kc, (lds_void*)(sa + (wave * INST + i) * 1024));
-      dma16(Bm + boff[i] + kc, (lds_void*)(sb + (wave * INST + i) * 1024));
+      if (q & 1) dma16(Bm + boff[i] + kc, (lds_void*)(sb + (wave * INST + i) * 1024));
+      else dma16(A + aoff[i] + kc, (lds_void*)(sa + (wave * INST + i) * 1024));
     }
   };
+  auto stage = [&](int kt) __attribute__((always_inline)) { stage_part(kt, 0, 2 * INST); };
 
   using Acc = typename std::conditional<KIND == 0, v16i, v16f>::type;
   using Frag = typename std::conditional<KIND == 0, v4i, v8i>::type;
@@ -252,6 +259,66 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
       if (i < FRAG_READS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
   };
+#if HALO_GEMM_ORDERED
+  // Explicit issue order of a sub-step: MFMA t, then the sub-step's t-th fragment read and
+  // t-th slab load (when there are that many); a scheduling barrier after each group keeps
+  // the order, so the loads and reads are spread evenly between the MFMAs instead of being
+  // issued in a burst that stalls the MFMA issue.
+  auto read_one = [&](int kt, int ks, int q, Frag* da, Frag* db) __attribute__((always_inline)) {
+    const char* sa = smem + (kt % NSTAGE) * SL::STAGE;
+    const char* sb = sa + SL::OPER;
+    const int c0 = KIND == 0 ? ks * 2 + fh : ks * 4 + fh * 2;
+    if constexpr (KIND == 0) {
+      const int t = q >> 1;
+      int keep = -1;
+      if constexpr (MASK) keep = (kt * BK + c0 * 16) < g.k ? -1 : 0;
+      if (q & 1) da[t] = *reinterpret_cast<const v4i*>(sa + SL::off(wm * 128 + t * 32 + fr, c0)) & keep;
+      else db[t] = *reinterpret_cast<const v4i*>(sb + SL::off(wn * 128 + t * 32 + fr, c0)) & keep;
+    } else {
+      const int t = q >> 2, h = q & 1;
+      int keep = -1;
+      if constexpr (MASK) keep = (kt * BK + (c0 + h) * 16) < g.k ? -1 : 0;
+      if (q & 2) {
+        const v4i v = *reinterpret_cast<const v4i*>(sa + SL::off(wm * 128 + t * 32 + fr, c0 + h)) & keep;
+        if (h) da[t].hi = v; else da[t].lo = v;
+      } else {
+        const v4i v = *reinterpret_cast<const v4i*>(sb + SL::off(wn * 128 + t * 32 + fr, c0 + h)) & keep;
+        if (h) db[t].hi = v; else db[t].lo = v;
+      }
+    }
+  };
+  auto load_one = [&](int kt, int q) __attribute__((always_inline)) { stage_part(kt, q, q + 1); };
+  auto ordered_step = [&](const Frag* da, const Frag* db, int rkt, int rks, Frag* nda, Frag* ndb,
+                          int nread, int lkt, int nload) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int i = t >> 2, j = t & 3;
+      if constexpr (KIND == 0)
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(db[i], da[j], acc[i][j], 0, 0, 0);
+      else
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(db[i], da[j], acc[i][j], BF,
+                                                                    AF, 0, 127, 0, 127);
+      if (t < nread) read_one(rkt, rks, t, nda, ndb);
+      if (t < nload) load_one(lkt, t);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto do_slab = [&](int kt, auto P) __attribute__((always_inline)) {
+    constexpr int P0 = decltype(P)::value;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int cur = (P0 + ks) & 1;
+      if (ks + 1 < KS) {
+        ordered_step(fa[cur], fb[cur], kt, ks + 1, fa[cur ^ 1], fb[cur ^ 1], FRAG_READS, 0, 0);
+      } else {
+        __builtin_amdgcn_s_waitcnt(HALO_VMCNT(2 * INST * (NSTAGE - 2)));  // slab kt + 1 landed
+        __syncthreads();
+        ordered_step(fa[cur], fb[cur], kt + 1, 0, fa[cur ^ 1], fb[cur ^ 1], FRAG_READS,
+                     kt + NSTAGE, 2 * INST);
+      }
+    }
+  };
+#else
   auto do_slab = [&](int kt, auto P) __attribute__((always_inline)) {
     constexpr int P0 = decltype(P)::value;
 #pragma unroll
@@ -271,6 +338,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
       }
     }
   };
+#endif
 
 #pragma unroll
   for (int t = 0; t < NSTAGE; ++t) stage(t);
