@@ -37,8 +37,8 @@
 namespace halo {
 
 constexpr int BM = 256, BN = 256;
-#ifndef HALO_GEMM_ORDERED
-#define HALO_GEMM_ORDERED 1
+#ifndef HALO_GEMM_WN
+#define HALO_GEMM_WN 4
 #endif
 constexpr int RING_BYTES = 128 * 1024;          // K-slab ring; the scales follow it
 constexpr int LDS_BYTES = RING_BYTES + 2 * 256 * 4;
@@ -110,10 +110,17 @@ __device__ __forceinline__ void store4(void* c, int64_t ldc, int64_t row, int64_
 // KIND 0: INT8.  KIND 1: FP8 with formats AF (a) and BF (b): 0 = E4M3, 1 = E5M2.
 // OUT 0: int32 accumulators, 1: fp32, 2: bf16.  MASK: fragments past k are zeroed (needed when
 // k is not a multiple of the slab, or when the FP8 loop pads one extra slab).
-template <int KIND, int AF, int BF, int OUT, bool MASK, int BK>
-__global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
+// WN: waves along N (2: four waves of 128 x 128, one per SIMD; 4: eight waves of 128 x 64, two
+// per SIMD, so one wave's stalls at the barrier or on loads are covered by the other's MFMAs).
+template <int KIND, int AF, int BF, int OUT, bool MASK, int BK, int WN>
+__global__ __launch_bounds__(128 * WN, 1) void gemm_kernel(GemmArgs g) {
   using SL = Slab<BK>;
-  constexpr int NSTAGE = SL::NSTAGE, INST = SL::INST, RPI = SL::RPI;
+  constexpr int NW = 2 * WN, NT = 64 * NW;         // waves, threads
+  constexpr int TN = BN / WN;                      // output columns per wave
+  constexpr int FA = 4, FB = TN / 32;              // 32-row fragments of a and b per wave
+  constexpr int NSTAGE = SL::NSTAGE, RPI = SL::RPI;
+  constexpr int INST = SL::OPER / (NT * 16);       // loads per thread per operand per slab
+  constexpr int WROWS = INST * RPI;                // slab rows one wave loads per operand
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   float* s_sa = reinterpret_cast<float*>(smem + RING_BYTES);
   float* s_sb = s_sa + 256;
@@ -134,26 +141,28 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS bases in SGPRs
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
 
   // scales of this tile's rows and columns (written to LDS once the prologue loads landed)
   float my_sa = 0.f, my_sb = 0.f;
   if constexpr (OUT != 0) {
-    my_sa = g.sa[min(m0 + tid, g.m - 1)];
-    my_sb = g.sb[min(n0 + tid, g.n - 1)];
+    if (tid < 256) {
+      my_sa = g.sa[min(m0 + tid, g.m - 1)];
+      my_sb = g.sb[min(n0 + tid, g.n - 1)];
+    }
   }
 
   // ---- direct-to-LDS assignment -----------------------------------------------------
   // Wave w's instruction i fills LDS bytes [(INST w + i) KB, +1 KB) of an operand's slab =
-  // rows 64 w + RPI i + [0, RPI); lane l lands in physical chunk l % CHUNKS of row
-  // 64 w + RPI i + l / CHUNKS and loads that row's logical chunk (l % CHUNKS) ^ swz(row).
+  // rows WROWS w + RPI i + [0, RPI); lane l lands in physical chunk l % CHUNKS of row
+  // WROWS w + RPI i + l / CHUNKS and loads that row's logical chunk (l % CHUNKS) ^ swz(row).
   const char* __restrict__ A = reinterpret_cast<const char*>(g.a);
   const char* __restrict__ Bm = reinterpret_cast<const char*>(g.b);
   uint32_t aoff[INST], boff[INST];  // byte offsets of the lane's rows (operands are < 4 GB)
   uint32_t cbo[INST];               // byte offset of the lane's chunk within a slab row
 #pragma unroll
   for (int i = 0; i < INST; ++i) {
-    const int r = wave * 64 + i * RPI + lane / SL::CHUNKS;
+    const int r = wave * WROWS + i * RPI + lane / SL::CHUNKS;
     cbo[i] = (uint32_t)(((lane % SL::CHUNKS) ^ SL::swz(r)) << 4);
     aoff[i] = (uint32_t)(min(m0 + r, g.m - 1) * g.lda);  // clamped rows feed unused outputs
     boff[i] = (uint32_t)(min(n0 + r, g.n - 1) * g.ldb);
@@ -164,10 +173,10 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
   const int nkr = (nk + UNROLL - 1) / UNROLL * UNROLL;
   const uint32_t klast = (uint32_t)g.k - 16;       // last in-bounds chunk of a row
 
-  // Stage slab kt into ring slot kt % NSTAGE: always 2 * INST direct-to-LDS loads per thread,
-  // so the vmcnt arithmetic is uniform.  Slabs past the end reload the last slab (never read)
-  // and chunks past k read the row's last chunk instead; their fragments are masked to zero.
-  // loads [q0, q1) of the slab: load q is operand q % 2, row group q / 2
+  // Loads [q0, q1) of slab kt into ring slot kt % NSTAGE (load q: operand q % 2, row group
+  // q / 2).  A whole slab is always 2 * INST direct-to-LDS loads per thread, so the vmcnt
+  // arithmetic is uniform.  Slabs past the end reload the last slab (never read) and chunks
+  // past k read the row's last chunk instead; their fragments are masked to zero.
   auto stage_part = [&](int kt, int q0, int q1) __attribute__((always_inline)) {
     char* sa = smem + (kt % NSTAGE) * SL::STAGE;
     char* sb = sa + SL::OPER;
@@ -186,120 +195,64 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
 
   using Acc = typename std::conditional<KIND == 0, v16i, v16f>::type;
   using Frag = typename std::conditional<KIND == 0, v4i, v8i>::type;
-  Acc acc[4][4];
+  Acc acc[FB][FA];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FB; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < FA; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
 
   const int fr = lane & 31, fh = lane >> 5;  // fragment row and K half
-  Frag fa[2][4], fb[2][4];
-  auto load_frags = [&](int kt, int ks, Frag* da, Frag* db) __attribute__((always_inline)) {
-    const char* sa = smem + (kt % NSTAGE) * SL::STAGE;
-    const char* sb = sa + SL::OPER;
-    const int c0 = KIND == 0 ? ks * 2 + fh : ks * 4 + fh * 2;  // first 16-byte chunk
-    int keep0 = -1, keep1 = -1;
-    if constexpr (MASK) {
-      keep0 = (kt * BK + c0 * 16) < g.k ? -1 : 0;
-      keep1 = (kt * BK + c0 * 16 + 16) < g.k ? -1 : 0;
-    }
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int rb = wn * 128 + t * 32 + fr, ra = wm * 128 + t * 32 + fr;
-      if constexpr (KIND == 0) {
-        db[t] = *reinterpret_cast<const v4i*>(sb + SL::off(rb, c0)) & keep0;
-        da[t] = *reinterpret_cast<const v4i*>(sa + SL::off(ra, c0)) & keep0;
-      } else {
-        v4i b0 = *reinterpret_cast<const v4i*>(sb + SL::off(rb, c0)) & keep0;
-        v4i b1 = *reinterpret_cast<const v4i*>(sb + SL::off(rb, c0 + 1)) & keep1;
-        v4i a0 = *reinterpret_cast<const v4i*>(sa + SL::off(ra, c0)) & keep0;
-        v4i a1 = *reinterpret_cast<const v4i*>(sa + SL::off(ra, c0 + 1)) & keep1;
-        db[t] = Frag{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-        da[t] = Frag{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-      }
-    }
-  };
-  auto mfma_step = [&](const Frag* da, const Frag* db) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if constexpr (KIND == 0)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(db[i], da[j], acc[i][j], 0, 0, 0);
-        else  // first operand = b tile (format BF), second = a tile (format AF); scales 2^0
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(db[i], da[j], acc[i][j], BF,
-                                                                      AF, 0, 127, 0, 127);
-      }
-  };
+  Frag fa[2][FA], fb[2][FB];
 
   // ---- main loop -------------------------------------------------------------------
-  // Sub-steps run in one flat sequence (slab kt, sub-step ks); the next sub-step's fragments
-  // are read while the current one's 16 MFMAs issue.  Before the last sub-step of slab kt the
-  // wave waits for its own loads of slab kt + 1 (later slabs may stay in flight), the barrier
-  // makes every wave's loads visible, and slab kt + NSTAGE is issued into slab kt's slot,
-  // which no wave reads any more.  The loop body has no branches, so the accumulators stay in
-  // AGPRs; scheduling hints spread reads and loads between the MFMAs.
-  constexpr int FRAG_READS = KIND == 0 ? 8 : 16;  // ds_read_b128 per sub-step
-  auto hint_reads = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < FRAG_READS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 fragment read
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
-  };
-  auto hint_reads_loads = [&]() __attribute__((always_inline)) {
-    constexpr int LD = 2 * INST;  // slab loads to spread over the 16 MFMAs
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // 1 MFMA
-      if (i < LD) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);     // 1 slab load
-      if (i < FRAG_READS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-  };
-#if HALO_GEMM_ORDERED
-  // Explicit issue order of a sub-step: MFMA t, then the sub-step's t-th fragment read and
-  // t-th slab load (when there are that many); a scheduling barrier after each group keeps
-  // the order, so the loads and reads are spread evenly between the MFMAs instead of being
-  // issued in a burst that stalls the MFMA issue.
+  // Sub-steps run in one flat sequence (slab kt, sub-step ks).  Issue order is explicit: MFMA
+  // t of a sub-step is followed by its share of the next sub-step's fragment reads and, in the
+  // slab's last sub-step, of the next slab loads; a scheduling barrier after each group keeps
+  // the order, so reads and loads are spread evenly between the MFMAs (a burst of loads, each
+  // needing its own M0, stalls the MFMA issue).  Before the last sub-step of slab kt the wave
+  // waits for its own loads of slab kt + 1, the barrier makes every wave's loads visible, and
+  // slab kt + NSTAGE is issued into slab kt's slot, which no wave reads any more.  The loop
+  // body has no branches, so the accumulators stay in AGPRs.
+  constexpr int RPF = KIND == 0 ? 1 : 2;             // ds_read_b128 per fragment
+  constexpr int FRAG_READS = (FA + FB) * RPF;        // per sub-step
+  constexpr int NMF = FA * FB;                       // MFMAs per sub-step
+  // read q of a sub-step: fragment q / RPF (b fragments first), 16-byte half q % RPF
   auto read_one = [&](int kt, int ks, int q, Frag* da, Frag* db) __attribute__((always_inline)) {
     const char* sa = smem + (kt % NSTAGE) * SL::STAGE;
     const char* sb = sa + SL::OPER;
-    const int c0 = KIND == 0 ? ks * 2 + fh : ks * 4 + fh * 2;
+    const int c0 = KIND == 0 ? ks * 2 + fh : ks * 4 + fh * 2;  // first 16-byte chunk
+    const int f = q / RPF, h = q % RPF;
+    int keep = -1;
+    if constexpr (MASK) keep = (kt * BK + (c0 + h) * 16) < g.k ? -1 : 0;
+    const bool isb = f < FB;
+    const int t = isb ? f : f - FB;
+    const char* base = isb ? sb : sa;
+    const int row = isb ? wn * TN + t * 32 + fr : wm * 128 + t * 32 + fr;
+    const v4i v = *reinterpret_cast<const v4i*>(base + SL::off(row, c0 + h)) & keep;
+    Frag* dst = isb ? &db[t] : &da[t];
     if constexpr (KIND == 0) {
-      const int t = q >> 1;
-      int keep = -1;
-      if constexpr (MASK) keep = (kt * BK + c0 * 16) < g.k ? -1 : 0;
-      if (q & 1) da[t] = *reinterpret_cast<const v4i*>(sa + SL::off(wm * 128 + t * 32 + fr, c0)) & keep;
-      else db[t] = *reinterpret_cast<const v4i*>(sb + SL::off(wn * 128 + t * 32 + fr, c0)) & keep;
+      *dst = v;
     } else {
-      const int t = q >> 2, h = q & 1;
-      int keep = -1;
-      if constexpr (MASK) keep = (kt * BK + (c0 + h) * 16) < g.k ? -1 : 0;
-      if (q & 2) {
-        const v4i v = *reinterpret_cast<const v4i*>(sa + SL::off(wm * 128 + t * 32 + fr, c0 + h)) & keep;
-        if (h) da[t].hi = v; else da[t].lo = v;
-      } else {
-        const v4i v = *reinterpret_cast<const v4i*>(sb + SL::off(wn * 128 + t * 32 + fr, c0 + h)) & keep;
-        if (h) db[t].hi = v; else db[t].lo = v;
-      }
+      if (h) dst->hi = v;
+      else dst->lo = v;
     }
   };
-  auto load_one = [&](int kt, int q) __attribute__((always_inline)) { stage_part(kt, q, q + 1); };
   auto ordered_step = [&](const Frag* da, const Frag* db, int rkt, int rks, Frag* nda, Frag* ndb,
-                          int nread, int lkt, int nload) __attribute__((always_inline)) {
+                          int lkt, bool loads) __attribute__((always_inline)) {
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const int i = t >> 2, j = t & 3;
+    for (int t = 0; t < NMF; ++t) {
+      const int i = t / FA, j = t % FA;
       if constexpr (KIND == 0)
         acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(db[i], da[j], acc[i][j], 0, 0, 0);
-      else
+      else  // first operand = b tile (format BF), second = a tile (format AF); scales 2^0
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(db[i], da[j], acc[i][j], BF,
                                                                     AF, 0, 127, 0, 127);
-      if (t < nread) read_one(rkt, rks, t, nda, ndb);
-      if (t < nload) load_one(lkt, t);
+#pragma unroll
+      for (int q = t * FRAG_READS / NMF; q < (t + 1) * FRAG_READS / NMF; ++q)
+        read_one(rkt, rks, q, nda, ndb);
+      if (loads) stage_part(lkt, t * 2 * INST / NMF, (t + 1) * 2 * INST / NMF);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -309,46 +262,27 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
     for (int ks = 0; ks < KS; ++ks) {
       const int cur = (P0 + ks) & 1;
       if (ks + 1 < KS) {
-        ordered_step(fa[cur], fb[cur], kt, ks + 1, fa[cur ^ 1], fb[cur ^ 1], FRAG_READS, 0, 0);
+        ordered_step(fa[cur], fb[cur], kt, ks + 1, fa[cur ^ 1], fb[cur ^ 1], 0, false);
       } else {
         __builtin_amdgcn_s_waitcnt(HALO_VMCNT(2 * INST * (NSTAGE - 2)));  // slab kt + 1 landed
         __syncthreads();
-        ordered_step(fa[cur], fb[cur], kt + 1, 0, fa[cur ^ 1], fb[cur ^ 1], FRAG_READS,
-                     kt + NSTAGE, 2 * INST);
+        ordered_step(fa[cur], fb[cur], kt + 1, 0, fa[cur ^ 1], fb[cur ^ 1], kt + NSTAGE, true);
       }
     }
   };
-#else
-  auto do_slab = [&](int kt, auto P) __attribute__((always_inline)) {
-    constexpr int P0 = decltype(P)::value;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int cur = (P0 + ks) & 1;
-      if (ks + 1 < KS) {
-        load_frags(kt, ks + 1, fa[cur ^ 1], fb[cur ^ 1]);
-        mfma_step(fa[cur], fb[cur]);
-        hint_reads();
-      } else {
-        __builtin_amdgcn_s_waitcnt(HALO_VMCNT(2 * INST * (NSTAGE - 2)));  // slab kt + 1 landed
-        __syncthreads();
-        stage(kt + NSTAGE);
-        load_frags(kt + 1, 0, fa[cur ^ 1], fb[cur ^ 1]);
-        mfma_step(fa[cur], fb[cur]);
-        hint_reads_loads();
-      }
-    }
-  };
-#endif
 
 #pragma unroll
   for (int t = 0; t < NSTAGE; ++t) stage(t);
   __builtin_amdgcn_s_waitcnt(HALO_VMCNT(2 * INST * (NSTAGE - 1)));  // slab 0 and the scales
   if constexpr (OUT != 0) {
-    s_sa[tid] = my_sa;
-    s_sb[tid] = my_sb;
+    if (tid < 256) {
+      s_sa[tid] = my_sa;
+      s_sb[tid] = my_sb;
+    }
   }
   __syncthreads();
-  load_frags(0, 0, fa[0], fb[0]);
+#pragma unroll
+  for (int q = 0; q < FRAG_READS; ++q) read_one(0, 0, q, fa[0], fb[0]);
   for (int kt = 0; kt < nkr; kt += UNROLL) {
     do_slab(kt, std::integral_constant<int, 0>{});
     if constexpr (UNROLL == 2) do_slab(kt + 1, std::integral_constant<int, KS & 1>{});
@@ -356,28 +290,30 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
   __builtin_amdgcn_s_waitcnt(HALO_VMCNT(0));  // no LDS write may outlive the workgroup
 
   // ---- epilogue -----------------------------------------------------------------------
+  // Lane (fr, fh) of accumulator tile (i, j) holds output row wm * 128 + j * 32 + fr and
+  // columns wn * TN + i * 32 + g * 8 + fh * 4 + [0, 4), g = 0..3.  Each wave stages its
+  // results in LDS 32 rows at a time and reads them back row-contiguous, 16 bytes per lane.
   __syncthreads();  // every wave is done with the K slabs
   if constexpr (OUT == 2) {
-    // bf16 output: the dequant (acc * sa[row]) * sb[col] and the rounding to bf16 happen in
-    // the accumulator layout (lane (fr, fh) of tile (i, j) holds output row j * 32 + fr and
-    // columns i * 32 + g * 8 + fh * 4 + [0, 4), g = 0..3); the packed bf16 are staged in LDS
-    // 32 rows at a time (pitch 264 bytes: the 8-byte writes of 32 consecutive rows cover all
-    // 64 banks) and read back row-contiguous, 16 bytes per lane, 16 lanes per 128-column row.
-    constexpr int BPITCH = 132;  // row pitch in bf16 elements (264 bytes)
+    // bf16: dequant (acc * sa[row]) * sb[col] and rounding in the accumulator layout; the
+    // staged row pitch (TN + 4 elements) makes the 8-byte writes of 32 consecutive rows cover
+    // all 64 banks.
+    constexpr int BPITCH = TN + 4;
+    constexpr int LPR = TN / 8, RPIT = 64 / LPR;    // lanes per row, rows per read-back
     uint16_t* btile = reinterpret_cast<uint16_t*>(smem) + wave * (32 * BPITCH);
-    float4 sbq[4][4];  // sb of the lane's columns, per (i, g)
+    float4 sbq[FB][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < FB; ++i)
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq)
-        sbq[i][gq] = *reinterpret_cast<const float4*>(s_sb + wn * 128 + i * 32 + gq * 8 + fh * 4);
-    const int rrow = lane >> 4, rcol = (lane & 15) * 8;  // read-back position
-    const int64_t col0 = n0 + wn * 128 + rcol;
+        sbq[i][gq] = *reinterpret_cast<const float4*>(s_sb + wn * TN + i * 32 + gq * 8 + fh * 4);
+    const int rrow = lane / LPR, rcol = (lane % LPR) * 8;
+    const int64_t col0 = n0 + wn * TN + rcol;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < FA; ++j) {
       const float sar = s_sa[wm * 128 + j * 32 + fr];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < FB; ++i)
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
           float a[4];
@@ -394,8 +330,8 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
         }
       // the wave reads back only what it wrote: program order plus the LDS wait suffice
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int r = t * 4 + rrow;
+      for (int t = 0; t < 32 / RPIT; ++t) {
+        const int r = t * RPIT + rrow;
         const int64_t row = m0 + wm * 128 + j * 32 + r;
         const uint4 w = *reinterpret_cast<const uint4*>(btile + r * BPITCH + rcol);
         if (row >= g.m || col0 >= g.n) continue;
@@ -411,26 +347,24 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
     }
     return;
   }
-  // int32 / fp32 output: each wave stages its raw accumulators in LDS, 32 output rows at a
-  // time (row pitch 132 words: the 16-byte writes of 16 consecutive rows fall in 16 different
-  // bank groups), and reads them back row-contiguous: 32 lanes cover one 128-column row, so
-  // stores are 512-byte runs.  The dequant (acc * sa[row]) * sb[col] is applied after the
-  // read-back, where each lane owns 4 fixed columns.
-  constexpr int PITCH = 132;
+  // int32 / fp32: the raw accumulators are staged (row pitch TN + 4 words: the 16-byte writes
+  // of 16 consecutive rows fall in 16 different bank groups) and read back 4 columns per lane;
+  // the dequant is applied after the read-back, where each lane owns 4 fixed columns.
+  constexpr int PITCH = TN + 4;
+  constexpr int ELR = TN / 4, ERPIT = 64 / ELR;      // lanes per row, rows per read-back
   uint32_t* stile = reinterpret_cast<uint32_t*>(smem) + wave * (32 * PITCH);
-  const int ecol = (lane & 31) * 4;  // 4 consecutive columns of this lane after read-back
-  const int64_t col0 = n0 + wn * 128 + ecol;
+  const int ecol = (lane % ELR) * 4;
+  const int64_t col0 = n0 + wn * TN + ecol;
   float4 sbv = make_float4(0.f, 0.f, 0.f, 0.f);
-  if constexpr (OUT != 0) sbv = *reinterpret_cast<const float4*>(s_sb + wn * 128 + ecol);
+  if constexpr (OUT != 0) sbv = *reinterpret_cast<const float4*>(s_sb + wn * TN + ecol);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    // lane (fr, fh) holds row fr, columns i * 32 + gq * 8 + fh * 4 + [0, 4) of this chunk
+  for (int j = 0; j < FA; ++j) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < FB; ++i)
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
         uint4 w;
-        if constexpr (KIND == 0) {  // raw int32; converted after the read-back
+        if constexpr (KIND == 0) {
           w = make_uint4(acc[i][j][gq * 4 + 0], acc[i][j][gq * 4 + 1], acc[i][j][gq * 4 + 2],
                          acc[i][j][gq * 4 + 3]);
         } else {
@@ -441,8 +375,8 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
       }
     // the wave reads back only what it wrote: program order plus the LDS wait suffice
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const int r = t * 2 + (lane >> 5);
+    for (int t = 0; t < 32 / ERPIT; ++t) {
+      const int r = t * ERPIT + lane / ELR;
       const int64_t row = m0 + wm * 128 + j * 32 + r;
       const uint4 w = *reinterpret_cast<const uint4*>(stile + r * PITCH + ecol);
       if (row >= g.m || col0 >= g.n) continue;
@@ -471,18 +405,19 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs g) {
 
 template <int KIND, int AF, int BF, int OUT, bool MASK, int BK>
 static hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
+  constexpr int WN = HALO_GEMM_WN;
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
   std::call_once(once, [] {
     attr_err = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&gemm_kernel<KIND, AF, BF, OUT, MASK, BK>),
+        reinterpret_cast<const void*>(&gemm_kernel<KIND, AF, BF, OUT, MASK, BK, WN>),
         hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
   });
   if (attr_err != hipSuccess) return attr_err;
   const int64_t tiles = ((g.m + BM - 1) / BM) * ((g.n + BN - 1) / BN);
   if (tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_kernel<KIND, AF, BF, OUT, MASK, BK>), dim3((unsigned)tiles), dim3(256),
-                     LDS_BYTES, st, g);
+  hipLaunchKernelGGL((gemm_kernel<KIND, AF, BF, OUT, MASK, BK, WN>), dim3((unsigned)tiles),
+                     dim3(128 * WN), LDS_BYTES, st, g);
   return hipGetLastError();
 }
 
