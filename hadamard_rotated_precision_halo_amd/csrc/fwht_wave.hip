@@ -249,6 +249,39 @@ __device__ __forceinline__ float stored_scale(const FqArgs& a, float mx) {
 // rows kernel
 // ---------------------------------------------------------------------------
 
+// One wave's slice of a rows pass with L <= 4096 and 4096 % L == 0: wave `gw` of the pass owns
+// rows [gw * 4096 / L, (gw + 1) * 4096 / L).  Lanes past the last row idle.
+template <typename Tin, int B, int QT>
+__device__ __forceinline__ void rows_wave(const FqArgs& a, int64_t gw, int lane) {
+  using S = Slice<B>;
+  const int L = (int)a.len;
+  const int64_t rpw = 4096 / L;              // rows per wave
+  const int r_in_wave = S::off(lane, 0) / L;
+  const int64_t row = gw * rpw + r_in_wave;
+  const int col0 = -r_in_wave * L;           // so that col0 + off(lane, j) is the column
+  const int row_lanes_log2 = 31 - __builtin_clz((unsigned)(L / 64));
+  const bool valid = row < a.nvec;
+  const Tin* __restrict__ xin = reinterpret_cast<const Tin*>(a.x);
+  // idle lanes read the first chunk of row 0
+  const Tin* rp = xin + (valid ? row : 0) * a.ldx;
+  float v[64];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int c = valid ? col0 + S::off(lane, j) : 0;
+    load8<Tin>(rp + c, &v[j * 8]);
+  }
+  const float sgn = rotate64<B>(v, lane);
+  float mx = valid ? absmax64(v) : 0.f;
+  mx = lane_max(mx, row_lanes_log2);
+  const bool writer = (lane & ((1 << row_lanes_log2) - 1)) == 0;
+  if (!valid) return;
+  if (writer) a.scale[row] = stored_scale<QT>(a, mx);
+  const float mul = quant_mul<QT>(a, mx) * sgn;
+  const int64_t base = row * a.ldq + col0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) store_chunk8<QT>(a.q, base + S::off(lane, j), &v[j * 8], mul);
+}
+
 // QT: 0 INT8, 1 E4M3, 2 E5M2, 3 fp32 rotated values.
 // multi = 1: one row per workgroup, wave w owns columns [4096 w, 4096 (w + 1)).
 // multi = 0: 4096 % L == 0, each wave owns 4096 / L whole rows.
@@ -266,30 +299,15 @@ __global__ __launch_bounds__(1024) void fq_rows2_kernel(FqPair pp, int multi) {
   const bool second = (int64_t)blockIdx.x >= pp.split;
   const FqArgs a = second ? pp.p1 : pp.p0;
   const int bid = (int)(blockIdx.x - (second ? pp.split : 0));
-
-  int64_t row;
-  int col0;  // column of the slice start within the row
-  int row_lanes_log2;
-  bool valid;
-  if (multi) {
-    row = bid;
-    col0 = w * 4096;
-    row_lanes_log2 = 6;
-    valid = col0 + S::off(lane, 0) < a.len;  // lanes past the row end idle (a whole lane or none)
-  } else {
-    const int L = (int)a.len;
-    const int rpw = 4096 / L;              // rows per wave
-    const int first = (bid * nw + w) * rpw;
-    const int r_in_wave = S::off(lane, 0) / L;
-    row = (int64_t)first + r_in_wave;
-    col0 = -r_in_wave * L;                 // so that col0 + off(lane, j) is the column
-    row_lanes_log2 = 31 - __builtin_clz((unsigned)(L / 64));
-    valid = row < a.nvec;
+  if (!multi) {
+    rows_wave<Tin, B, QT>(a, (int64_t)bid * nw + w, lane);
+    return;
   }
+  const int64_t row = bid;
+  const int col0 = w * 4096;
+  const bool valid = col0 + S::off(lane, 0) < a.len;  // lanes past the row end idle (whole lanes)
   const Tin* __restrict__ xin = reinterpret_cast<const Tin*>(a.x);
-  // idle lanes (past the row end, or past the last row) read the first chunk of row 0
-  const Tin* rp = xin + (valid ? row : 0) * a.ldx;
-
+  const Tin* rp = xin + row * a.ldx;
   float v[64];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -297,19 +315,16 @@ __global__ __launch_bounds__(1024) void fq_rows2_kernel(FqPair pp, int multi) {
     load8<Tin>(rp + c, &v[j * 8]);
   }
   const float sgn = rotate64<B>(v, lane);
-
   float mx = valid ? absmax64(v) : 0.f;
-  mx = lane_max(mx, row_lanes_log2);
-  if (multi && nw > 1) {
+  mx = lane_max(mx, 6);
+  if (nw > 1) {
     __shared__ float s_wmax[16];
     if (lane == 0) s_wmax[w] = mx;
     __syncthreads();
     mx = 0.f;
     for (int i = 0; i < nw; ++i) mx = __builtin_fmaxf(mx, s_wmax[i]);
   }
-
-  const bool writer = multi ? (w == 0 && lane == 0) : ((lane & ((1 << row_lanes_log2) - 1)) == 0);
-  if (valid && writer) a.scale[row] = stored_scale<QT>(a, mx);
+  if (w == 0 && lane == 0) a.scale[row] = stored_scale<QT>(a, mx);
   if (!valid) return;
   const float mul = quant_mul<QT>(a, mx) * sgn;
   const int64_t base = row * a.ldq + col0;
@@ -369,43 +384,35 @@ __device__ __forceinline__ uint32_t bf16_pair(uint32_t lo_word, uint32_t hi_word
   return __builtin_amdgcn_perm(hi_word, lo_word, half ? 0x07060302u : 0x05040100u);
 }
 
-// One column pass of a launch: its arguments and its scratch (column maxima and per-strip
-// arrival counters, both zero at launch; unused when P == 1).
-struct Cols2Prob {
+// One column pass: its arguments, its geometry (R rows per task, P tasks per strip of C =
+// 65536 / R columns) and its scratch (column maxima and per-strip arrival counters, both zero
+// at launch; unused when P == 1).
+struct ColsProb {
   FqArgs a;
   float* colmax;
   uint32_t* arrive;
-};
-// Up to two passes over columns of the same length (tasks below `split` run the first).
-struct Cols2Pair {
-  Cols2Prob p0, p1;
-  int64_t split, tasks;
   int R, P, C;
 };
 
+// One task (one R-row part of one column strip) of a column pass, run by a whole workgroup of
+// 16 waves.
 template <int B, int QT>
-__global__ __launch_bounds__(1024) void fq_cols2_kernel(Cols2Pair cp) {
-  extern __shared__ __attribute__((aligned(16))) uint4 lds[];
+__device__ __forceinline__ void cols_task(const ColsProb& pr, int64_t ltask, uint4* lds) {
   using S = Slice<B>;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int R = cp.R, P = cp.P, C = cp.C;
+  const FqArgs& a = pr.a;
+  const int R = pr.R, P = pr.P, C = pr.C;
   const int CC = C / 8;                      // 16-byte column chunks per row of the tile
   const int cpw = 4096 / R;                  // column segments per wave
   const int cc = t % CC, rg = t / CC;        // loader: column chunk, group of 8 rows
   const int row_lanes_log2 = 31 - __builtin_clz((unsigned)(R / 64));
-
-  for (int64_t task = blockIdx.x; task < cp.tasks; task += gridDim.x) {
-    const bool second = task >= cp.split;
-    const Cols2Prob pr = second ? cp.p1 : cp.p0;
-    const FqArgs& a = pr.a;
-    float* colmax = pr.colmax;
-    uint32_t* arrive = pr.arrive;
-    const int64_t ncols = a.nvec;
-    const uint16_t* __restrict__ xin = reinterpret_cast<const uint16_t*>(a.x);
-    const int64_t ltask = task - (second ? cp.split : 0);
-    const int64_t strip = ltask / P;
-    const int part = (int)(ltask % P);
-    const int64_t c0 = strip * C;
+  float* colmax = pr.colmax;
+  uint32_t* arrive = pr.arrive;
+  const int64_t ncols = a.nvec;
+  const uint16_t* __restrict__ xin = reinterpret_cast<const uint16_t*>(a.x);
+  const int64_t strip = ltask / P;
+  const int part = (int)(ltask % P);
+  const int64_t c0 = strip * C;
 
     // ---- load 8 rows x 8 columns, transpose, write to LDS ------------------------------
     {
@@ -454,17 +461,21 @@ __global__ __launch_bounds__(1024) void fq_cols2_kernel(Cols2Pair cp) {
     // ---- column maxima of a strip split over P tasks ---------------------------------------
     // Device-scope atomics only (they are performed at the device's coherence point, across
     // XCDs): each task max-reduces its partial maxima into colmax (non-negative floats order
-    // like their bit patterns) with returning atomics, so they have been performed before the
-    // barrier; one thread then counts the task in, waits for all P, and every lane reads the
-    // column maxima back with atomic loads.  No cache-wide fence is needed.
+    // like their bit patterns) and waits for their returned values; one thread then counts the task
+    // in and waits for all P; one thread per column reads the final maximum back with an
+    // atomic load and shares it through LDS.  No cache-wide fence is needed.
     if (P > 1) {
+      __shared__ float s_cmax[1024];
       uint32_t* cm = reinterpret_cast<uint32_t*>(colmax);
       uint32_t seen = 0;
       if (valid && writer)
         seen = __hip_atomic_fetch_max(&cm[col], __float_as_uint(mx), __ATOMIC_RELAXED,
                                       __HIP_MEMORY_SCOPE_AGENT);
-      // the returned value is consumed, so the atomic has completed before the barrier
-      if (__builtin_expect(seen == 0xffffffffu, 0)) mx = __uint_as_float(seen);
+      // every wave waits for the values its atomics return (so they have been performed at
+      // the coherence point) before it reaches the barrier, so the arrival counted below
+      // covers them: a workgroup barrier alone does not wait for outstanding memory operations,
+      // and an unused return value would let the compiler drop the wait
+      asm volatile("s_waitcnt vmcnt(0)" ::"v"(seen) : "memory");
       __syncthreads();
       if (t == 0) {
         __hip_atomic_fetch_add(&arrive[strip], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -478,8 +489,11 @@ __global__ __launch_bounds__(1024) void fq_cols2_kernel(Cols2Pair cp) {
         }
       }
       __syncthreads();
-      if (valid)
-        mx = __uint_as_float(__hip_atomic_load(&cm[col], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      if (t < C && c0 + t < ncols)
+        s_cmax[t] = __uint_as_float(
+            __hip_atomic_load(&cm[c0 + t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      __syncthreads();
+      if (valid) mx = s_cmax[w * cpw + seg];
     }
 
     // ---- quantise and store the transposed codes ------------------------------------------
@@ -490,7 +504,42 @@ __global__ __launch_bounds__(1024) void fq_cols2_kernel(Cols2Pair cp) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) store_chunk8<QT>(a.q, base + S::off(lane, j), &v[j * 8], mul);
     }
+}
+
+template <int B, int QT>
+__global__ __launch_bounds__(1024) void fq_cols2_kernel(ColsProb c0, ColsProb c1, int64_t split,
+                                                        int64_t tasks) {
+  extern __shared__ __attribute__((aligned(16))) uint4 lds[];
+  for (int64_t task = blockIdx.x; task < tasks; task += gridDim.x) {
+    const bool second = task >= split;
+    const ColsProb pr = second ? c1 : c0;
+    cols_task<B, QT>(pr, task - (second ? split : 0), lds);
     __syncthreads();  // the next task overwrites the LDS tile
+  }
+}
+
+// The rotation passes of a layer backward in one launch: the rows of dY (codes QG) and the
+// columns of W (QW), dY (QG) and X (QW).  Workgroups [0, rows_wg) run the rows pass, 16 waves
+// each; the column passes follow in order, one task per workgroup.  All passes read bf16.
+struct FqBatch {
+  FqArgs rows;
+  int64_t rows_wg;
+  ColsProb cw, cdy, cx;
+  int64_t end_w, end_dy, end_x;  // one past the last workgroup of each column pass
+};
+
+template <int B, int QG, int QW>
+__global__ __launch_bounds__(1024) void fq_batch_kernel(FqBatch fb) {
+  extern __shared__ __attribute__((aligned(16))) uint4 lds[];
+  const int64_t bid = blockIdx.x;
+  if (bid < fb.rows_wg) {
+    rows_wave<uint16_t, B, QG>(fb.rows, bid * 16 + (threadIdx.x >> 6), threadIdx.x & 63);
+  } else if (bid < fb.end_w) {
+    cols_task<B, QW>(fb.cw, bid - fb.rows_wg, lds);
+  } else if (bid < fb.end_dy) {
+    cols_task<B, QG>(fb.cdy, bid - fb.end_w, lds);
+  } else {
+    cols_task<B, QW>(fb.cx, bid - fb.end_dy, lds);
   }
 }
 
@@ -549,58 +598,64 @@ static void cols2_scratch(void* ws, int64_t strips, float** colmax, uint32_t** a
   *words = (int64_t)(cnt / 4);
 }
 
-template <int B, int QT>
-static hipError_t launch_cols2_t(const FqArgs& a0, void* ws0, const FqArgs* a1, void* ws1,
-                                 int prezeroed, hipStream_t st) {
-  const int64_t rows = a0.len;
-  const int R = cols2_rows_per_task(rows, a0.block);
-  const int P = (int)(rows / R), C = 65536 / R;
-  const void* fn = reinterpret_cast<const void*>(&fq_cols2_kernel<B, QT>);
+// Geometry and scratch of one column pass (rows = a.len); tasks = 0 for an empty pass.
+static ColsProb cols2_prob(const FqArgs& a, void* ws, int64_t* tasks, int64_t* scratch_words) {
+  ColsProb pr{};
+  pr.a = a;
+  pr.R = cols2_rows_per_task(a.len, a.block);
+  pr.P = (int)(a.len / pr.R);
+  pr.C = 65536 / pr.R;
+  const int64_t strips = (a.nvec + pr.C - 1) / pr.C;
+  *tasks = (a.nvec == 0 || a.len == 0) ? 0 : strips * pr.P;
+  *scratch_words = 0;
+  if (pr.P > 1 && *tasks > 0) {
+    cols2_scratch(ws, strips, &pr.colmax, &pr.arrive, scratch_words);
+    *scratch_words += a.nvec;
+  }
+  return pr;
+}
+
+template <typename K>
+static hipError_t set_cols_lds(K* fn) {
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
   std::call_once(once, [fn] {
-    attr_err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kColsLdsBytes);
+    attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, kColsLdsBytes);
   });
-  if (attr_err != hipSuccess) return attr_err;
-  Cols2Pair cp{};
-  cp.R = R;
-  cp.P = P;
-  cp.C = C;
-  const FqArgs* probs[2] = {&a0, a1};
-  void* wss[2] = {ws0, ws1};
-  Cols2Prob* dst[2] = {&cp.p0, &cp.p1};
-  int64_t tasks[2] = {0, 0};
-  for (int i = 0; i < 2; ++i) {
-    if (!probs[i] || probs[i]->nvec == 0 || rows == 0) continue;
-    const int64_t strips = (probs[i]->nvec + C - 1) / C;
-    tasks[i] = strips * P;
-    dst[i]->a = *probs[i];
-    if (P > 1) {
-      int64_t words = 0;
-      cols2_scratch(wss[i], strips, &dst[i]->colmax, &dst[i]->arrive, &words);
-      if (!prezeroed) {
-        const hipError_t e = launch_fill_zero(reinterpret_cast<float*>(wss[i]),
-                                              words + probs[i]->nvec, st);
-        if (e != hipSuccess) return e;
-      }
-    }
+  return attr_err;
+}
+
+template <int B, int QT>
+static hipError_t launch_cols2_t(const FqArgs& a0, void* ws0, const FqArgs* a1, void* ws1,
+                                 int prezeroed, hipStream_t st) {
+  auto* fn = &fq_cols2_kernel<B, QT>;
+  hipError_t e = set_cols_lds(fn);
+  if (e != hipSuccess) return e;
+  int64_t t0 = 0, t1 = 0, w0 = 0, w1 = 0;
+  ColsProb p0 = cols2_prob(a0, ws0, &t0, &w0);
+  ColsProb p1 = a1 ? cols2_prob(*a1, ws1, &t1, &w1) : p0;
+  if (!prezeroed) {
+    if (w0 > 0 && (e = launch_fill_zero(reinterpret_cast<float*>(ws0), w0, st)) != hipSuccess) return e;
+    if (w1 > 0 && (e = launch_fill_zero(reinterpret_cast<float*>(ws1), w1, st)) != hipSuccess) return e;
   }
-  if (tasks[0] == 0) {  // keep the first slot filled: the kernel picks by task index
-    cp.p0 = cp.p1;
-    tasks[0] = tasks[1];
-    tasks[1] = 0;
+  if (t0 == 0) {  // keep the first slot filled: the kernel picks by task index
+    p0 = p1;
+    t0 = t1;
+    t1 = 0;
   }
-  cp.split = tasks[0];
-  cp.tasks = tasks[0] + tasks[1];
-  if (cp.tasks == 0) return hipSuccess;
+  const int64_t tasks = t0 + t1;
+  if (tasks == 0) return hipSuccess;
   // one task per workgroup; the P tasks of a strip are consecutive workgroups.  A waiting
   // workgroup only waits for the other members of its own group, and the hardware dispatches
   // workgroups in index order on each XCD: every group below the lowest undispatched
   // workgroup is fully dispatched and finishes, freeing room for the rest, so every wait ends
   // as long as one group fits on the device at once.
-  if (P > 1 && cols2_capacity(fn) < P) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fq_cols2_kernel<B, QT>), dim3((unsigned)cp.tasks), dim3(1024), kColsLdsBytes,
-                     st, cp);
+  const int P = p0.P > p1.P ? p0.P : p1.P;
+  if (P > 1 && cols2_capacity(reinterpret_cast<const void*>(fn)) < P)
+    return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((fq_cols2_kernel<B, QT>), dim3((unsigned)tasks), dim3(1024), kColsLdsBytes,
+                     st, p0, p1, t0, tasks);
   return hipGetLastError();
 }
 
@@ -626,6 +681,67 @@ hipError_t launch_fq_cols2_pair(const FqArgs& a0, void* ws0, const FqArgs* a1, v
     case 2: return cols2_block<2>(a0, ws0, a1, ws1, prezeroed, st);
     case 3: return cols2_block<3>(a0, ws0, a1, ws1, prezeroed, st);
   }
+  return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
+// backward batch
+// ---------------------------------------------------------------------------
+
+bool fq_batch_rows_ok(int64_t len) { return len >= 64 && len <= 4096 && 4096 % len == 0; }
+
+template <int B, int QG, int QW>
+static hipError_t launch_batch_t(const FqArgs* rows, const FqArgs& cw, void* ws_w,
+                                 const FqArgs& cdy, void* ws_dy, const FqArgs& cx, void* ws_x,
+                                 hipStream_t st) {
+  auto* fn = &fq_batch_kernel<B, QG, QW>;
+  hipError_t e = set_cols_lds(fn);
+  if (e != hipSuccess) return e;
+  FqBatch fb{};
+  int64_t tw = 0, tdy = 0, tx = 0, scratch = 0;
+  if (rows) {
+    fb.rows = *rows;
+    const int64_t waves = (rows->nvec * rows->len + 4095) / 4096;
+    fb.rows_wg = rows->nvec == 0 ? 0 : (waves + 15) / 16;
+  }
+  fb.cw = cols2_prob(cw, ws_w, &tw, &scratch);
+  fb.cdy = cols2_prob(cdy, ws_dy, &tdy, &scratch);
+  fb.cx = cols2_prob(cx, ws_x, &tx, &scratch);
+  fb.end_w = fb.rows_wg + tw;
+  fb.end_dy = fb.end_w + tdy;
+  fb.end_x = fb.end_dy + tx;
+  if (fb.end_x == 0) return hipSuccess;
+  int P = fb.cw.P;
+  if (fb.cdy.P > P) P = fb.cdy.P;
+  if (fb.cx.P > P) P = fb.cx.P;
+  if (P > 1 && cols2_capacity(reinterpret_cast<const void*>(fn)) < P)
+    return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((fq_batch_kernel<B, QG, QW>), dim3((unsigned)fb.end_x), dim3(1024),
+                     kColsLdsBytes, st, fb);
+  return hipGetLastError();
+}
+
+template <int QG, int QW>
+static hipError_t batch_block(int block, const FqArgs* rows, const FqArgs& cw, void* ws_w,
+                              const FqArgs& cdy, void* ws_dy, const FqArgs& cx, void* ws_x,
+                              hipStream_t st) {
+#define HALO_B_CASE(BB) \
+  case BB: return launch_batch_t<BB, QG, QW>(rows, cw, ws_w, cdy, ws_dy, cx, ws_x, st);
+  switch (block) {
+    HALO_B_CASE(1) HALO_B_CASE(2) HALO_B_CASE(4) HALO_B_CASE(8) HALO_B_CASE(16)
+    HALO_B_CASE(32) HALO_B_CASE(64) HALO_B_CASE(128) HALO_B_CASE(256) HALO_B_CASE(512)
+    HALO_B_CASE(1024) HALO_B_CASE(2048) HALO_B_CASE(4096)
+    default: return hipErrorInvalidValue;
+  }
+#undef HALO_B_CASE
+}
+
+hipError_t launch_fq_batch(const FqArgs* rows, const FqArgs& cw, void* ws_w, const FqArgs& cdy,
+                           void* ws_dy, const FqArgs& cx, void* ws_x, int qg, int qw,
+                           hipStream_t st) {
+  if (qg == 0 && qw == 0) return batch_block<0, 0>(cw.block, rows, cw, ws_w, cdy, ws_dy, cx, ws_x, st);
+  if (qg == 2 && qw == 1) return batch_block<2, 1>(cw.block, rows, cw, ws_w, cdy, ws_dy, cx, ws_x, st);
+  if (qg == 1 && qw == 1) return batch_block<1, 1>(cw.block, rows, cw, ws_w, cdy, ws_dy, cx, ws_x, st);
   return hipErrorInvalidValue;
 }
 

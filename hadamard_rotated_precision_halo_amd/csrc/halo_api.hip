@@ -353,6 +353,50 @@ halo_status halo_linear_bwd(const void* dy, const void* x, const void* w, halo_d
                  0, st);
     }
   };
+  const int qg = qt_index(grad_q_type), qw = qt_index(q_type);
+  const bool pair_ok = (qg == 0 && qw == 0) || (qg == 2 && qw == 1) || (qg == 1 && qw == 1);
+  if (dx && dw && inb && pair_ok && fq_cols2_supported(n, k, block, 1, p.scr_w) &&
+      fq_cols2_supported(m, n, block, 1, p.scr_dy) && fq_cols2_supported(m, k, block, 1, p.scr_x)) {
+    // every rotation pass of the backward in one launch (or two, when the dY rows are long):
+    // the passes overlap on the device, then the two products
+    void* qdy = base + p.off[0];
+    float* sdy = reinterpret_cast<float*>(base + p.off[1]);
+    void* qwt = base + p.off[2];
+    float* swt = reinterpret_cast<float*>(base + p.off[3]);
+    void* qdyt = base + p.off[4];
+    float* sdyt = reinterpret_cast<float*>(base + p.off[5]);
+    void* qxt = base + p.off[6];
+    float* sxt = reinterpret_cast<float*>(base + p.off[7]);
+    const FqArgs rows = make_fq(dy, m, n, n, HALO_ALONG_ROWS, block, grad_q_type, qdy, n, sdy);
+    const FqArgs cw = make_fq(w, n, k, k, HALO_ALONG_COLS, block, q_type, qwt, n, swt);
+    const FqArgs cdy = make_fq(dy, m, n, n, HALO_ALONG_COLS, block, grad_q_type, qdyt, m, sdyt);
+    const FqArgs cx = make_fq(x, m, k, k, HALO_ALONG_COLS, block, q_type, qxt, m, sxt);
+    const bool rows_in = fq_batch_rows_ok(n);
+    if (rows_in) {
+      clear_scratch();
+    } else if (fq_rows2_supported(n, block)) {
+      FqPair pp{};
+      pp.p0 = rows;
+      if (zero_pending) {
+        pp.zero = reinterpret_cast<uint32_t*>(scr);
+        pp.nzero = (int64_t)(p.scratch_bytes / 4);
+        zero_pending = false;
+      }
+      s = from_hip(launch_fq_rows2_pair(pp, inb, qg, st));
+    } else {
+      s = run_fq(dy, io_type, m, n, n, HALO_ALONG_ROWS, block, grad_q_type, qdy, n, sdy, nullptr,
+                 0, st);
+      clear_scratch();
+    }
+    if (s == HALO_OK)
+      s = from_hip(launch_fq_batch(rows_in ? &rows : nullptr, cw, scr_w, cdy, scr_dy, cx, scr_x,
+                                   qg, qw, st));
+    if (s == HALO_OK)
+      s = gemm_any(qdy, grad_q_type, n, sdy, qwt, q_type, n, swt, m, k, n, dx, io_type, k, st);
+    if (s == HALO_OK)
+      s = gemm_any(qdyt, grad_q_type, m, sdyt, qxt, q_type, m, sxt, n, k, m, dw, io_type, k, st);
+    return s;
+  }
   if (dx) {  // dX[m x k] = dY W: contraction over n
     void* qdy = base + p.off[0];
     float* sdy = reinterpret_cast<float*>(base + p.off[1]);

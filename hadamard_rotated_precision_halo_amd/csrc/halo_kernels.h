@@ -34,6 +34,15 @@ size_t fq_cols2_ws_bytes(int64_t rows, int64_t cols, int block, int in_bf16);
 bool fq_cols2_supported(int64_t rows, int64_t cols, int block, int in_bf16, size_t ws_bytes);
 hipError_t launch_fq_cols2(const FqArgs& a, int qt, void* ws, hipStream_t st);
 
+// The rotation passes of a layer backward in one launch (bf16 input): the rows of dY (codes
+// qg; may be NULL, else fq_batch_rows_ok(len) must hold) and the single-read column passes of
+// W (qw), dY (qg) and X (qw), whose scratch must be zero at launch.  Code type pairs (qg, qw):
+// (0, 0), (2, 1), (1, 1).
+bool fq_batch_rows_ok(int64_t len);
+hipError_t launch_fq_batch(const FqArgs* rows, const FqArgs& cw, void* ws_w, const FqArgs& cdy,
+                           void* ws_dy, const FqArgs& cx, void* ws_x, int qg, int qw,
+                           hipStream_t st);
+
 // Zero n floats (also used for 32-bit counters).
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 
