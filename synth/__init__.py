@@ -52,6 +52,14 @@ def grads(rng, m, n):
     return (1e-3 * rng.standard_t(4.0, size=(m, n))).astype(np.float32)
 
 
+def sign_words(length, seed):
+    """Packed random signs for the randomised transform H D: ceil(length / 32) uint32 words
+    drawn from one seed (bit i set = element i negated).  Every party that draws with the same
+    seed gets the same signs."""
+    rng = np.random.default_rng(seed)
+    return rng.integers(0, 2 ** 32, size=-(-int(length) // 32), dtype=np.uint32)
+
+
 def _cast(a, io):
     return bf16_bits(a) if io == BF16 else np.ascontiguousarray(a, dtype=np.float32)
 

@@ -464,6 +464,8 @@ def test_sampled_vectors_match_full():
 def test_oracle_rejects_bad_arguments():
     x = np.zeros((4, 48), dtype=np.float32)
     with pytest.raises(ValueError):
-        O.fwht_quant(x, O.ROWS, 32, O.I8)  # 48 not a multiple of 32
-    with pytest.raises(ValueError):
         O.fwht_quant(x, O.ROWS, 3, O.I8)  # not a power of two
+    with pytest.raises(ValueError):
+        O.fwht_quant(x, O.ROWS, 16, O.F64, rounding=O.STOCHASTIC)  # rounding of values
+    with pytest.raises(ValueError):
+        O.fwht_quant(x, O.ROWS, 16, O.I8, rounding=2)
