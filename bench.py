@@ -49,17 +49,23 @@ GEMM_BYTES = 2 * M * K + 2 * M * N + 4 * (M + N)  # both code operands, bf16 out
 COPY_BYTES = 64 << 20                       # calibration copy: 64 MiB read + 64 MiB written
 KERNEL_SOURCES = ["hadamard_rotated_precision_halo_amd/csrc/gemm.hip",
                   "hadamard_rotated_precision_halo_amd/csrc/fwht_quant.hip",
+                  "hadamard_rotated_precision_halo_amd/csrc/fwht_wave.h",
                   "hadamard_rotated_precision_halo_amd/csrc/fwht_wave.hip",
+                  "hadamard_rotated_precision_halo_amd/csrc/fwht_wave_sr.hip",
                   "hadamard_rotated_precision_halo_amd/csrc/halo_device.h"]
+K_PAD = 4000                                # rows of 4000 elements, padded to 4096 codes
+FQ_PAD_BYTES = M * K_PAD * 2 + M * K + 4 * M
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic_4096.json")
 
 # kernel-name patterns of each measured pass (rocprofv3 Kernel_Name substrings); a pass may
 # launch several kernels per call
 PASSES = {
     "gemm_i8_4096": ["halo::gemm_kernel<0"],
-    "fq_rows_4096": ["halo::fq_rows2_kernel<unsigned short, 256, 0>"],
+    "fq_rows_4096": ["halo::fq_rows2_kernel<unsigned short, 256, 0, false>"],
     "fq_cols_4096": ["halo::fq_cols_kernel<unsigned short, 256, 0", "halo::fill_zero_kernel",
-                     "halo::finalize_scale_kernel", "halo::fq_cols2_kernel<256, 0>"],
+                     "halo::finalize_scale_kernel", "halo::fq_cols2_kernel<256, 0, false>"],
+    "fq_rows_opt_4096": ["halo::fq_rows2_kernel<unsigned short, 256, 0, true>"],
+    "fq_cols_opt_4096": ["halo::fq_cols2_kernel<256, 0, true>"],
     "copy_64MiB": ["__amd_rocclr_copyBuffer"],
 }
 
@@ -146,9 +152,14 @@ def make_inputs(torch):
     return sets
 
 
+SEED64 = 0x0123456789ABCDEF  # Philox key of the stochastic-rounding legs
+
+
 def measure_kernels(H, torch, sets, iters, with_copy=False):
     """Per-launch time (ms) of the dominant kernels, in the configuration the step launches
-    them: INT8 GEMM 4096^3 -> bf16, rows pass of X, columns pass of dY (block 256)."""
+    them: INT8 GEMM 4096^3 -> bf16, rows pass of X, columns pass of dY (block 256); and the
+    option legs: the rows and columns passes of dY with the randomised transform's signs and
+    stochastic rounding, and a rows pass over rows of 4000 elements zero-padded to 4096."""
     codes = [H.fwht_quant(X, axis=H.ROWS, block=BLOCK) for (X, _, _) in sets[:2]]
     wcodes = [H.fwht_quant(W, axis=H.ROWS, block=BLOCK) for (_, W, _) in sets[:2]]
     y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
@@ -167,12 +178,30 @@ def measure_kernels(H, torch, sets, iters, with_copy=False):
         H.fwht_quant(sets[i % N_SETS][2], axis=H.COLS, block=BLOCK, q=qbuf, scale=sbuf[:N],
                      workspace=wsc)
 
-    for f in (gemm, rows, cols):
+    signs = H.hadamard_signs(K, seed=2024, device="cuda:0")
+
+    def rows_opt(i):
+        H.fwht_quant(sets[i % N_SETS][2], axis=H.ROWS, block=BLOCK, q=qbuf, scale=sbuf[:M],
+                     signs=signs, rounding="stochastic", seed=SEED64, counter=i)
+
+    def cols_opt(i):
+        H.fwht_quant(sets[i % N_SETS][2], axis=H.COLS, block=BLOCK, q=qbuf, scale=sbuf[:N],
+                     workspace=wsc, signs=signs, rounding="stochastic", seed=SEED64, counter=i)
+
+    padded = [X[:, :K_PAD].contiguous() for (X, _, _) in sets]
+
+    def rows_pad(i):
+        H.fwht_quant(padded[i % N_SETS], axis=H.ROWS, block=BLOCK, q=qbuf, scale=sbuf[:M])
+
+    for f in (gemm, rows, cols, rows_opt, cols_opt, rows_pad):
         for i in range(3):
             f(i)
     out = {"gemm_i8_4096": time_events(gemm, iters, torch),
            "fq_rows_4096": time_events(rows, iters, torch),
-           "fq_cols_4096": time_events(cols, iters, torch)}
+           "fq_cols_4096": time_events(cols, iters, torch),
+           "fq_rows_opt_4096": time_events(rows_opt, iters, torch),
+           "fq_cols_opt_4096": time_events(cols_opt, iters, torch),
+           "fq_rows_pad_4000": time_events(rows_pad, iters, torch)}
     if with_copy:
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0").normal_()
         dst = torch.empty_like(src)
@@ -336,6 +365,22 @@ def main():
     value = STEP_GOP / (ms_step * 1e-3) / 1e3  # TOP/s
     per_step = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
 
+    # ---- the same step with the options: randomised transform on every contraction dim,
+    # stochastic rounding of the dY codes (a fresh counter per step) ----
+    sk = H.hadamard_signs(K, seed=11, device="cuda:0")
+    sn = H.hadamard_signs(N, seed=12, device="cuda:0")
+    sm = H.hadamard_signs(M, seed=13, device="cuda:0")
+
+    def step_opt(i):
+        X, W, DY = sets[i % N_SETS]
+        H.linear_fwd(X, W, BLOCK, y=y, workspace=ws_f, signs_k=sk)
+        H.linear_bwd(DY, X, W, BLOCK, dx=dx, dw=dw, workspace=ws_b, signs_n=sn, signs_m=sm,
+                     grad_rounding="stochastic", seed=SEED64, counter=i)
+
+    for i in range(3):
+        step_opt(i)
+    ms_opt = time_events(step_opt, args.steps, torch)
+
     # ---- per-kernel measurements (same kernels, same shapes, HIP events on the stream) ----
     t = measure_kernels(H, torch, sets, args.kernel_iters)
     t_gemm, t_rows, t_cols = t["gemm_i8_4096"], t["fq_rows_4096"], t["fq_cols_4096"]
@@ -343,10 +388,13 @@ def main():
     rows_gbs = FQ_BYTES / (t_rows * 1e-3) / 1e9
     cols_gbs = FQ_BYTES / (t_cols * 1e-3) / 1e9
 
-    def hbm(gbs, ms, key):
+    def hbm(gbs, ms, key, nbytes=FQ_BYTES):
         return {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": load_traffic(key),
-                "ms_per_launch": round(ms, 5), "algorithmic_bytes": FQ_BYTES}
+                "ms_per_launch": round(ms, 5), "algorithmic_bytes": nbytes}
+
+    def hbm_pass(key, nbytes=FQ_BYTES):
+        return hbm(nbytes / (t[key] * 1e-3) / 1e9, t[key], key, nbytes)
 
     result = {
         "metric": METRIC,
@@ -375,6 +423,15 @@ def main():
                      "ms_per_launch": round(t_gemm, 5), "algorithmic_ops": GEMM_OPS},
         "fwht_quant": {"rows": hbm(rows_gbs, t_rows, "fq_rows_4096"),
                        "cols": hbm(cols_gbs, t_cols, "fq_cols_4096")},
+        "options": {
+            "step": {"ms": round(ms_opt, 4),
+                     "effective_tops": round(STEP_GOP / (ms_opt * 1e-3) / 1e3, 3),
+                     "what": "the same fwd+bwd step with the randomised transform H D along "
+                             "K, N and M and stochastic rounding of the dY codes"},
+            "rows_signs_sr": hbm_pass("fq_rows_opt_4096"),
+            "cols_signs_sr": hbm_pass("fq_cols_opt_4096"),
+            "rows_padded_4000_to_4096": hbm_pass("fq_rows_pad_4000", FQ_PAD_BYTES),
+        },
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline()

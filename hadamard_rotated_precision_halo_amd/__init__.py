@@ -8,7 +8,9 @@ without it raises immediately -- there is no fallback path.
 Method: "HALO: Hadamard-Assisted Lower-Precision Optimization for LLMs" (abstract: rotations
 in the forward and backward pass, all large products in 8 bits; key design 2: INT8 or FP8),
 with the orthonormal Walsh-Hadamard transform and absmax quantiser of
-"QWHA方法：基于Walsh-Hadamard变换的高效大模型微调技术" s2.1-s2.2, applied blockwise (s3.1).
+"QWHA方法：基于Walsh-Hadamard变换的高效大模型微调技术" s2.1-s2.2, applied blockwise (s3.1), with
+the zero padding and stochastic rounding of its s5, and the seeded randomised transform H D of
+"企业官网建设流程全解析" s4.2.
 """
 import ctypes
 import os
@@ -20,11 +22,28 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhalo.so"
 # halo_dtype / halo_axis / halo_status values of include/halo.h
 F32, BF16, I8, E4M3, E5M2, I32 = range(6)
 ROWS, COLS = 0, 1
+NEAREST, STOCHASTIC = 0, 1  # halo_rounding
 STATUS = {0: "HALO_OK", 1: "HALO_ERR_NULL", 2: "HALO_ERR_SHAPE", 3: "HALO_ERR_BLOCK",
-          4: "HALO_ERR_DTYPE", 5: "HALO_ERR_ALIGN", 6: "HALO_ERR_WORKSPACE", 7: "HALO_ERR_HIP"}
+          4: "HALO_ERR_DTYPE", 5: "HALO_ERR_ALIGN", 6: "HALO_ERR_WORKSPACE", 7: "HALO_ERR_HIP",
+          8: "HALO_ERR_OPTION"}
 
-EXPORTS = ("halo_fwht_quant", "halo_fwht_quant_workspace_bytes", "halo_gemm_i8", "halo_gemm_fp8",
-           "halo_linear_workspace_bytes", "halo_linear_fwd", "halo_linear_bwd", "halo_status_str")
+EXPORTS = ("halo_fwht_quant", "halo_fwht_quant_ex", "halo_fwht_quant_workspace_bytes",
+           "halo_gemm_i8", "halo_gemm_fp8", "halo_linear_workspace_bytes",
+           "halo_linear_workspace_bytes_ex", "halo_linear_fwd", "halo_linear_fwd_ex",
+           "halo_linear_bwd", "halo_linear_bwd_ex", "halo_status_str")
+
+
+class QuantOpts(ctypes.Structure):
+    """halo_quant_opts of include/halo.h."""
+    _fields_ = [("signs", ctypes.c_void_p), ("rounding", ctypes.c_int32),
+                ("seed", ctypes.c_uint32 * 2), ("counter", ctypes.c_uint32 * 2)]
+
+
+class LinearOpts(ctypes.Structure):
+    """halo_linear_opts of include/halo.h."""
+    _fields_ = [("signs_k", ctypes.c_void_p), ("signs_n", ctypes.c_void_p),
+                ("signs_m", ctypes.c_void_p), ("grad_rounding", ctypes.c_int32),
+                ("seed", ctypes.c_uint32 * 2), ("counter", ctypes.c_uint32 * 2)]
 
 _TORCH_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.int8: I8,
                torch.float8_e4m3fn: E4M3, torch.float8_e5m2: E5M2, torch.int32: I32}
@@ -58,10 +77,19 @@ def lib():
         L.halo_linear_workspace_bytes.restype = sz
         L.halo_linear_fwd.argtypes = [vp, vp, e, i64, i64, i64, i32, e, vp, e, vp, sz, vp]
         L.halo_linear_bwd.argtypes = [vp, vp, vp, e, i64, i64, i64, i32, e, e, vp, vp, vp, sz, vp]
+        qo, lo = ctypes.POINTER(QuantOpts), ctypes.POINTER(LinearOpts)
+        L.halo_fwht_quant_ex.argtypes = [vp, e, i64, i64, i64, e, i32, e, vp, i64, vp, qo, vp, sz,
+                                         vp]
+        L.halo_linear_workspace_bytes_ex.argtypes = [i64, i64, i64, i32, e, ctypes.c_int]
+        L.halo_linear_workspace_bytes_ex.restype = sz
+        L.halo_linear_fwd_ex.argtypes = [vp, vp, e, i64, i64, i64, i32, e, vp, e, lo, vp, sz, vp]
+        L.halo_linear_bwd_ex.argtypes = [vp, vp, vp, e, i64, i64, i64, i32, e, e, vp, vp, lo, vp,
+                                         sz, vp]
         L.halo_status_str.argtypes = [e]
         L.halo_status_str.restype = ctypes.c_char_p
-        for f in ("halo_fwht_quant", "halo_gemm_i8", "halo_gemm_fp8", "halo_linear_fwd",
-                  "halo_linear_bwd"):
+        for f in ("halo_fwht_quant", "halo_fwht_quant_ex", "halo_gemm_i8", "halo_gemm_fp8",
+                  "halo_linear_fwd", "halo_linear_fwd_ex", "halo_linear_bwd",
+                  "halo_linear_bwd_ex"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -104,25 +132,62 @@ def _ld(t):
     return t.stride(0)
 
 
+def padded_len(length, block):
+    """Rotated length of a vector of `length` elements: rounded up to a multiple of block
+    (the zero padding)."""
+    return -(-int(length) // int(block)) * int(block)
+
+
+def hadamard_signs(length, seed, device=None):
+    """Packed random signs of the randomised transform H D for vectors of `length` elements:
+    ceil(length / 32) 32-bit words (bit i set = element i negated), drawn on the host from
+    `seed`, so every process that uses the same seed gets the same transform.  Returned as an
+    int32 tensor (the words' bit patterns) on `device`."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    words = torch.randint(-(2 ** 31), 2 ** 31, (-(-int(length) // 32),), dtype=torch.int32,
+                          generator=g)
+    return words.to(device) if device is not None else words
+
+
+def _u32x2(v):
+    v = int(v)
+    return (ctypes.c_uint32 * 2)(v & 0xFFFFFFFF, (v >> 32) & 0xFFFFFFFF)
+
+
+_ROUNDING = {"nearest": NEAREST, "stochastic": STOCHASTIC, NEAREST: NEAREST,
+             STOCHASTIC: STOCHASTIC}
+
+
+def _rounding(r):
+    try:
+        return _ROUNDING[r]
+    except KeyError:
+        raise ValueError(f"rounding must be 'nearest' or 'stochastic', not {r!r}") from None
+
+
 def fwht_quant_workspace_bytes(rows, cols, axis, block, x_dtype=torch.bfloat16):
     return int(lib().halo_fwht_quant_workspace_bytes(rows, cols, axis, int(block),
                                                      _code(x_dtype)))
 
 
 def fwht_quant(x, axis=ROWS, block=256, q_dtype=torch.int8, q=None, scale=None, workspace=None,
-               stream=None):
+               stream=None, signs=None, rounding="nearest", seed=0, counter=0):
     """Rotate + quantise the rows (axis ROWS) or columns (axis COLS) of x.
 
-    Returns (q, scale): q is [rows x cols] (ROWS) or [cols x rows] (COLS) of q_dtype
+    Returns (q, scale): q is [rows x Lp] (ROWS) or [cols x Lp] (COLS) of q_dtype
     (torch.int8 / float8_e4m3fn / float8_e5m2, or torch.float32 for the rotated values
-    themselves), scale is float32 with one entry per vector.  `workspace` is the optional
-    scratch of the single-read columns pass: a uint8 device tensor, allocated here when None
-    and the shape can use one; pass False to run without it.
+    themselves), Lp the vector length padded with zeros to a multiple of block; scale is
+    float32 with one entry per vector.  `workspace` is the optional scratch of the single-read
+    columns pass: a uint8 device tensor, allocated here when None and the shape can use one;
+    pass False to run without it.  `signs`: the randomised transform's packed sign words (an
+    int32 device tensor, see hadamard_signs) or None.  `rounding`: "nearest" or "stochastic"
+    (Philox key `seed`, counter words 2-3 `counter`, each a 64-bit integer).
     """
     rows, cols = x.shape
     nvec, L = (rows, cols) if axis == ROWS else (cols, rows)
     if q is None:
-        q = torch.empty((nvec, L), dtype=q_dtype, device=x.device)
+        q = torch.empty((nvec, padded_len(L, block)), dtype=q_dtype, device=x.device)
     if scale is None:
         scale = torch.empty(nvec, dtype=torch.float32, device=x.device)
     if workspace is False:
@@ -135,10 +200,15 @@ def fwht_quant(x, axis=ROWS, block=256, q_dtype=torch.int8, q=None, scale=None, 
             ws_ptr, ws_bytes = None, 0
         else:
             ws_ptr, ws_bytes = _ptr(workspace), workspace.numel()
-    st = lib().halo_fwht_quant(_ptr(x), _code(x.dtype), rows, cols, _ld(x), axis, int(block),
-                               _code(q.dtype), _ptr(q), _ld(q), _ptr(scale), ws_ptr, ws_bytes,
-                               _stream(stream))
-    _check(st, "halo_fwht_quant")
+    opts = None
+    rnd = _rounding(rounding)
+    if signs is not None or rnd != NEAREST:
+        opts = QuantOpts(_ptr(signs), rnd, _u32x2(seed), _u32x2(counter))
+    st = lib().halo_fwht_quant_ex(_ptr(x), _code(x.dtype), rows, cols, _ld(x), axis, int(block),
+                                  _code(q.dtype), _ptr(q), _ld(q), _ptr(scale),
+                                  ctypes.byref(opts) if opts is not None else None, ws_ptr,
+                                  ws_bytes, _stream(stream))
+    _check(st, "halo_fwht_quant_ex")
     return q, scale
 
 
@@ -167,8 +237,13 @@ def gemm_fp8(a, sa, b, sb, out_dtype=torch.bfloat16, c=None, stream=None):
     return c
 
 
-def linear_workspace_bytes(m, n, k, q_dtype=torch.int8, backward=False):
-    return int(lib().halo_linear_workspace_bytes(m, n, k, _code(q_dtype), 1 if backward else 0))
+def linear_workspace_bytes(m, n, k, q_dtype=torch.int8, backward=False, block=None):
+    """Workspace bytes of the layer calls: for one block size, or for every block (None)."""
+    if block is None:
+        return int(lib().halo_linear_workspace_bytes(m, n, k, _code(q_dtype),
+                                                     1 if backward else 0))
+    return int(lib().halo_linear_workspace_bytes_ex(m, n, k, int(block), _code(q_dtype),
+                                                    1 if backward else 0))
 
 
 def _workspace(nbytes, device, ws):
@@ -178,24 +253,32 @@ def _workspace(nbytes, device, ws):
 
 
 def linear_fwd(x, w, block, q_dtype=torch.int8, y=None, y_dtype=None, workspace=None,
-               stream=None):
-    """Y = X W^T with both operands rotated and quantised along K (the layer's forward)."""
+               stream=None, signs_k=None):
+    """Y = X W^T with both operands rotated and quantised along K (the layer's forward);
+    signs_k: the randomised transform's sign words along K (see hadamard_signs) or None."""
     m, k = x.shape
     n = w.shape[0]
     if y is None:
         y = torch.empty((m, n), dtype=y_dtype or x.dtype, device=x.device)
-    need = linear_workspace_bytes(m, n, k, q_dtype, False)
+    need = linear_workspace_bytes(m, n, k, q_dtype, False, block)
     ws = _workspace(need, x.device, workspace)
-    st = lib().halo_linear_fwd(_ptr(x), _ptr(w), _code(x.dtype), m, n, k, int(block),
-                               _code(q_dtype), _ptr(y), _code(y.dtype), _ptr(ws),
-                               ws.numel() * ws.element_size(), _stream(stream))
-    _check(st, "halo_linear_fwd")
+    opts = LinearOpts(_ptr(signs_k), None, None, NEAREST) if signs_k is not None else None
+    st = lib().halo_linear_fwd_ex(_ptr(x), _ptr(w), _code(x.dtype), m, n, k, int(block),
+                                  _code(q_dtype), _ptr(y), _code(y.dtype),
+                                  ctypes.byref(opts) if opts is not None else None, _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "halo_linear_fwd_ex")
     return y
 
 
 def linear_bwd(dy, x, w, block, q_dtype=torch.int8, grad_q_dtype=None, want_dx=True,
-               want_dw=True, dx=None, dw=None, workspace=None, stream=None):
-    """dX = dY W (rotated along N) and dW = dY^T X (rotated along M), 8-bit products."""
+               want_dw=True, dx=None, dw=None, workspace=None, stream=None, signs_n=None,
+               signs_m=None, grad_rounding="nearest", seed=0, counter=0):
+    """dX = dY W (rotated along N) and dW = dY^T X (rotated along M), 8-bit products.
+
+    signs_n / signs_m: the randomised transform's sign words along N / M (or None).
+    grad_rounding: "nearest" or "stochastic" rounding of the dY codes (Philox key `seed`,
+    counter words 2-3 `counter`; the columns of dY draw with counter word 3 ^ 2^31)."""
     m, k = x.shape
     n = w.shape[0]
     grad_q_dtype = grad_q_dtype or q_dtype
@@ -203,11 +286,17 @@ def linear_bwd(dy, x, w, block, q_dtype=torch.int8, grad_q_dtype=None, want_dx=T
         dx = torch.empty((m, k), dtype=x.dtype, device=x.device)
     if want_dw and dw is None:
         dw = torch.empty((n, k), dtype=x.dtype, device=x.device)
-    need = linear_workspace_bytes(m, n, k, q_dtype, True)
+    need = linear_workspace_bytes(m, n, k, q_dtype, True, block)
     ws = _workspace(need, x.device, workspace)
-    st = lib().halo_linear_bwd(_ptr(dy), _ptr(x), _ptr(w), _code(x.dtype), m, n, k, int(block),
-                               _code(q_dtype), _code(grad_q_dtype),
-                               _ptr(dx) if want_dx else None, _ptr(dw) if want_dw else None,
-                               _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
-    _check(st, "halo_linear_bwd")
+    rnd = _rounding(grad_rounding)
+    opts = None
+    if signs_n is not None or signs_m is not None or rnd != NEAREST:
+        opts = LinearOpts(None, _ptr(signs_n), _ptr(signs_m), rnd, _u32x2(seed),
+                          _u32x2(counter))
+    st = lib().halo_linear_bwd_ex(_ptr(dy), _ptr(x), _ptr(w), _code(x.dtype), m, n, k,
+                                  int(block), _code(q_dtype), _code(grad_q_dtype),
+                                  _ptr(dx) if want_dx else None, _ptr(dw) if want_dw else None,
+                                  ctypes.byref(opts) if opts is not None else None, _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "halo_linear_bwd_ex")
     return (dx if want_dx else None), (dw if want_dw else None)

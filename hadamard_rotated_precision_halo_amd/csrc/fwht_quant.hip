@@ -24,6 +24,9 @@
 // sweep reduces the column maxima into the scale array with integer atomics (non-negative
 // floats order like their bit patterns), the second recomputes the rotation and writes the
 // transposed codes; a last tiny launch turns maxima into scales.
+//
+// Both kernels also take the options of a pass: the randomised transform's sign bits, zero
+// padding past in_len, and stochastic rounding of the codes (store_chunk_opt).
 #include "halo_device.h"
 #include "halo_kernels.h"
 
@@ -159,6 +162,25 @@ __device__ __forceinline__ void store_chunk(void* dst, const float* y, float m) 
 template <int QT>
 struct CodeSize { static constexpr int value = QT == 3 ? 4 : 1; };
 
+// Store one chunk, with stochastic rounding when the pass asks for it (code types only):
+// element pos + e of vector vec rounds by its own Philox uniform.
+template <int QT>
+__device__ __forceinline__ void store_chunk_opt(void* dst, const float* y, float m, const FqArgs& a,
+                                                int64_t vec, int64_t pos) {
+  if constexpr (QT != 3) {
+    if (a.sr) {
+      uint32_t w[8];
+      sr_words8(vec, pos, a.key0, a.key1, a.ctr2, a.ctr3, w);
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = sr_value<QT>(mulz(y[e], m), w[e], a.qmax);
+      store_chunk<QT>(dst, v, 1.f);
+      return;
+    }
+  }
+  store_chunk<QT>(dst, y, m);
+}
+
 // ---------------------------------------------------------------------------
 // rows kernel
 // ---------------------------------------------------------------------------
@@ -186,9 +208,11 @@ __global__ __launch_bounds__(256) void fq_rows_kernel(FqArgs a) {
     const int item = grp + it * NG;
     if (item < nitems) {
       const int vec = item / items_per_vec, blk = item % items_per_vec;
-      const Tin* p = xin + (v0 + vec) * a.ldx + (int64_t)blk * E + x * 8;
+      const Tin* vp = xin + (v0 + vec) * a.ldx;
+      const int64_t pos = (int64_t)blk * E + x * 8;
 #pragma unroll
-      for (int u = 0; u < U; ++u) load8<Tin>(p + u * 8 * G, &val[it][u * 8]);
+      for (int u = 0; u < U; ++u)
+        load8_vec<Tin>(vp, pos + u * 8 * G, a.in_len, a.signs, &val[it][u * 8]);
     } else {
 #pragma unroll
       for (int i = 0; i < U * 8; ++i) val[it][i] = 0.f;
@@ -233,9 +257,11 @@ __global__ __launch_bounds__(256) void fq_rows_kernel(FqArgs a) {
     if (item < nitems) {
       const int vec = item / items_per_vec, blk = item % items_per_vec;
       const float m = s_mul[vec];
-      char* p = qout + ((v0 + vec) * a.ldq + (int64_t)blk * E + x * 8) * CS;
+      const int64_t pos = (int64_t)blk * E + x * 8;
+      char* p = qout + ((v0 + vec) * a.ldq + pos) * CS;
 #pragma unroll
-      for (int u = 0; u < U; ++u) store_chunk<QT>(p + u * 8 * G * CS, &val[it][u * 8], m);
+      for (int u = 0; u < U; ++u)
+        store_chunk_opt<QT>(p + u * 8 * G * CS, &val[it][u * 8], m, a, v0 + vec, pos + u * 8 * G);
     }
   }
 }
@@ -244,11 +270,17 @@ __global__ __launch_bounds__(256) void fq_rows_kernel(FqArgs a) {
 // cols kernels
 // ---------------------------------------------------------------------------
 
-// Load the NV columns x 8 rows a lane owns for one chunk, transposed to [NV][8].
+// Load the NV columns x 8 rows a lane owns for one chunk, transposed to [NV][8]; rows from
+// `nvalid` on are the zero padding and are not read.
 template <typename Tin, int NV>
-__device__ __forceinline__ void load_cols(const Tin* p, int64_t ldx, float (*o)[8]) {
+__device__ __forceinline__ void load_cols(const Tin* p, int64_t ldx, int64_t nvalid, float (*o)[8]) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
+    if (e >= nvalid) {
+#pragma unroll
+      for (int c = 0; c < NV; ++c) o[c][e] = 0.f;
+      continue;
+    }
     const Tin* r = p + e * ldx;
     if constexpr (sizeof(Tin) == 2) {
       if constexpr (NV == 8) {
@@ -291,11 +323,14 @@ __global__ __launch_bounds__(256) void fq_cols_kernel(FqArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float t[NV][8];
-      load_cols<Tin, NV>(xin + (r0 + u * 8 * G + x * 8) * a.ldx + c0, a.ldx, t);
+      const int64_t rb = r0 + u * 8 * G + x * 8;  // first row of the chunk
+      load_cols<Tin, NV>(xin + rb * a.ldx + c0, a.ldx, a.in_len - rb, t);
 #pragma unroll
-      for (int c = 0; c < NV; ++c)
+      for (int c = 0; c < NV; ++c) {
+        if (a.signs) apply_signs8(t[c], a.signs, rb);
 #pragma unroll
         for (int e = 0; e < 8; ++e) val[c][u * 8 + e] = t[c][e];
+      }
     }
   } else {
 #pragma unroll
@@ -330,7 +365,8 @@ __global__ __launch_bounds__(256) void fq_cols_kernel(FqArgs a) {
       const float m = QT == 3 ? a.inv_sqrt_b : (amax > 0.f ? a.qmax / amax : 0.f);
       char* p = qout + ((c0 + c) * a.ldq + r0 + x * 8) * CS;
 #pragma unroll
-      for (int u = 0; u < U; ++u) store_chunk<QT>(p + u * 8 * G * CS, &val[c][u * 8], m);
+      for (int u = 0; u < U; ++u)
+        store_chunk_opt<QT>(p + u * 8 * G * CS, &val[c][u * 8], m, a, c0 + c, r0 + x * 8 + u * 8 * G);
     }
   }
 }
@@ -423,7 +459,8 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st) {
 
 hipError_t launch_fwht_quant(const FqArgs& a, int in_bf16, int qt, int axis, void* ws,
                              size_t ws_bytes, hipStream_t st) {
-  if (axis == 0 && fq_rows2_supported(a.len, a.block)) return launch_fq_rows2(a, in_bf16, qt, st);
+  if (axis == 0 && fq_rows2_supported(a.len, a.block) && (in_bf16 || !a.sr))
+    return launch_fq_rows2(a, in_bf16, qt, st);
   if (axis == 1 && fq_cols2_supported(a.len, a.nvec, a.block, in_bf16, ws_bytes))
     return launch_fq_cols2(a, qt, ws, st);
   if (in_bf16) {

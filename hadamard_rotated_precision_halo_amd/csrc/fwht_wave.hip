@@ -1,557 +1,14 @@
-// fwht_wave.hip -- rotation + quantisation with one wave per 4096-element slice, for gfx950:
-// rows (the contiguous axis) and columns (the strided axis, codes written transposed).
-//
-// What is computed is the same as in fwht_quant.hip ("QWHA方法：基于Walsh-Hadamard变换的高效
-// 大模型微调技术" s2.1-s2.2, s3.1: natural-order butterflies over blocks of B contiguous indices
-// of each vector, one absmax scale per vector): this file only changes how the work maps onto
-// the hardware.
-//
-// Wave slice.  A wave holds 4096 elements of one or more vectors, 64 per lane, as 8 chunks of
-// 8 consecutive elements.  For B >= 64, g = B / 64 lanes share a block and chunk j of lane lo
-// sits at block offset (j * g + lo) * 8, so the 3 low index bits and the 3 high index bits of
-// a block are butterflied in registers and only log2(g) stages cross lanes; for B < 64 a lane
-// holds 64 / B whole blocks.  The two lowest lane stages are single v_fmac_f32 instructions
-// with a DPP quad permutation on the partner value (z <- z + c * z[lane ^ s], c = +1 on the
-// lower and -1 on the upper lane; the upper lane then holds the negated difference, a sign
-// folded into its quantisation multiplier); higher lane stages use ds_swizzle / permlane.
-// All stages run in increasing index-bit order with the same operand order as a sequential
-// fp32 butterfly, so the values are bit-identical to it.
-//
-// Rows kernel.  A wave reads its slice straight from HBM: 4096 / L whole rows when L <= 4096
-// (no barrier), or a workgroup of ceil(L / 4096) waves per row with one LDS exchange of wave
-// maxima.
-//
-// Columns kernel.  A workgroup of 16 waves owns a tile of C = 65536 / R columns by R rows
-// (R = 1024 for long columns): each lane loads 8 consecutive rows of 8 adjacent columns with
-// full 128-byte row segments, transposes them in registers with v_perm_b32 (8 rows of one
-// column in one 16-byte word) and writes them to LDS in the order the compute waves read them
-// (bank-conflict-free by an XOR swizzle); the waves then run the slice computation on column
-// segments of R rows.  When a column is longer than R, the P = rows / R workgroups of one
-// column strip combine their partial maxima through device-scope atomics: each max-reduces
-// its maxima into the strip's column maxima, increments the strip's arrival counter, and
-// waits until all P have arrived.  The
-// P tasks of a strip are consecutive workgroups and workgroups are dispatched in index order,
-// so the wait always ends (see the launcher); a bounded spin guards it regardless.  The input
-// is read once and the codes written once.
-#include "halo_device.h"
-#include "halo_kernels.h"
-
-#include <mutex>
+// fwht_wave.hip -- launch interface of the wave-slice rotation kernels (fwht_wave.h): shape
+// support, scratch sizes, and the nearest-even instantiations.  The stochastic-rounding
+// instantiations live in fwht_wave_sr.hip, so the two halves compile in parallel.
+#include "fwht_wave.h"
 
 namespace halo {
-
-// ---------------------------------------------------------------------------
-// wave-slice helpers
-// ---------------------------------------------------------------------------
-
-// z[i] <- z[i] + c * z[i] of lane ^ (1 << S), S = 0 or 1, for 8 values: one v_fmac_f32 with a
-// DPP quad permutation of src0 each.  The leading s_nop covers the two wait states a DPP read
-// needs after a VALU write of its source; inside the block each source was written earlier.
-template <int S>
-__device__ __forceinline__ void dpp_fmac8(float* z, float c) {
-  if constexpr (S == 0) {
-    asm volatile(
-        "s_nop 1\n\t"
-        "v_fmac_f32_dpp %0, %0, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %1, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %2, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %3, %3, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %4, %4, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %5, %5, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %6, %6, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %7, %7, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
-        : "+v"(z[0]), "+v"(z[1]), "+v"(z[2]), "+v"(z[3]), "+v"(z[4]), "+v"(z[5]), "+v"(z[6]),
-          "+v"(z[7])
-        : "v"(c));
-  } else {
-    asm volatile(
-        "s_nop 1\n\t"
-        "v_fmac_f32_dpp %0, %0, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %1, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %2, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %3, %3, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %4, %4, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %5, %5, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %6, %6, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %7, %7, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
-        : "+v"(z[0]), "+v"(z[1]), "+v"(z[2]), "+v"(z[3]), "+v"(z[4]), "+v"(z[5]), "+v"(z[6]),
-          "+v"(z[7])
-        : "v"(c));
-  }
-}
-
-// Butterflies between in-register values at index distance D (the values of one lane are
-// v[j * 8 + e]; D is a power of two, the pair is (t, t + D) within groups of 2D).
-template <int D>
-__device__ __forceinline__ void reg_stage(float* v) {
-#pragma unroll
-  for (int i = 0; i < 64; i += 2 * D)
-#pragma unroll
-    for (int t = i; t < i + D; ++t) {
-      const float p = v[t], q = v[t + D];
-      v[t] = p + q;
-      v[t + D] = p - q;
-    }
-}
-
-// Lane geometry of a block of B elements inside a wave slice.
-template <int B>
-struct Slice {
-  static constexpr int G = B >= 64 ? B / 64 : 1;  // lanes per block
-  // element offset of chunk j of `lane` within the 4096-element slice
-  __device__ static __forceinline__ int off(int lane, int j) {
-    if constexpr (B >= 64) return (lane / G) * B + (j * G + lane % G) * 8;
-    else return lane * 64 + j * 8;
-  }
-  // inverse: the lane and chunk holding slice offset o (a multiple of 8)
-  __device__ static __forceinline__ void where(int o, int& lane, int& j) {
-    if constexpr (B >= 64) {
-      const int r = (o % B) / 8;
-      lane = (o / B) * G + r % G;
-      j = r / G;
-    } else {
-      lane = o / 64;
-      j = (o % 64) / 8;
-    }
-  }
-};
-
-// Rotate the 64 values of a lane in place; returns the sign the DPP stages left on them.
-template <int B>
-__device__ __forceinline__ float rotate64(float* v, int lane) {
-  constexpr int G = Slice<B>::G;
-  const int lo = lane % G;
-  if constexpr (B >= 2) reg_stage<1>(v);
-  if constexpr (B >= 4) reg_stage<2>(v);
-  if constexpr (B >= 8) reg_stage<4>(v);
-  float sgn = 1.f;
-  if constexpr (B >= 64) {
-    if constexpr (G >= 2) {
-      const float c = (lo & 1) ? -1.f : 1.f;
-#pragma unroll
-      for (int i = 0; i < 64; i += 8) dpp_fmac8<0>(&v[i], c);
-      sgn *= c;
-    }
-    if constexpr (G >= 4) {
-      const float c = (lo & 2) ? -1.f : 1.f;
-#pragma unroll
-      for (int i = 0; i < 64; i += 8) dpp_fmac8<1>(&v[i], c);
-      sgn *= c;
-    }
-    if constexpr (G >= 8) {
-      const float c = (lo & 4) ? -1.f : 1.f;
-#pragma unroll
-      for (int i = 0; i < 64; ++i) v[i] = xbutterfly<2>(v[i], c);
-    }
-    if constexpr (G >= 16) {
-      const float c = (lo & 8) ? -1.f : 1.f;
-#pragma unroll
-      for (int i = 0; i < 64; ++i) v[i] = xbutterfly<3>(v[i], c);
-    }
-    if constexpr (G >= 32) {
-      const float c = (lo & 16) ? -1.f : 1.f;
-#pragma unroll
-      for (int i = 0; i < 64; ++i) v[i] = xbutterfly<4>(v[i], c);
-    }
-    if constexpr (G >= 64) {
-      const float c = (lo & 32) ? -1.f : 1.f;
-#pragma unroll
-      for (int i = 0; i < 64; ++i) v[i] = xbutterfly<5>(v[i], c);
-    }
-    // top bits: the 8 chunks of the lane
-    reg_stage<8>(v);
-    reg_stage<16>(v);
-    reg_stage<32>(v);
-  } else {
-    // blocks of 16 or 32 elements: chunk bits inside the block
-    if constexpr (B >= 16) reg_stage<8>(v);
-    if constexpr (B >= 32) reg_stage<16>(v);
-  }
-  return sgn;
-}
-
-__device__ __forceinline__ float absmax64(const float* v) {
-  float mx = 0.f;
-#pragma unroll
-  for (int i = 0; i < 64; i += 2)
-    mx = __builtin_fmaxf(__builtin_fmaxf(mx, fabsf(v[i])), fabsf(v[i + 1]));
-  return mx;
-}
-
-// Maximum over the lanes whose low `lane_bits` lane-index bits vary (the lanes of one vector).
-__device__ __forceinline__ float lane_max(float v, int lane_bits) {
-  if (lane_bits > 0) v = xmax<0>(v);
-  if (lane_bits > 1) v = xmax<1>(v);
-  if (lane_bits > 2) v = xmax<2>(v);
-  if (lane_bits > 3) v = xmax<3>(v);
-  if (lane_bits > 4) v = xmax<4>(v);
-  if (lane_bits > 5) v = xmax<5>(v);
-  return v;
-}
-
-// Encoders for 8 consecutive values (one chunk) -> 8 bytes of codes.
-template <int QT>
-__device__ __forceinline__ uint2 encode8(const float* y, float m) {
-  uint2 w;
-  if constexpr (QT == 0) {
-    uint32_t t[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) t[e] = __float_as_uint(__builtin_fmaf(y[e], m, 12582912.0f));
-    // v_perm_b32: byte 0 of each of two dwords -> bytes 0 and 1 (selector 0x0c zeroes)
-    const uint32_t p01 = __builtin_amdgcn_perm(t[1], t[0], 0x0c0c0400u);
-    const uint32_t p23 = __builtin_amdgcn_perm(t[3], t[2], 0x0c0c0400u);
-    const uint32_t p45 = __builtin_amdgcn_perm(t[5], t[4], 0x0c0c0400u);
-    const uint32_t p67 = __builtin_amdgcn_perm(t[7], t[6], 0x0c0c0400u);
-    w.x = __builtin_amdgcn_perm(p23, p01, 0x05040100u);
-    w.y = __builtin_amdgcn_perm(p67, p45, 0x05040100u);
-  } else {
-    // v_cvt_pk_{fp8,bf8}_f32 writes one 16-bit half of its destination and keeps the other
-    if constexpr (QT == 1) {
-      w.x = __builtin_amdgcn_cvt_pk_fp8_f32(mulz(y[2], m), mulz(y[3], m),
-                                            __builtin_amdgcn_cvt_pk_fp8_f32(mulz(y[0], m), mulz(y[1], m), 0, false), true);
-      w.y = __builtin_amdgcn_cvt_pk_fp8_f32(mulz(y[6], m), mulz(y[7], m),
-                                            __builtin_amdgcn_cvt_pk_fp8_f32(mulz(y[4], m), mulz(y[5], m), 0, false), true);
-    } else {
-      w.x = __builtin_amdgcn_cvt_pk_bf8_f32(mulz(y[2], m), mulz(y[3], m),
-                                            __builtin_amdgcn_cvt_pk_bf8_f32(mulz(y[0], m), mulz(y[1], m), 0, false), true);
-      w.y = __builtin_amdgcn_cvt_pk_bf8_f32(mulz(y[6], m), mulz(y[7], m),
-                                            __builtin_amdgcn_cvt_pk_bf8_f32(mulz(y[4], m), mulz(y[5], m), 0, false), true);
-    }
-  }
-  return w;
-}
-
-// Store chunk j of the lane (8 values y) at element `idx` of the code array: 8 code bytes, or
-// 8 fp32 rotated values for the value mode (QT 3).
-template <int QT>
-__device__ __forceinline__ void store_chunk8(void* q, int64_t idx, const float* y, float mul) {
-  if constexpr (QT == 3) {
-    float4* d = reinterpret_cast<float4*>(reinterpret_cast<float*>(q) + idx);
-    d[0] = make_float4(mulz(y[0], mul), mulz(y[1], mul), mulz(y[2], mul), mulz(y[3], mul));
-    d[1] = make_float4(mulz(y[4], mul), mulz(y[5], mul), mulz(y[6], mul), mulz(y[7], mul));
-  } else {
-    *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(q) + idx) = encode8<QT>(y, mul);
-  }
-}
-
-// Quantisation multiplier and stored scale from the vector's absmax.
-template <int QT>
-__device__ __forceinline__ float quant_mul(const FqArgs& a, float mx) {
-  if constexpr (QT == 3) return a.inv_sqrt_b;
-  else return mx > 0.f ? a.qmax / mx : 0.f;
-}
-template <int QT>
-__device__ __forceinline__ float stored_scale(const FqArgs& a, float mx) {
-  return QT == 3 ? mx * a.inv_sqrt_b : mx / a.denom;
-}
-
-// ---------------------------------------------------------------------------
-// rows kernel
-// ---------------------------------------------------------------------------
-
-// One wave's slice of a rows pass with L <= 4096 and 4096 % L == 0: wave `gw` of the pass owns
-// rows [gw * 4096 / L, (gw + 1) * 4096 / L).  Lanes past the last row idle.
-template <typename Tin, int B, int QT>
-__device__ __forceinline__ void rows_wave(const FqArgs& a, int64_t gw, int lane) {
-  using S = Slice<B>;
-  const int L = (int)a.len;
-  const int64_t rpw = 4096 / L;              // rows per wave
-  const int r_in_wave = S::off(lane, 0) / L;
-  const int64_t row = gw * rpw + r_in_wave;
-  const int col0 = -r_in_wave * L;           // so that col0 + off(lane, j) is the column
-  const int row_lanes_log2 = 31 - __builtin_clz((unsigned)(L / 64));
-  const bool valid = row < a.nvec;
-  const Tin* __restrict__ xin = reinterpret_cast<const Tin*>(a.x);
-  // idle lanes read the first chunk of row 0
-  const Tin* rp = xin + (valid ? row : 0) * a.ldx;
-  float v[64];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int c = valid ? col0 + S::off(lane, j) : 0;
-    load8<Tin>(rp + c, &v[j * 8]);
-  }
-  const float sgn = rotate64<B>(v, lane);
-  float mx = valid ? absmax64(v) : 0.f;
-  mx = lane_max(mx, row_lanes_log2);
-  const bool writer = (lane & ((1 << row_lanes_log2) - 1)) == 0;
-  if (!valid) return;
-  if (writer) a.scale[row] = stored_scale<QT>(a, mx);
-  const float mul = quant_mul<QT>(a, mx) * sgn;
-  const int64_t base = row * a.ldq + col0;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) store_chunk8<QT>(a.q, base + S::off(lane, j), &v[j * 8], mul);
-}
-
-// QT: 0 INT8, 1 E4M3, 2 E5M2, 3 fp32 rotated values.
-// multi = 1: one row per workgroup, wave w owns columns [4096 w, 4096 (w + 1)).
-// multi = 0: 4096 % L == 0, each wave owns 4096 / L whole rows.
-// One launch serves up to two passes of the same geometry (workgroups below pp.split run the
-// first), and can clear a scratch range for the column passes that follow it on the stream.
-template <typename Tin, int B, int QT>
-__global__ __launch_bounds__(1024) void fq_rows2_kernel(FqPair pp, int multi) {
-  using S = Slice<B>;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  if (pp.zero) {
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < pp.nzero; i += stride)
-      pp.zero[i] = 0u;
-  }
-  const bool second = (int64_t)blockIdx.x >= pp.split;
-  const FqArgs a = second ? pp.p1 : pp.p0;
-  const int bid = (int)(blockIdx.x - (second ? pp.split : 0));
-  if (!multi) {
-    rows_wave<Tin, B, QT>(a, (int64_t)bid * nw + w, lane);
-    return;
-  }
-  const int64_t row = bid;
-  const int col0 = w * 4096;
-  const bool valid = col0 + S::off(lane, 0) < a.len;  // lanes past the row end idle (whole lanes)
-  const Tin* __restrict__ xin = reinterpret_cast<const Tin*>(a.x);
-  const Tin* rp = xin + row * a.ldx;
-  float v[64];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int c = valid ? col0 + S::off(lane, j) : 0;
-    load8<Tin>(rp + c, &v[j * 8]);
-  }
-  const float sgn = rotate64<B>(v, lane);
-  float mx = valid ? absmax64(v) : 0.f;
-  mx = lane_max(mx, 6);
-  if (nw > 1) {
-    __shared__ float s_wmax[16];
-    if (lane == 0) s_wmax[w] = mx;
-    __syncthreads();
-    mx = 0.f;
-    for (int i = 0; i < nw; ++i) mx = __builtin_fmaxf(mx, s_wmax[i]);
-  }
-  if (w == 0 && lane == 0) a.scale[row] = stored_scale<QT>(a, mx);
-  if (!valid) return;
-  const float mul = quant_mul<QT>(a, mx) * sgn;
-  const int64_t base = row * a.ldq + col0;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) store_chunk8<QT>(a.q, base + S::off(lane, j), &v[j * 8], mul);
-}
-
-// Workgroups of one rows pass (0 for an empty one).
-static int64_t rows2_grid(const FqArgs& a) {
-  if (a.nvec == 0) return 0;
-  if (a.len >= 4096) return a.nvec;
-  const int64_t rpw = 4096 / a.len;
-  const int64_t waves = (a.nvec + rpw - 1) / rpw;
-  return (waves + 3) / 4;
-}
-
-template <typename Tin, int B, int QT>
-static hipError_t launch_rows2_t(FqPair pp, hipStream_t st) {
-  const int64_t L = pp.p0.len;
-  const int64_t g0 = rows2_grid(pp.p0), g1 = pp.has1 ? rows2_grid(pp.p1) : 0;
-  pp.split = g0;
-  const int64_t grid = g0 + g1;
-  if (grid == 0) {
-    if (pp.zero && pp.nzero > 0) return launch_fill_zero(reinterpret_cast<float*>(pp.zero), pp.nzero, st);
-    return hipSuccess;
-  }
-  const int multi = L >= 4096 ? 1 : 0;
-  const int nw = multi ? (int)((L + 4095) / 4096) : 4;
-  hipLaunchKernelGGL((fq_rows2_kernel<Tin, B, QT>), dim3((unsigned)grid), dim3(64 * nw), 0, st, pp,
-                     multi);
-  return hipGetLastError();
-}
 
 bool fq_rows2_supported(int64_t len, int block) {
   if (len <= 0 || len % 64 != 0 || len > 16 * 4096) return false;
   if (len < 4096 && 4096 % len != 0) return false;
   return block >= 1 && block <= 4096 && len % block == 0;
-}
-
-// ---------------------------------------------------------------------------
-// columns kernel
-// ---------------------------------------------------------------------------
-
-constexpr int kColsLdsBytes = 16 * 512 * 16;  // 16 waves x 512 chunks of 16 bytes
-
-// LDS chunk (16-byte slot) of chunk j of `lane` in wave w: lane-major per wave, so the compute
-// reads are contiguous; the XOR on the low 4 lane bits spreads the transposing writes over all
-// 64 banks.
-template <int B>
-__device__ __forceinline__ int lds_slot(int w, int lane, int j) {
-  constexpr int JA = B >= 64 ? B / 64 : 1;
-  return w * 512 + j * 64 + (lane ^ (((j * JA) ^ w) & 15));
-}
-
-__device__ __forceinline__ uint32_t bf16_pair(uint32_t lo_word, uint32_t hi_word, int half) {
-  // column `half` (0: low 16 bits, 1: high 16 bits) of two rows -> one dword, lower row first
-  return __builtin_amdgcn_perm(hi_word, lo_word, half ? 0x07060302u : 0x05040100u);
-}
-
-// One column pass: its arguments, its geometry (R rows per task, P tasks per strip of C =
-// 65536 / R columns) and its scratch (column maxima and per-strip arrival counters, both zero
-// at launch; unused when P == 1).
-struct ColsProb {
-  FqArgs a;
-  float* colmax;
-  uint32_t* arrive;
-  int R, P, C;
-};
-
-// One task (one R-row part of one column strip) of a column pass, run by a whole workgroup of
-// 16 waves.
-template <int B, int QT>
-__device__ __forceinline__ void cols_task(const ColsProb& pr, int64_t ltask, uint4* lds) {
-  using S = Slice<B>;
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const FqArgs& a = pr.a;
-  const int R = pr.R, P = pr.P, C = pr.C;
-  const int CC = C / 8;                      // 16-byte column chunks per row of the tile
-  const int cpw = 4096 / R;                  // column segments per wave
-  const int cc = t % CC, rg = t / CC;        // loader: column chunk, group of 8 rows
-  const int row_lanes_log2 = 31 - __builtin_clz((unsigned)(R / 64));
-  float* colmax = pr.colmax;
-  uint32_t* arrive = pr.arrive;
-  const int64_t ncols = a.nvec;
-  const uint16_t* __restrict__ xin = reinterpret_cast<const uint16_t*>(a.x);
-  const int64_t strip = ltask / P;
-  const int part = (int)(ltask % P);
-  const int64_t c0 = strip * C;
-
-    // ---- load 8 rows x 8 columns, transpose, write to LDS ------------------------------
-    {
-      const int64_t col = c0 + cc * 8;
-      const bool cvalid = col < ncols;
-      const uint16_t* p = xin + ((int64_t)part * R + rg * 8) * a.ldx + (cvalid ? col : 0);
-      uint4 raw[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) raw[i] = *reinterpret_cast<const uint4*>(p + i * a.ldx);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int cl = cc * 8 + e;             // column within the tile
-        const int wr = cl / cpw, ciw = cl % cpw;
-        int ln, j;
-        S::where(ciw * R + rg * 8, ln, j);
-        uint32_t d0, d1, d2, d3;
-        if ((e >> 1) == 0) {
-          d0 = bf16_pair(raw[0].x, raw[1].x, e & 1); d1 = bf16_pair(raw[2].x, raw[3].x, e & 1);
-          d2 = bf16_pair(raw[4].x, raw[5].x, e & 1); d3 = bf16_pair(raw[6].x, raw[7].x, e & 1);
-        } else if ((e >> 1) == 1) {
-          d0 = bf16_pair(raw[0].y, raw[1].y, e & 1); d1 = bf16_pair(raw[2].y, raw[3].y, e & 1);
-          d2 = bf16_pair(raw[4].y, raw[5].y, e & 1); d3 = bf16_pair(raw[6].y, raw[7].y, e & 1);
-        } else if ((e >> 1) == 2) {
-          d0 = bf16_pair(raw[0].z, raw[1].z, e & 1); d1 = bf16_pair(raw[2].z, raw[3].z, e & 1);
-          d2 = bf16_pair(raw[4].z, raw[5].z, e & 1); d3 = bf16_pair(raw[6].z, raw[7].z, e & 1);
-        } else {
-          d0 = bf16_pair(raw[0].w, raw[1].w, e & 1); d1 = bf16_pair(raw[2].w, raw[3].w, e & 1);
-          d2 = bf16_pair(raw[4].w, raw[5].w, e & 1); d3 = bf16_pair(raw[6].w, raw[7].w, e & 1);
-        }
-        lds[lds_slot<B>(wr, ln, j)] = make_uint4(d0, d1, d2, d3);
-      }
-    }
-    __syncthreads();
-
-    // ---- rotate the wave's column segments ------------------------------------------------
-    float v[64];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) unpack_bf16x8(lds[lds_slot<B>(w, lane, j)], &v[j * 8]);
-    const float sgn = rotate64<B>(v, lane);
-    const int seg = S::off(lane, 0) / R;       // column segment of this lane within the wave
-    const int64_t col = c0 + w * cpw + seg;
-    const bool valid = col < ncols;
-    float mx = lane_max(absmax64(v), row_lanes_log2);
-    const bool writer = (lane & ((1 << row_lanes_log2) - 1)) == 0;
-
-    // ---- column maxima of a strip split over P tasks ---------------------------------------
-    // Device-scope atomics only (they are performed at the device's coherence point, across
-    // XCDs): each task max-reduces its partial maxima into colmax (non-negative floats order
-    // like their bit patterns) and waits for their returned values; one thread then counts the task
-    // in and waits for all P; one thread per column reads the final maximum back with an
-    // atomic load and shares it through LDS.  No cache-wide fence is needed.
-    if (P > 1) {
-      __shared__ float s_cmax[1024];
-      uint32_t* cm = reinterpret_cast<uint32_t*>(colmax);
-      uint32_t seen = 0;
-      if (valid && writer)
-        seen = __hip_atomic_fetch_max(&cm[col], __float_as_uint(mx), __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT);
-      // every wave waits for the values its atomics return (so they have been performed at
-      // the coherence point) before it reaches the barrier, so the arrival counted below
-      // covers them: a workgroup barrier alone does not wait for outstanding memory operations,
-      // and an unused return value would let the compiler drop the wait
-      asm volatile("s_waitcnt vmcnt(0)" ::"v"(seen) : "memory");
-      __syncthreads();
-      if (t == 0) {
-        __hip_atomic_fetch_add(&arrive[strip], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        // the other tasks of this strip are dispatched (workgroups start in index order), so
-        // the count reaches P; the bound only guards against a broken launch
-        for (uint32_t it = 0; it < (1u << 20); ++it) {
-          if (__hip_atomic_load(&arrive[strip], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >=
-              (uint32_t)P)
-            break;
-          __builtin_amdgcn_s_sleep(2);
-        }
-      }
-      __syncthreads();
-      if (t < C && c0 + t < ncols)
-        s_cmax[t] = __uint_as_float(
-            __hip_atomic_load(&cm[c0 + t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-      __syncthreads();
-      if (valid) mx = s_cmax[w * cpw + seg];
-    }
-
-    // ---- quantise and store the transposed codes ------------------------------------------
-    if (valid) {
-      if (part == 0 && writer) a.scale[col] = stored_scale<QT>(a, mx);
-      const float mul = quant_mul<QT>(a, mx) * sgn;
-      const int64_t base = col * a.ldq + (int64_t)part * R - (int64_t)seg * R;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) store_chunk8<QT>(a.q, base + S::off(lane, j), &v[j * 8], mul);
-    }
-}
-
-template <int B, int QT>
-__global__ __launch_bounds__(1024) void fq_cols2_kernel(ColsProb c0, ColsProb c1, int64_t split,
-                                                        int64_t tasks) {
-  extern __shared__ __attribute__((aligned(16))) uint4 lds[];
-  for (int64_t task = blockIdx.x; task < tasks; task += gridDim.x) {
-    const bool second = task >= split;
-    const ColsProb pr = second ? c1 : c0;
-    cols_task<B, QT>(pr, task - (second ? split : 0), lds);
-    __syncthreads();  // the next task overwrites the LDS tile
-  }
-}
-
-// The rotation passes of a layer backward in one launch: the rows of dY (codes QG) and the
-// columns of W (QW), dY (QG) and X (QW).  Workgroups [0, rows_wg) run the rows pass, 16 waves
-// each; the column passes follow in order, one task per workgroup.  All passes read bf16.
-struct FqBatch {
-  FqArgs rows;
-  int64_t rows_wg;
-  ColsProb cw, cdy, cx;
-  int64_t end_w, end_dy, end_x;  // one past the last workgroup of each column pass
-};
-
-template <int B, int QG, int QW>
-__global__ __launch_bounds__(1024) void fq_batch_kernel(FqBatch fb) {
-  extern __shared__ __attribute__((aligned(16))) uint4 lds[];
-  const int64_t bid = blockIdx.x;
-  if (bid < fb.rows_wg) {
-    rows_wave<uint16_t, B, QG>(fb.rows, bid * 16 + (threadIdx.x >> 6), threadIdx.x & 63);
-  } else if (bid < fb.end_w) {
-    cols_task<B, QW>(fb.cw, bid - fb.rows_wg, lds);
-  } else if (bid < fb.end_dy) {
-    cols_task<B, QG>(fb.cdy, bid - fb.end_w, lds);
-  } else {
-    cols_task<B, QW>(fb.cx, bid - fb.end_dy, lds);
-  }
-}
-
-// Rows per task for a column of `rows` elements; 0 when the shape is not covered.
-static int cols2_rows_per_task(int64_t rows, int block) {
-  int R;
-  if (block > 1024) R = block;
-  else if (rows >= 1024) R = 1024;
-  else R = (int)rows;
-  if (R < 64 || R > 4096 || (R & (R - 1)) != 0) return 0;
-  if (rows % R != 0 || R % block != 0) return 0;
-  return R;
 }
 
 size_t fq_cols2_ws_bytes(int64_t rows, int64_t cols, int block, int in_bf16) {
@@ -573,175 +30,19 @@ bool fq_cols2_supported(int64_t rows, int64_t cols, int block, int in_bf16, size
   return rows / R == 1 || ws_bytes >= fq_cols2_ws_bytes(rows, cols, block, in_bf16);
 }
 
-// Workgroups that can be resident at once (one per compute unit: the tile takes 128 KB of
-// LDS), queried once per device.
-static int cols2_capacity(const void* fn) {
-  static int cap[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cap[dev] > 0) return cap[dev];
-  int cus = 0, per_cu = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 1024, kColsLdsBytes) != hipSuccess)
-    return 0;
-  cap[dev] = cus * per_cu;
-  return cap[dev];
-}
-
-// Scratch layout of one pass: arrival counters (padded to 256 bytes), then the column maxima.
-static void cols2_scratch(void* ws, int64_t strips, float** colmax, uint32_t** arrive,
-                          int64_t* words) {
-  const size_t cnt = ((size_t)strips * 4 + 255) & ~(size_t)255;
-  *arrive = reinterpret_cast<uint32_t*>(ws);
-  *colmax = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + cnt);
-  *words = (int64_t)(cnt / 4);
-}
-
-// Geometry and scratch of one column pass (rows = a.len); tasks = 0 for an empty pass.
-static ColsProb cols2_prob(const FqArgs& a, void* ws, int64_t* tasks, int64_t* scratch_words) {
-  ColsProb pr{};
-  pr.a = a;
-  pr.R = cols2_rows_per_task(a.len, a.block);
-  pr.P = (int)(a.len / pr.R);
-  pr.C = 65536 / pr.R;
-  const int64_t strips = (a.nvec + pr.C - 1) / pr.C;
-  *tasks = (a.nvec == 0 || a.len == 0) ? 0 : strips * pr.P;
-  *scratch_words = 0;
-  if (pr.P > 1 && *tasks > 0) {
-    cols2_scratch(ws, strips, &pr.colmax, &pr.arrive, scratch_words);
-    *scratch_words += a.nvec;
-  }
-  return pr;
-}
-
-template <typename K>
-static hipError_t set_cols_lds(K* fn) {
-  static std::once_flag once;
-  static hipError_t attr_err = hipSuccess;
-  std::call_once(once, [fn] {
-    attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, kColsLdsBytes);
-  });
-  return attr_err;
-}
-
-template <int B, int QT>
-static hipError_t launch_cols2_t(const FqArgs& a0, void* ws0, const FqArgs* a1, void* ws1,
-                                 int prezeroed, hipStream_t st) {
-  auto* fn = &fq_cols2_kernel<B, QT>;
-  hipError_t e = set_cols_lds(fn);
-  if (e != hipSuccess) return e;
-  int64_t t0 = 0, t1 = 0, w0 = 0, w1 = 0;
-  ColsProb p0 = cols2_prob(a0, ws0, &t0, &w0);
-  ColsProb p1 = a1 ? cols2_prob(*a1, ws1, &t1, &w1) : p0;
-  if (!prezeroed) {
-    if (w0 > 0 && (e = launch_fill_zero(reinterpret_cast<float*>(ws0), w0, st)) != hipSuccess) return e;
-    if (w1 > 0 && (e = launch_fill_zero(reinterpret_cast<float*>(ws1), w1, st)) != hipSuccess) return e;
-  }
-  if (t0 == 0) {  // keep the first slot filled: the kernel picks by task index
-    p0 = p1;
-    t0 = t1;
-    t1 = 0;
-  }
-  const int64_t tasks = t0 + t1;
-  if (tasks == 0) return hipSuccess;
-  // one task per workgroup; the P tasks of a strip are consecutive workgroups.  A waiting
-  // workgroup only waits for the other members of its own group, and the hardware dispatches
-  // workgroups in index order on each XCD: every group below the lowest undispatched
-  // workgroup is fully dispatched and finishes, freeing room for the rest, so every wait ends
-  // as long as one group fits on the device at once.
-  const int P = p0.P > p1.P ? p0.P : p1.P;
-  if (P > 1 && cols2_capacity(reinterpret_cast<const void*>(fn)) < P)
-    return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fq_cols2_kernel<B, QT>), dim3((unsigned)tasks), dim3(1024), kColsLdsBytes,
-                     st, p0, p1, t0, tasks);
-  return hipGetLastError();
-}
-
-template <int QT>
-static hipError_t cols2_block(const FqArgs& a0, void* ws0, const FqArgs* a1, void* ws1,
-                              int prezeroed, hipStream_t st) {
-#define HALO_C2_CASE(BB) \
-  case BB: return launch_cols2_t<BB, QT>(a0, ws0, a1, ws1, prezeroed, st);
-  switch (a0.block) {
-    HALO_C2_CASE(1) HALO_C2_CASE(2) HALO_C2_CASE(4) HALO_C2_CASE(8) HALO_C2_CASE(16)
-    HALO_C2_CASE(32) HALO_C2_CASE(64) HALO_C2_CASE(128) HALO_C2_CASE(256) HALO_C2_CASE(512)
-    HALO_C2_CASE(1024) HALO_C2_CASE(2048) HALO_C2_CASE(4096)
-    default: return hipErrorInvalidValue;
-  }
-#undef HALO_C2_CASE
-}
+bool fq_batch_rows_ok(int64_t len) { return len >= 64 && len <= 4096 && 4096 % len == 0; }
 
 hipError_t launch_fq_cols2_pair(const FqArgs& a0, void* ws0, const FqArgs* a1, void* ws1, int qt,
                                 int prezeroed, hipStream_t st) {
+  // the two passes of one launch share the rounding mode
+  if (a1 && a1->sr != a0.sr) return hipErrorInvalidValue;
+  if (a0.sr && qt != 3) return cols2_dispatch_sr(a0, ws0, a1, ws1, qt, prezeroed, st);
   switch (qt) {
-    case 0: return cols2_block<0>(a0, ws0, a1, ws1, prezeroed, st);
-    case 1: return cols2_block<1>(a0, ws0, a1, ws1, prezeroed, st);
-    case 2: return cols2_block<2>(a0, ws0, a1, ws1, prezeroed, st);
-    case 3: return cols2_block<3>(a0, ws0, a1, ws1, prezeroed, st);
+    case 0: return cols2_block<0, false>(a0, ws0, a1, ws1, prezeroed, st);
+    case 1: return cols2_block<1, false>(a0, ws0, a1, ws1, prezeroed, st);
+    case 2: return cols2_block<2, false>(a0, ws0, a1, ws1, prezeroed, st);
+    case 3: return cols2_block<3, false>(a0, ws0, a1, ws1, prezeroed, st);
   }
-  return hipErrorInvalidValue;
-}
-
-// ---------------------------------------------------------------------------
-// backward batch
-// ---------------------------------------------------------------------------
-
-bool fq_batch_rows_ok(int64_t len) { return len >= 64 && len <= 4096 && 4096 % len == 0; }
-
-template <int B, int QG, int QW>
-static hipError_t launch_batch_t(const FqArgs* rows, const FqArgs& cw, void* ws_w,
-                                 const FqArgs& cdy, void* ws_dy, const FqArgs& cx, void* ws_x,
-                                 hipStream_t st) {
-  auto* fn = &fq_batch_kernel<B, QG, QW>;
-  hipError_t e = set_cols_lds(fn);
-  if (e != hipSuccess) return e;
-  FqBatch fb{};
-  int64_t tw = 0, tdy = 0, tx = 0, scratch = 0;
-  if (rows) {
-    fb.rows = *rows;
-    const int64_t waves = (rows->nvec * rows->len + 4095) / 4096;
-    fb.rows_wg = rows->nvec == 0 ? 0 : (waves + 15) / 16;
-  }
-  fb.cw = cols2_prob(cw, ws_w, &tw, &scratch);
-  fb.cdy = cols2_prob(cdy, ws_dy, &tdy, &scratch);
-  fb.cx = cols2_prob(cx, ws_x, &tx, &scratch);
-  fb.end_w = fb.rows_wg + tw;
-  fb.end_dy = fb.end_w + tdy;
-  fb.end_x = fb.end_dy + tx;
-  if (fb.end_x == 0) return hipSuccess;
-  int P = fb.cw.P;
-  if (fb.cdy.P > P) P = fb.cdy.P;
-  if (fb.cx.P > P) P = fb.cx.P;
-  if (P > 1 && cols2_capacity(reinterpret_cast<const void*>(fn)) < P)
-    return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fq_batch_kernel<B, QG, QW>), dim3((unsigned)fb.end_x), dim3(1024),
-                     kColsLdsBytes, st, fb);
-  return hipGetLastError();
-}
-
-template <int QG, int QW>
-static hipError_t batch_block(int block, const FqArgs* rows, const FqArgs& cw, void* ws_w,
-                              const FqArgs& cdy, void* ws_dy, const FqArgs& cx, void* ws_x,
-                              hipStream_t st) {
-#define HALO_B_CASE(BB) \
-  case BB: return launch_batch_t<BB, QG, QW>(rows, cw, ws_w, cdy, ws_dy, cx, ws_x, st);
-  switch (block) {
-    HALO_B_CASE(1) HALO_B_CASE(2) HALO_B_CASE(4) HALO_B_CASE(8) HALO_B_CASE(16)
-    HALO_B_CASE(32) HALO_B_CASE(64) HALO_B_CASE(128) HALO_B_CASE(256) HALO_B_CASE(512)
-    HALO_B_CASE(1024) HALO_B_CASE(2048) HALO_B_CASE(4096)
-    default: return hipErrorInvalidValue;
-  }
-#undef HALO_B_CASE
-}
-
-hipError_t launch_fq_batch(const FqArgs* rows, const FqArgs& cw, void* ws_w, const FqArgs& cdy,
-                           void* ws_dy, const FqArgs& cx, void* ws_x, int qg, int qw,
-                           hipStream_t st) {
-  if (qg == 0 && qw == 0) return batch_block<0, 0>(cw.block, rows, cw, ws_w, cdy, ws_dy, cx, ws_x, st);
-  if (qg == 2 && qw == 1) return batch_block<2, 1>(cw.block, rows, cw, ws_w, cdy, ws_dy, cx, ws_x, st);
-  if (qg == 1 && qw == 1) return batch_block<1, 1>(cw.block, rows, cw, ws_w, cdy, ws_dy, cx, ws_x, st);
   return hipErrorInvalidValue;
 }
 
@@ -749,46 +50,47 @@ hipError_t launch_fq_cols2(const FqArgs& a, int qt, void* ws, hipStream_t st) {
   return launch_fq_cols2_pair(a, ws, nullptr, nullptr, qt, 0, st);
 }
 
-// ---------------------------------------------------------------------------
-// rows dispatch
-// ---------------------------------------------------------------------------
+hipError_t launch_fq_batch(const FqArgs* rows, const FqArgs& cw, void* ws_w, const FqArgs& cdy,
+                           void* ws_dy, const FqArgs& cx, void* ws_x, int qg, int qw,
+                           hipStream_t st) {
+  // stochastic rounding applies to the dY passes only
+  if (cw.sr || cx.sr || (rows && rows->sr != cdy.sr)) return hipErrorInvalidValue;
+  if (cdy.sr) return batch_dispatch_sr(qg, qw, rows, cw, ws_w, cdy, ws_dy, cx, ws_x, st);
+  if (qg == 0 && qw == 0) return batch_block<0, 0, false>(cw.block, rows, cw, ws_w, cdy, ws_dy, cx, ws_x, st);
+  if (qg == 2 && qw == 1) return batch_block<2, 1, false>(cw.block, rows, cw, ws_w, cdy, ws_dy, cx, ws_x, st);
+  if (qg == 1 && qw == 1) return batch_block<1, 1, false>(cw.block, rows, cw, ws_w, cdy, ws_dy, cx, ws_x, st);
+  return hipErrorInvalidValue;
+}
 
-template <typename Tin, int QT>
-static hipError_t rows2_block(const FqPair& a, hipStream_t st) {
-#define HALO_R2_CASE(BB) \
-  case BB: return launch_rows2_t<Tin, BB, QT>(a, st);
-  switch (a.p0.block) {
-    HALO_R2_CASE(1) HALO_R2_CASE(2) HALO_R2_CASE(4) HALO_R2_CASE(8) HALO_R2_CASE(16)
-    HALO_R2_CASE(32) HALO_R2_CASE(64) HALO_R2_CASE(128) HALO_R2_CASE(256) HALO_R2_CASE(512)
-    HALO_R2_CASE(1024) HALO_R2_CASE(2048) HALO_R2_CASE(4096)
-    default: return hipErrorInvalidValue;
+hipError_t launch_fq_rows2_pair(const FqPair& a, int in_bf16, int qt, hipStream_t st) {
+  // the two passes of one launch share the rounding mode
+  if (a.has1 && a.p1.sr != a.p0.sr) return hipErrorInvalidValue;
+  if (a.p0.sr && qt != 3) {  // stochastic rounding: bf16 input (fp32 takes the older kernel)
+    if (!in_bf16) return hipErrorInvalidValue;
+    return rows2_dispatch_sr(a, qt, st);
   }
-#undef HALO_R2_CASE
+  if (in_bf16) {
+    switch (qt) {
+      case 0: return rows2_block<uint16_t, 0, false>(a, st);
+      case 1: return rows2_block<uint16_t, 1, false>(a, st);
+      case 2: return rows2_block<uint16_t, 2, false>(a, st);
+      case 3: return rows2_block<uint16_t, 3, false>(a, st);
+    }
+  } else {
+    switch (qt) {
+      case 0: return rows2_block<float, 0, false>(a, st);
+      case 1: return rows2_block<float, 1, false>(a, st);
+      case 2: return rows2_block<float, 2, false>(a, st);
+      case 3: return rows2_block<float, 3, false>(a, st);
+    }
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_fq_rows2(const FqArgs& a, int in_bf16, int qt, hipStream_t st) {
   FqPair pp{};
   pp.p0 = a;
   return launch_fq_rows2_pair(pp, in_bf16, qt, st);
-}
-
-hipError_t launch_fq_rows2_pair(const FqPair& a, int in_bf16, int qt, hipStream_t st) {
-  if (in_bf16) {
-    switch (qt) {
-      case 0: return rows2_block<uint16_t, 0>(a, st);
-      case 1: return rows2_block<uint16_t, 1>(a, st);
-      case 2: return rows2_block<uint16_t, 2>(a, st);
-      case 3: return rows2_block<uint16_t, 3>(a, st);
-    }
-  } else {
-    switch (qt) {
-      case 0: return rows2_block<float, 0>(a, st);
-      case 1: return rows2_block<float, 1>(a, st);
-      case 2: return rows2_block<float, 2>(a, st);
-      case 3: return rows2_block<float, 3>(a, st);
-    }
-  }
-  return hipErrorInvalidValue;
 }
 
 }  // namespace halo

@@ -48,10 +48,25 @@ float qmax_of(halo_dtype q) {
 
 halo_status from_hip(hipError_t e) { return e == hipSuccess ? HALO_OK : HALO_ERR_HIP; }
 
+int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+// Padded (rotated) length of a vector of L elements: a multiple of the block (the zero
+// padding of the QWHA page, s5).
+int64_t padded_len(int64_t L, int32_t block) { return round_up(L, block); }
+
+// Contraction length of a layer product: the dimension zero-padded to a multiple of the block
+// and of 32 (the FP8 matrix cores' k step); blocks past the padded length are all zero and
+// get zero codes, so the product equals the one over the padded operands.
+int64_t contraction_len(int64_t d, int32_t block) { return round_up(d, block > 32 ? block : 32); }
+
+halo_status check_signs(const uint32_t* signs) {
+  return signs && !aligned16(signs) ? HALO_ERR_ALIGN : HALO_OK;
+}
+
 // Validation of one rotation pass; shared by halo_fwht_quant and the layer calls.
 halo_status check_fq(const void* x, halo_dtype xt, int64_t rows, int64_t cols, int64_t ldx,
                      halo_axis axis, int32_t block, halo_dtype qt, const void* q, int64_t ldq,
-                     const float* scale) {
+                     const float* scale, const halo_quant_opts* o) {
   if (rows < 0 || cols < 0) return HALO_ERR_SHAPE;
   const bool any = rows > 0 && cols > 0;  // empty matrices may come with NULL pointers
   if ((any && (!x || !q)) || (!scale && (axis == HALO_ALONG_ROWS ? rows : cols) > 0))
@@ -61,25 +76,56 @@ halo_status check_fq(const void* x, halo_dtype xt, int64_t rows, int64_t cols, i
   if (axis != HALO_ALONG_ROWS && axis != HALO_ALONG_COLS) return HALO_ERR_SHAPE;
   if (rows < 0 || cols < 0 || rows >= kMaxDim || cols >= kMaxDim) return HALO_ERR_SHAPE;
   if (ldx < cols || ldx < 1) return HALO_ERR_SHAPE;
+  if (!valid_block(block)) return HALO_ERR_BLOCK;
   const int64_t L = axis == HALO_ALONG_ROWS ? cols : rows;
+  const int64_t Lp = padded_len(L, block);
   const int64_t nvec = axis == HALO_ALONG_ROWS ? rows : cols;
-  if (ldq < L || ldq < 1) return HALO_ERR_SHAPE;
-  if (!valid_block(block) || (L % block) != 0) return HALO_ERR_BLOCK;
-  if (L % 8 != 0) return HALO_ERR_SHAPE;
+  if (ldq < Lp || ldq < 1) return HALO_ERR_SHAPE;
+  if (Lp % 8 != 0) return HALO_ERR_SHAPE;
+  if (axis == HALO_ALONG_ROWS && L % 8 != 0) return HALO_ERR_SHAPE;
   if (axis == HALO_ALONG_COLS && nvec % 8 != 0) return HALO_ERR_SHAPE;
-  if (axis == HALO_ALONG_ROWS && L > fq_rows_max_len(block)) return HALO_ERR_SHAPE;
+  if (axis == HALO_ALONG_ROWS && Lp > fq_rows_max_len(block)) return HALO_ERR_SHAPE;
+  if (o) {
+    if (o->rounding != HALO_ROUND_NEAREST_EVEN && o->rounding != HALO_ROUND_STOCHASTIC)
+      return HALO_ERR_OPTION;
+    if (o->rounding == HALO_ROUND_STOCHASTIC && qt == HALO_F32) return HALO_ERR_OPTION;
+  }
   if (!aligned16(x) || !aligned16(q) || !aligned16(scale)) return HALO_ERR_ALIGN;
   if ((ldx * esize(xt)) % 16 != 0 || (ldq * esize(qt)) % 16 != 0) return HALO_ERR_ALIGN;
+  if (o && check_signs(o->signs) != HALO_OK) return HALO_ERR_ALIGN;
   return HALO_OK;
 }
 
+// Options of one pass: the transform's signs and the rounding of its codes.
+struct PassOpts {
+  const uint32_t* signs = nullptr;
+  int sr = 0;
+  uint32_t key0 = 0, key1 = 0, ctr2 = 0, ctr3 = 0;
+};
+
+PassOpts pass_opts(const halo_quant_opts* o) {
+  PassOpts p;
+  if (!o) return p;
+  p.signs = o->signs;
+  p.sr = o->rounding == HALO_ROUND_STOCHASTIC ? 1 : 0;
+  p.key0 = o->seed[0];
+  p.key1 = o->seed[1];
+  p.ctr2 = o->counter[0];
+  p.ctr3 = o->counter[1];
+  return p;
+}
+
+// Arguments of one pass over x[rows x cols]; len: the rotated (padded) length, 0 = the
+// vector length padded to a multiple of the block.
 FqArgs make_fq(const void* x, int64_t rows, int64_t cols, int64_t ldx, halo_axis axis,
-               int32_t block, halo_dtype qt, void* q, int64_t ldq, float* scale) {
+               int32_t block, halo_dtype qt, void* q, int64_t ldq, float* scale,
+               const PassOpts& po = PassOpts(), int64_t len = 0) {
   FqArgs a{};
   a.x = x;
   a.ldx = ldx;
   a.nvec = axis == HALO_ALONG_ROWS ? rows : cols;
-  a.len = axis == HALO_ALONG_ROWS ? cols : rows;
+  a.in_len = axis == HALO_ALONG_ROWS ? cols : rows;
+  a.len = len > 0 ? len : padded_len(a.in_len, block);
   a.q = q;
   a.ldq = ldq;
   a.scale = scale;
@@ -87,32 +133,34 @@ FqArgs make_fq(const void* x, int64_t rows, int64_t cols, int64_t ldx, halo_axis
   a.qmax = qmax_of(qt);
   a.denom = (float)((double)a.qmax * std::sqrt((double)block));
   a.inv_sqrt_b = (float)(1.0 / std::sqrt((double)block));
+  a.signs = po.signs;
+  a.sr = po.sr;
+  a.key0 = po.key0;
+  a.key1 = po.key1;
+  a.ctr2 = po.ctr2;
+  a.ctr3 = po.ctr3;
   return a;
 }
 
-halo_status run_fq(const void* x, halo_dtype xt, int64_t rows, int64_t cols, int64_t ldx,
-                   halo_axis axis, int32_t block, halo_dtype qt, void* q, int64_t ldq,
-                   float* scale, void* ws, size_t ws_bytes, hipStream_t st) {
-  FqArgs a{};
-  a.x = x;
-  a.ldx = ldx;
-  a.nvec = axis == HALO_ALONG_ROWS ? rows : cols;
-  a.len = axis == HALO_ALONG_ROWS ? cols : rows;
-  a.q = q;
-  a.ldq = ldq;
-  a.scale = scale;
-  a.block = block;
-  a.qmax = qmax_of(qt);
-  a.denom = (float)((double)a.qmax * std::sqrt((double)block));
-  a.inv_sqrt_b = (float)(1.0 / std::sqrt((double)block));
+halo_status run_fa(const FqArgs& a, halo_dtype xt, halo_axis axis, halo_dtype qt, void* ws,
+                   size_t ws_bytes, hipStream_t st) {
   return from_hip(launch_fwht_quant(a, xt == HALO_BF16 ? 1 : 0, qt_index(qt), (int)axis, ws,
                                     ws ? ws_bytes : 0, st));
 }
 
-// Scratch of one rotation pass (the single-read columns kernel's partial maxima and counters).
-size_t fq_ws_bytes(int64_t rows, int64_t cols, halo_axis axis, int32_t block, halo_dtype xt) {
+halo_status run_fq(const void* x, halo_dtype xt, int64_t rows, int64_t cols, int64_t ldx,
+                   halo_axis axis, int32_t block, halo_dtype qt, void* q, int64_t ldq,
+                   float* scale, void* ws, size_t ws_bytes, hipStream_t st,
+                   const PassOpts& po = PassOpts(), int64_t len = 0) {
+  const FqArgs a = make_fq(x, rows, cols, ldx, axis, block, qt, q, ldq, scale, po, len);
+  return run_fa(a, xt, axis, qt, ws, ws_bytes, st);
+}
+
+// Scratch of one rotation pass (the single-read columns kernel's partial maxima and counters);
+// len: the rotated (padded) length.
+size_t fq_ws_bytes_len(int64_t len, int64_t nvec, halo_axis axis, int32_t block, halo_dtype xt) {
   if (axis != HALO_ALONG_COLS) return 0;
-  return fq_cols2_ws_bytes(rows, cols, block, xt == HALO_BF16 ? 1 : 0);
+  return fq_cols2_ws_bytes(len, nvec, block, xt == HALO_BF16 ? 1 : 0);
 }
 
 halo_status check_gemm(const void* a, int64_t lda, const void* b, int64_t ldb, int64_t m,
@@ -146,19 +194,21 @@ WsPlan plan_ws(int64_t m, int64_t n, int64_t k, int backward, int32_t block, hal
   WsPlan p{};
   size_t sizes[9];
   int cnt = 0;
+  const int64_t kq = contraction_len(k, block), nq = contraction_len(n, block),
+                mq = contraction_len(m, block);
   if (!backward) {
-    sizes[cnt++] = (size_t)m * k;      // X codes   [m x k]
+    sizes[cnt++] = (size_t)m * kq;     // X codes   [m x kq]
     sizes[cnt++] = (size_t)m * 4;      // X scales
-    sizes[cnt++] = (size_t)n * k;      // W codes   [n x k]
+    sizes[cnt++] = (size_t)n * kq;     // W codes   [n x kq]
     sizes[cnt++] = (size_t)n * 4;      // W scales
   } else {
-    sizes[cnt++] = (size_t)m * n;      // dY row codes     [m x n]
+    sizes[cnt++] = (size_t)m * nq;     // dY row codes     [m x nq]
     sizes[cnt++] = (size_t)m * 4;
-    sizes[cnt++] = (size_t)k * n;      // W column codes   [k x n]
+    sizes[cnt++] = (size_t)k * nq;     // W column codes   [k x nq]
     sizes[cnt++] = (size_t)k * 4;
-    sizes[cnt++] = (size_t)n * m;      // dY column codes  [n x m]
+    sizes[cnt++] = (size_t)n * mq;     // dY column codes  [n x mq]
     sizes[cnt++] = (size_t)n * 4;
-    sizes[cnt++] = (size_t)k * m;      // X column codes   [k x m]
+    sizes[cnt++] = (size_t)k * mq;     // X column codes   [k x mq]
     sizes[cnt++] = (size_t)k * 4;
   }
   size_t o = 0;
@@ -167,9 +217,9 @@ WsPlan plan_ws(int64_t m, int64_t n, int64_t k, int backward, int32_t block, hal
     o += round256(sizes[i]);
   }
   if (backward) {
-    p.scr_w = round256(fq_ws_bytes(n, k, HALO_ALONG_COLS, block, io));   // W columns along n
-    p.scr_dy = round256(fq_ws_bytes(m, n, HALO_ALONG_COLS, block, io));  // dY columns along m
-    p.scr_x = round256(fq_ws_bytes(m, k, HALO_ALONG_COLS, block, io));   // X columns along m
+    p.scr_w = round256(fq_ws_bytes_len(nq, k, HALO_ALONG_COLS, block, io));   // W columns along n
+    p.scr_dy = round256(fq_ws_bytes_len(mq, n, HALO_ALONG_COLS, block, io));  // dY columns along m
+    p.scr_x = round256(fq_ws_bytes_len(mq, k, HALO_ALONG_COLS, block, io));   // X columns along m
   }
   p.scratch_off = o;
   p.scratch_bytes = p.scr_w + p.scr_dy + p.scr_x;
@@ -197,11 +247,12 @@ const char* halo_status_str(halo_status s) {
     case HALO_OK: return "ok";
     case HALO_ERR_NULL: return "a required pointer is NULL";
     case HALO_ERR_SHAPE: return "unsupported or inconsistent sizes";
-    case HALO_ERR_BLOCK: return "block must be a power of two in [1, 4096] dividing the rotated length";
+    case HALO_ERR_BLOCK: return "block must be a power of two in [1, 4096]";
     case HALO_ERR_DTYPE: return "unsupported element type";
     case HALO_ERR_ALIGN: return "pointer or leading dimension not 16-byte aligned";
     case HALO_ERR_WORKSPACE: return "workspace missing or too small";
     case HALO_ERR_HIP: return "HIP launch failed";
+    case HALO_ERR_OPTION: return "invalid rounding option";
   }
   return "unknown status";
 }
@@ -210,18 +261,27 @@ size_t halo_fwht_quant_workspace_bytes(int64_t rows, int64_t cols, halo_axis axi
                                        int32_t block, halo_dtype x_type) {
   if (rows < 0 || cols < 0 || rows >= kMaxDim || cols >= kMaxDim || !valid_block(block))
     return 0;
-  return fq_ws_bytes(rows, cols, axis, block, x_type);
+  if (axis != HALO_ALONG_COLS) return 0;
+  return fq_ws_bytes_len(padded_len(rows, block), cols, axis, block, x_type);
+}
+
+halo_status halo_fwht_quant_ex(const void* x, halo_dtype x_type, int64_t rows, int64_t cols,
+                               int64_t ldx, halo_axis axis, int32_t block, halo_dtype q_type,
+                               void* q, int64_t ldq, float* scale, const halo_quant_opts* opts,
+                               void* ws, size_t ws_bytes, void* stream) {
+  halo_status s = check_fq(x, x_type, rows, cols, ldx, axis, block, q_type, q, ldq, scale, opts);
+  if (s != HALO_OK) return s;
+  if (ws && !aligned16(ws)) return HALO_ERR_ALIGN;
+  return run_fq(x, x_type, rows, cols, ldx, axis, block, q_type, q, ldq, scale, ws, ws_bytes,
+                (hipStream_t)stream, pass_opts(opts));
 }
 
 halo_status halo_fwht_quant(const void* x, halo_dtype x_type, int64_t rows, int64_t cols,
                             int64_t ldx, halo_axis axis, int32_t block, halo_dtype q_type,
                             void* q, int64_t ldq, float* scale, void* ws, size_t ws_bytes,
                             void* stream) {
-  halo_status s = check_fq(x, x_type, rows, cols, ldx, axis, block, q_type, q, ldq, scale);
-  if (s != HALO_OK) return s;
-  if (ws && !aligned16(ws)) return HALO_ERR_ALIGN;
-  return run_fq(x, x_type, rows, cols, ldx, axis, block, q_type, q, ldq, scale, ws, ws_bytes,
-                (hipStream_t)stream);
+  return halo_fwht_quant_ex(x, x_type, rows, cols, ldx, axis, block, q_type, q, ldq, scale,
+                            nullptr, ws, ws_bytes, stream);
 }
 
 halo_status halo_gemm_i8(const int8_t* a, int64_t lda, const float* sa, const int8_t* b,
@@ -249,34 +309,48 @@ halo_status halo_gemm_fp8(const void* a, halo_dtype a_type, int64_t lda, const f
                   (hipStream_t)stream);
 }
 
+namespace {
+bool layer_dims_ok(int64_t m, int64_t n, int64_t k) {
+  return m >= 0 && n >= 0 && k >= 0 && m < kMaxDim && n < kMaxDim && k < kMaxDim;
+}
+}  // namespace
+
+size_t halo_linear_workspace_bytes_ex(int64_t m, int64_t n, int64_t k, int32_t block,
+                                      halo_dtype q_type, int backward) {
+  if (!layer_dims_ok(m, n, k) || !valid_block(block)) return 0;
+  if (q_type != HALO_I8 && q_type != HALO_E4M3) return 0;
+  // the columns passes' scratch is sized for bf16 input (fp32 input needs none)
+  return plan_ws(m, n, k, backward ? 1 : 0, block, HALO_BF16).total;
+}
+
 size_t halo_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, halo_dtype q_type,
                                    int backward) {
-  if (m < 0 || n < 0 || k < 0 || m >= kMaxDim || n >= kMaxDim || k >= kMaxDim) return 0;
-  if (q_type != HALO_I8 && q_type != HALO_E4M3) return 0;
-  // the block and the input type decide the columns passes' scratch: size it for the most
-  // demanding case (bf16 input, the block that needs the most partial maxima)
   size_t most = 0;
   for (int32_t b = 1; b <= 4096; b *= 2) {
-    const size_t t = plan_ws(m, n, k, backward ? 1 : 0, b, HALO_BF16).total;
+    const size_t t = halo_linear_workspace_bytes_ex(m, n, k, b, q_type, backward);
     if (t > most) most = t;
   }
   return most;
 }
 
-halo_status halo_linear_fwd(const void* x, const void* w, halo_dtype io_type, int64_t m,
-                            int64_t n, int64_t k, int32_t block, halo_dtype q_type, void* y,
-                            halo_dtype y_type, void* ws, size_t ws_bytes, void* stream) {
-  if (m < 0 || n < 0 || k <= 0 || m >= kMaxDim || n >= kMaxDim || k >= kMaxDim)
-    return HALO_ERR_SHAPE;
+halo_status halo_linear_fwd_ex(const void* x, const void* w, halo_dtype io_type, int64_t m,
+                               int64_t n, int64_t k, int32_t block, halo_dtype q_type, void* y,
+                               halo_dtype y_type, const halo_linear_opts* opts, void* ws,
+                               size_t ws_bytes, void* stream) {
+  if (!layer_dims_ok(m, n, k) || k == 0) return HALO_ERR_SHAPE;
   if ((m > 0 && !x) || (n > 0 && !w) || (m > 0 && n > 0 && !y)) return HALO_ERR_NULL;
   if (io_type != HALO_F32 && io_type != HALO_BF16) return HALO_ERR_DTYPE;
   if (q_type != HALO_I8 && q_type != HALO_E4M3) return HALO_ERR_DTYPE;
   if (y_type != HALO_F32 && y_type != HALO_BF16) return HALO_ERR_DTYPE;
-  if (k % 32 != 0) return HALO_ERR_SHAPE;
-  if (!valid_block(block) || k % block != 0) return HALO_ERR_BLOCK;
-  if (k > fq_rows_max_len(block)) return HALO_ERR_SHAPE;
+  if (!valid_block(block)) return HALO_ERR_BLOCK;
+  const int64_t kq = contraction_len(k, block);
+  if (k % 8 != 0 || kq > fq_rows_max_len(block)) return HALO_ERR_SHAPE;
+  if (opts && (opts->grad_rounding != HALO_ROUND_NEAREST_EVEN &&
+               opts->grad_rounding != HALO_ROUND_STOCHASTIC))
+    return HALO_ERR_OPTION;
   if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return HALO_ERR_ALIGN;
   if ((n * esize(y_type)) % 16 != 0) return HALO_ERR_ALIGN;
+  if (opts && check_signs(opts->signs_k) != HALO_OK) return HALO_ERR_ALIGN;
   const WsPlan p = plan_ws(m, n, k, 0, block, io_type);
   if (!ws || ws_bytes < p.total) return HALO_ERR_WORKSPACE;
   if (!aligned16(ws)) return HALO_ERR_ALIGN;
@@ -286,26 +360,38 @@ halo_status halo_linear_fwd(const void* x, const void* w, halo_dtype io_type, in
   void* qw = base + p.off[2];
   float* sw = reinterpret_cast<float*>(base + p.off[3]);
   hipStream_t st = (hipStream_t)stream;
+  PassOpts po;  // X and W: the signs along k, nearest-even codes
+  if (opts) po.signs = opts->signs_k;
+  const FqArgs ax = make_fq(x, m, k, k, HALO_ALONG_ROWS, block, q_type, qx, kq, sx, po, kq);
+  const FqArgs aw = make_fq(w, n, k, k, HALO_ALONG_ROWS, block, q_type, qw, kq, sw, po, kq);
   halo_status s = HALO_OK;
-  if (fq_rows2_supported(k, block)) {  // X and W rows in one launch
+  if (fq_rows2_supported(kq, block)) {  // X and W rows in one launch
     FqPair pp{};
-    pp.p0 = make_fq(x, m, k, k, HALO_ALONG_ROWS, block, q_type, qx, k, sx);
-    pp.p1 = make_fq(w, n, k, k, HALO_ALONG_ROWS, block, q_type, qw, k, sw);
+    pp.p0 = ax;
+    pp.p1 = aw;
     pp.has1 = 1;
     s = from_hip(launch_fq_rows2_pair(pp, io_type == HALO_BF16 ? 1 : 0, qt_index(q_type), st));
   } else {
-    s = run_fq(x, io_type, m, k, k, HALO_ALONG_ROWS, block, q_type, qx, k, sx, nullptr, 0, st);
-    if (s == HALO_OK)
-      s = run_fq(w, io_type, n, k, k, HALO_ALONG_ROWS, block, q_type, qw, k, sw, nullptr, 0, st);
+    s = run_fa(ax, io_type, HALO_ALONG_ROWS, q_type, nullptr, 0, st);
+    if (s == HALO_OK) s = run_fa(aw, io_type, HALO_ALONG_ROWS, q_type, nullptr, 0, st);
   }
-  if (s == HALO_OK) s = gemm_any(qx, q_type, k, sx, qw, q_type, k, sw, m, n, k, y, y_type, n, st);
+  if (s == HALO_OK)
+    s = gemm_any(qx, q_type, kq, sx, qw, q_type, kq, sw, m, n, kq, y, y_type, n, st);
   return s;
 }
 
-halo_status halo_linear_bwd(const void* dy, const void* x, const void* w, halo_dtype io_type,
-                            int64_t m, int64_t n, int64_t k, int32_t block, halo_dtype q_type,
-                            halo_dtype grad_q_type, void* dx, void* dw, void* ws,
-                            size_t ws_bytes, void* stream) {
+halo_status halo_linear_fwd(const void* x, const void* w, halo_dtype io_type, int64_t m,
+                            int64_t n, int64_t k, int32_t block, halo_dtype q_type, void* y,
+                            halo_dtype y_type, void* ws, size_t ws_bytes, void* stream) {
+  return halo_linear_fwd_ex(x, w, io_type, m, n, k, block, q_type, y, y_type, nullptr, ws,
+                            ws_bytes, stream);
+}
+
+halo_status halo_linear_bwd_ex(const void* dy, const void* x, const void* w, halo_dtype io_type,
+                               int64_t m, int64_t n, int64_t k, int32_t block, halo_dtype q_type,
+                               halo_dtype grad_q_type, void* dx, void* dw,
+                               const halo_linear_opts* opts, void* ws, size_t ws_bytes,
+                               void* stream) {
   if (!dy || !x || !w) return HALO_ERR_NULL;
   if (io_type != HALO_F32 && io_type != HALO_BF16) return HALO_ERR_DTYPE;
   if (q_type == HALO_I8) {
@@ -315,13 +401,18 @@ halo_status halo_linear_bwd(const void* dy, const void* x, const void* w, halo_d
   } else {
     return HALO_ERR_DTYPE;
   }
-  if (m <= 0 || n <= 0 || k <= 0 || m >= kMaxDim || n >= kMaxDim || k >= kMaxDim)
-    return HALO_ERR_SHAPE;
-  if (m % 32 != 0 || n % 32 != 0 || k % 32 != 0) return HALO_ERR_SHAPE;
-  if (!valid_block(block) || m % block != 0 || n % block != 0) return HALO_ERR_BLOCK;
-  if (dx && n > fq_rows_max_len(block)) return HALO_ERR_SHAPE;
+  if (!layer_dims_ok(m, n, k) || m == 0 || n == 0 || k == 0) return HALO_ERR_SHAPE;
+  if (!valid_block(block)) return HALO_ERR_BLOCK;
+  const int64_t nq = contraction_len(n, block), mq = contraction_len(m, block);
+  if (n % 8 != 0 || k % 8 != 0) return HALO_ERR_SHAPE;
+  if (dx && nq > fq_rows_max_len(block)) return HALO_ERR_SHAPE;
+  if (opts && (opts->grad_rounding != HALO_ROUND_NEAREST_EVEN &&
+               opts->grad_rounding != HALO_ROUND_STOCHASTIC))
+    return HALO_ERR_OPTION;
   if (!aligned16(dy) || !aligned16(x) || !aligned16(w)) return HALO_ERR_ALIGN;
   if ((dx && !aligned16(dx)) || (dw && !aligned16(dw))) return HALO_ERR_ALIGN;
+  if (opts && (check_signs(opts->signs_n) != HALO_OK || check_signs(opts->signs_m) != HALO_OK))
+    return HALO_ERR_ALIGN;
   const WsPlan p = plan_ws(m, n, k, 1, block, io_type);
   if (!ws || ws_bytes < p.total) return HALO_ERR_WORKSPACE;
   if (!aligned16(ws)) return HALO_ERR_ALIGN;
@@ -333,6 +424,34 @@ halo_status halo_linear_bwd(const void* dy, const void* x, const void* w, halo_d
   const int inb = io_type == HALO_BF16 ? 1 : 0;
   hipStream_t st = (hipStream_t)stream;
   halo_status s = HALO_OK;
+
+  // pass options: the signs along each contraction dimension; the dY codes' rounding (its
+  // columns pass draws at counter word 3 ^ 2^31)
+  PassOpts on, om, gn, gm;
+  if (opts) {
+    on.signs = gn.signs = opts->signs_n;
+    om.signs = gm.signs = opts->signs_m;
+    gn.sr = gm.sr = opts->grad_rounding == HALO_ROUND_STOCHASTIC ? 1 : 0;
+    gn.key0 = gm.key0 = opts->seed[0];
+    gn.key1 = gm.key1 = opts->seed[1];
+    gn.ctr2 = gm.ctr2 = opts->counter[0];
+    gn.ctr3 = opts->counter[1];
+    gm.ctr3 = opts->counter[1] ^ 0x80000000u;
+  }
+  void* qdy = base + p.off[0];
+  float* sdy = reinterpret_cast<float*>(base + p.off[1]);
+  void* qwt = base + p.off[2];
+  float* swt = reinterpret_cast<float*>(base + p.off[3]);
+  void* qdyt = base + p.off[4];
+  float* sdyt = reinterpret_cast<float*>(base + p.off[5]);
+  void* qxt = base + p.off[6];
+  float* sxt = reinterpret_cast<float*>(base + p.off[7]);
+  // dX = dY W: rows of dY and columns of W along n; dW = dY^T X: columns of dY and X along m
+  const FqArgs rows = make_fq(dy, m, n, n, HALO_ALONG_ROWS, block, grad_q_type, qdy, nq, sdy, gn, nq);
+  const FqArgs cw = make_fq(w, n, k, k, HALO_ALONG_COLS, block, q_type, qwt, nq, swt, on, nq);
+  const FqArgs cdy = make_fq(dy, m, n, n, HALO_ALONG_COLS, block, grad_q_type, qdyt, mq, sdyt, gm, mq);
+  const FqArgs cx = make_fq(x, m, k, k, HALO_ALONG_COLS, block, q_type, qxt, mq, sxt, om, mq);
+
   // the single-read column passes need their scratch cleared: folded into the first kernel
   // when that is a rows pass, else one fill
   bool zero_pending = p.scratch_bytes > 0;
@@ -341,40 +460,18 @@ halo_status halo_linear_bwd(const void* dy, const void* x, const void* w, halo_d
     s = from_hip(launch_fill_zero(reinterpret_cast<float*>(scr), (int64_t)(p.scratch_bytes / 4), st));
     zero_pending = false;
   };
-  // one column pass along the rows of x (length `rows`): single-read when covered
-  auto cols_pass = [&](const void* xx, int64_t rows, int64_t cols, halo_dtype qt, void* q,
-                       float* sc, void* sws, size_t sbytes) {
+  // one column pass: single-read when covered (its scratch already clear), else two reads
+  auto cols_pass = [&](const FqArgs& a, halo_dtype qt, void* sws, size_t sbytes) {
     if (s != HALO_OK) return;
-    if (fq_cols2_supported(rows, cols, block, inb, sbytes)) {
-      const FqArgs a = make_fq(xx, rows, cols, cols, HALO_ALONG_COLS, block, qt, q, rows, sc);
+    if (fq_cols2_supported(a.len, a.nvec, block, inb, sbytes))
       s = from_hip(launch_fq_cols2_pair(a, sws, nullptr, nullptr, qt_index(qt), 1, st));
-    } else {
-      s = run_fq(xx, io_type, rows, cols, cols, HALO_ALONG_COLS, block, qt, q, rows, sc, nullptr,
-                 0, st);
-    }
+    else
+      s = run_fa(a, io_type, HALO_ALONG_COLS, qt, nullptr, 0, st);
   };
-  const int qg = qt_index(grad_q_type), qw = qt_index(q_type);
-  const bool pair_ok = (qg == 0 && qw == 0) || (qg == 2 && qw == 1) || (qg == 1 && qw == 1);
-  if (dx && dw && inb && pair_ok && fq_cols2_supported(n, k, block, 1, p.scr_w) &&
-      fq_cols2_supported(m, n, block, 1, p.scr_dy) && fq_cols2_supported(m, k, block, 1, p.scr_x)) {
-    // every rotation pass of the backward in one launch (or two, when the dY rows are long):
-    // the passes overlap on the device, then the two products
-    void* qdy = base + p.off[0];
-    float* sdy = reinterpret_cast<float*>(base + p.off[1]);
-    void* qwt = base + p.off[2];
-    float* swt = reinterpret_cast<float*>(base + p.off[3]);
-    void* qdyt = base + p.off[4];
-    float* sdyt = reinterpret_cast<float*>(base + p.off[5]);
-    void* qxt = base + p.off[6];
-    float* sxt = reinterpret_cast<float*>(base + p.off[7]);
-    const FqArgs rows = make_fq(dy, m, n, n, HALO_ALONG_ROWS, block, grad_q_type, qdy, n, sdy);
-    const FqArgs cw = make_fq(w, n, k, k, HALO_ALONG_COLS, block, q_type, qwt, n, swt);
-    const FqArgs cdy = make_fq(dy, m, n, n, HALO_ALONG_COLS, block, grad_q_type, qdyt, m, sdyt);
-    const FqArgs cx = make_fq(x, m, k, k, HALO_ALONG_COLS, block, q_type, qxt, m, sxt);
-    const bool rows_in = fq_batch_rows_ok(n);
-    if (rows_in) {
-      clear_scratch();
-    } else if (fq_rows2_supported(n, block)) {
+  // the rows pass of dY, clearing the scratch as a side job when it runs as the wave kernel
+  auto rows_pass = [&]() {
+    if (s != HALO_OK) return;
+    if (fq_rows2_supported(nq, block) && (inb || !rows.sr)) {
       FqPair pp{};
       pp.p0 = rows;
       if (zero_pending) {
@@ -382,64 +479,56 @@ halo_status halo_linear_bwd(const void* dy, const void* x, const void* w, halo_d
         pp.nzero = (int64_t)(p.scratch_bytes / 4);
         zero_pending = false;
       }
-      s = from_hip(launch_fq_rows2_pair(pp, inb, qg, st));
+      s = from_hip(launch_fq_rows2_pair(pp, inb, qt_index(grad_q_type), st));
     } else {
-      s = run_fq(dy, io_type, m, n, n, HALO_ALONG_ROWS, block, grad_q_type, qdy, n, sdy, nullptr,
-                 0, st);
+      s = run_fa(rows, io_type, HALO_ALONG_ROWS, grad_q_type, nullptr, 0, st);
+    }
+  };
+  const int qg = qt_index(grad_q_type), qw = qt_index(q_type);
+  const bool pair_ok = (qg == 0 && qw == 0) || (qg == 2 && qw == 1) || (qg == 1 && qw == 1);
+  if (dx && dw && inb && pair_ok && fq_cols2_supported(nq, k, block, 1, p.scr_w) &&
+      fq_cols2_supported(mq, n, block, 1, p.scr_dy) && fq_cols2_supported(mq, k, block, 1, p.scr_x)) {
+    // every rotation pass of the backward in one launch (or two, when the dY rows are long):
+    // the passes overlap on the device, then the two products
+    const bool rows_in = fq_batch_rows_ok(nq);
+    if (rows_in) {
+      clear_scratch();
+    } else {
+      rows_pass();
       clear_scratch();
     }
     if (s == HALO_OK)
       s = from_hip(launch_fq_batch(rows_in ? &rows : nullptr, cw, scr_w, cdy, scr_dy, cx, scr_x,
                                    qg, qw, st));
-    if (s == HALO_OK)
-      s = gemm_any(qdy, grad_q_type, n, sdy, qwt, q_type, n, swt, m, k, n, dx, io_type, k, st);
-    if (s == HALO_OK)
-      s = gemm_any(qdyt, grad_q_type, m, sdyt, qxt, q_type, m, sxt, n, k, m, dw, io_type, k, st);
-    return s;
-  }
-  if (dx) {  // dX[m x k] = dY W: contraction over n
-    void* qdy = base + p.off[0];
-    float* sdy = reinterpret_cast<float*>(base + p.off[1]);
-    void* qwt = base + p.off[2];
-    float* swt = reinterpret_cast<float*>(base + p.off[3]);
-    if (fq_rows2_supported(n, block)) {
-      FqPair pp{};
-      pp.p0 = make_fq(dy, m, n, n, HALO_ALONG_ROWS, block, grad_q_type, qdy, n, sdy);
-      if (zero_pending) {
-        pp.zero = reinterpret_cast<uint32_t*>(scr);
-        pp.nzero = (int64_t)(p.scratch_bytes / 4);
-        zero_pending = false;
+  } else {
+    if (dx) rows_pass();
+    clear_scratch();
+    if (dx) cols_pass(cw, q_type, scr_w, p.scr_w);
+    if (dw) {
+      const bool c1 = fq_cols2_supported(mq, n, block, inb, p.scr_dy);
+      const bool c2 = fq_cols2_supported(mq, k, block, inb, p.scr_x);
+      if (s == HALO_OK && c1 && c2 && grad_q_type == q_type && cdy.sr == cx.sr) {
+        // dY and X columns in one launch
+        s = from_hip(launch_fq_cols2_pair(cdy, scr_dy, &cx, scr_x, qt_index(q_type), 1, st));
+      } else {
+        cols_pass(cdy, grad_q_type, scr_dy, p.scr_dy);
+        cols_pass(cx, q_type, scr_x, p.scr_x);
       }
-      s = from_hip(launch_fq_rows2_pair(pp, inb, qt_index(grad_q_type), st));
-    } else {
-      s = run_fq(dy, io_type, m, n, n, HALO_ALONG_ROWS, block, grad_q_type, qdy, n, sdy, nullptr,
-                 0, st);
     }
-    clear_scratch();
-    cols_pass(w, n, k, q_type, qwt, swt, scr_w, p.scr_w);
-    if (s == HALO_OK)
-      s = gemm_any(qdy, grad_q_type, n, sdy, qwt, q_type, n, swt, m, k, n, dx, io_type, k, st);
   }
-  if (s == HALO_OK && dw) {  // dW[n x k] = dY^T X: contraction over m
-    void* qdyt = base + p.off[4];
-    float* sdyt = reinterpret_cast<float*>(base + p.off[5]);
-    void* qxt = base + p.off[6];
-    float* sxt = reinterpret_cast<float*>(base + p.off[7]);
-    clear_scratch();
-    const bool c1 = fq_cols2_supported(m, n, block, inb, p.scr_dy);
-    const bool c2 = fq_cols2_supported(m, k, block, inb, p.scr_x);
-    if (s == HALO_OK && c1 && c2 && grad_q_type == q_type) {  // dY and X columns in one launch
-      const FqArgs a0 = make_fq(dy, m, n, n, HALO_ALONG_COLS, block, grad_q_type, qdyt, m, sdyt);
-      const FqArgs a1 = make_fq(x, m, k, k, HALO_ALONG_COLS, block, q_type, qxt, m, sxt);
-      s = from_hip(launch_fq_cols2_pair(a0, scr_dy, &a1, scr_x, qt_index(q_type), 1, st));
-    } else {
-      cols_pass(dy, m, n, grad_q_type, qdyt, sdyt, scr_dy, p.scr_dy);
-      cols_pass(x, m, k, q_type, qxt, sxt, scr_x, p.scr_x);
-    }
-    if (s == HALO_OK)
-      s = gemm_any(qdyt, grad_q_type, m, sdyt, qxt, q_type, m, sxt, n, k, m, dw, io_type, k, st);
-  }
+  if (s == HALO_OK && dx)
+    s = gemm_any(qdy, grad_q_type, nq, sdy, qwt, q_type, nq, swt, m, k, nq, dx, io_type, k, st);
+  if (s == HALO_OK && dw)
+    s = gemm_any(qdyt, grad_q_type, mq, sdyt, qxt, q_type, mq, sxt, n, k, mq, dw, io_type, k, st);
   return s;
+}
+
+halo_status halo_linear_bwd(const void* dy, const void* x, const void* w, halo_dtype io_type,
+                            int64_t m, int64_t n, int64_t k, int32_t block, halo_dtype q_type,
+                            halo_dtype grad_q_type, void* dx, void* dw, void* ws,
+                            size_t ws_bytes, void* stream) {
+  return halo_linear_bwd_ex(dy, x, w, io_type, m, n, k, block, q_type, grad_q_type, dx, dw,
+                            nullptr, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

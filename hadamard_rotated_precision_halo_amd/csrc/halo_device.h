@@ -117,6 +117,88 @@ __device__ __forceinline__ uint32_t fp8_pair(float a, float b) {
     return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false) & 0xffffu;
 }
 
+// ---------------------------------------------------------------------------
+// randomised transform and stochastic rounding
+// ---------------------------------------------------------------------------
+
+// Signs of the randomised transform H D for the 8 consecutive elements starting at position
+// pos (a multiple of 8) of a vector: bit i of the packed sign stream negates element i.
+__device__ __forceinline__ void apply_signs8(float* v, const uint32_t* signs, int64_t pos) {
+  const uint32_t b = signs[pos >> 5] >> (pos & 31);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = __uint_as_float(__float_as_uint(v[e]) ^ (((b >> e) & 1u) << 31));
+}
+
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3",
+// SC'11): ten rounds, each multiplying counter words 0 and 2 by the Philox constants and
+// forming (hi(c2 m1) ^ c1 ^ k0, lo(c2 m1), hi(c0 m0) ^ c3 ^ k1, lo(c0 m0)); the key advances
+// by the Weyl increments between rounds.
+__device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                               uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
+    const uint32_t lo2 = 0xCD9E8D57u * c2, hi2 = __umulhi(0xCD9E8D57u, c2);
+    const uint32_t n0 = hi2 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo2;
+    c2 = n2;
+    c3 = lo0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return make_uint4(c0, c1, c2, c3);
+}
+
+// Chunk of 8 elements at position pos (a multiple of 8) of the vector whose element 0 is at
+// v0: zeros at and past in_len (the padding, never read), then the transform's signs.
+template <typename T>
+__device__ __forceinline__ void load8_vec(const T* v0, int64_t pos, int64_t in_len,
+                                          const uint32_t* signs, float* o) {
+  if (pos < in_len) {
+    load8<T>(v0 + pos, o);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = 0.f;
+  }
+  if (signs) apply_signs8(o, signs, pos);
+}
+
+// The 24-bit uniforms w (u = w / 2^24) of positions pos .. pos + 7 (pos a multiple of 8) of
+// vector vec: word p % 4 of Philox4x32-10 at counter (p / 4, vec, c2, c3), top 24 bits.
+__device__ __forceinline__ void sr_words8(int64_t vec, int64_t pos, uint32_t k0, uint32_t k1,
+                                          uint32_t c2, uint32_t c3, uint32_t* w) {
+  const uint32_t c0 = (uint32_t)(pos >> 2), c1 = (uint32_t)vec;
+  const uint4 r0 = philox4x32_10(c0, c1, c2, c3, k0, k1);
+  const uint4 r1 = philox4x32_10(c0 + 1u, c1, c2, c3, k0, k1);
+  w[0] = r0.x >> 8; w[1] = r0.y >> 8; w[2] = r0.z >> 8; w[3] = r0.w >> 8;
+  w[4] = r1.x >> 8; w[5] = r1.y >> 8; w[6] = r1.z >> 8; w[7] = r1.w >> 8;
+}
+
+// Stochastic rounding of t (|t| <= qmax after the clamp; an exact zero already +0) to the grid
+// of the code type: the grid point below t plus one step when w / 2^24 is below the fraction
+// of the way to the next point.  QT 0: INT8 (step 1); 1: E4M3, 2: E5M2 (step = the quantum
+// of |t|'s binade, the subnormal quantum below the smallest normal).  Every step is exact in
+// fp32 (the steps are powers of two) except the fraction of a negative t above -2^-24, which
+// rounds to 1.  The result is a grid value; a zero result is +0.
+template <int QT>
+__device__ __forceinline__ float sr_value(float t, uint32_t w, float qmax) {
+  t = __builtin_fminf(__builtin_fmaxf(t, -qmax), qmax);
+  float s = 1.f, inv = 1.f;
+  if constexpr (QT != 0) {
+    constexpr uint32_t MB = QT == 1 ? 3u : 2u;         // mantissa bits
+    constexpr uint32_t EMINB = QT == 1 ? 121u : 113u;  // fp32 biased exponent of the min normal
+    uint32_t e = (__float_as_uint(t) >> 23) & 0xffu;
+    e = e < EMINB ? EMINB : e;
+    s = __uint_as_float((e - MB) << 23);
+    inv = __uint_as_float((254u - e + MB) << 23);
+  }
+  const float r = t * inv;
+  const float fl = floorf(r);
+  const float up = (float)w < (r - fl) * 16777216.0f ? 1.f : 0.f;
+  return (fl + up) * s;
+}
+
 // fp32 -> bf16 bits, round to nearest even (finite inputs).
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);

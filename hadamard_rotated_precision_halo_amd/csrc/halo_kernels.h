@@ -20,6 +20,12 @@ struct FqArgs {
   float qmax;          // 127, 448, 57344
   float denom;         // fl32(qmax * sqrt(block)): scale = max|b| / denom
   float inv_sqrt_b;    // fl32(1 / sqrt(block)) for the fp32 test mode
+  int64_t in_len;      // input elements per vector (<= len); positions [in_len, len) are the
+                       // zero padding and are not read
+  const uint32_t* signs;  // randomised transform: bit i set negates element i (NULL: none)
+  int sr;                 // 1: stochastic rounding of the codes (code types only)
+  uint32_t key0, key1;    // Philox4x32-10 key
+  uint32_t ctr2, ctr3;    // Philox counter words 2 and 3 (word 0: position / 4, word 1: vector)
 };
 
 // in_bf16: 1 for bf16 input, 0 for fp32.  qt: 0 INT8, 1 E4M3, 2 E5M2, 3 fp32 values.

@@ -44,12 +44,13 @@ typedef enum {
     HALO_OK = 0,
     HALO_ERR_NULL = 1,      /* a required pointer is NULL                                  */
     HALO_ERR_SHAPE = 2,     /* a size is negative, too large, or not a supported multiple  */
-    HALO_ERR_BLOCK = 3,     /* block not a power of two in [1, 4096] or not dividing the   */
-                            /* rotated length                                              */
+    HALO_ERR_BLOCK = 3,     /* block not a power of two in [1, 4096]                       */
     HALO_ERR_DTYPE = 4,     /* unsupported element type or type pair                      */
     HALO_ERR_ALIGN = 5,     /* pointer or leading dimension not 16-byte aligned            */
     HALO_ERR_WORKSPACE = 6, /* workspace NULL or smaller than the size query returns       */
-    HALO_ERR_HIP = 7        /* the HIP runtime refused a launch                            */
+    HALO_ERR_HIP = 7,       /* the HIP runtime refused a launch                            */
+    HALO_ERR_OPTION = 8     /* invalid option: unknown rounding mode, or stochastic        */
+                            /* rounding asked of the fp32 value mode                       */
 } halo_status;
 
 typedef enum {
@@ -72,17 +73,20 @@ typedef enum {
  *
  * Defined by: the blockwise orthonormal Walsh-Hadamard transform of each vector (QWHA page
  * s2.1-s2.2, s3.1) followed by the per-vector absmax quantiser (s2.2), i.e. for a vector v
- * of length L:  y = v (I_{L/block} (x) H_block) / sqrt(block),  a = max|y|,
- * code = round_to_nearest_even(y * qmax / a),  scale = a / qmax.
+ * of length L, padded with zeros to Lp = L rounded up to a multiple of block (QWHA page s5:
+ * lengths padded with zeros for the transform):
+ *   y = v (I_{Lp/block} (x) H_block) / sqrt(block),  a = max|y|,
+ *   code = round_to_nearest_even(y * qmax / a),  scale = a / qmax.
+ * Every one of the Lp rotated positions gets a code (the last block mixes data and zeros).
  *
  *   x_type   HALO_F32 or HALO_BF16.
- *   axis     HALO_ALONG_ROWS: vector r = x[r, :], L = cols; q is [rows x cols] (ldq >= cols)
- *                             and scale has `rows` entries.
- *            HALO_ALONG_COLS: vector c = x[:, c], L = rows; q is [cols x rows] (ldq >= rows),
+ *   axis     HALO_ALONG_ROWS: vector r = x[r, :], L = cols (a multiple of 8); q is [rows x Lp]
+ *                             (ldq >= Lp) and scale has `rows` entries.
+ *            HALO_ALONG_COLS: vector c = x[:, c], L = rows; q is [cols x Lp] (ldq >= Lp),
  *                             i.e. the codes of column c form row c of q; scale has `cols`
  *                             entries.  cols must be a multiple of 8.
- *   block    power of two in [1, 4096] dividing L; L must be a multiple of 8.  block 1 is the
- *            identity (plain per-vector absmax quantisation).
+ *   block    power of two in [1, 4096]; Lp must be a multiple of 8 (so L too when block < 8).
+ *            block 1 is the identity (plain per-vector absmax quantisation).
  *   q_type   HALO_I8, HALO_E4M3, HALO_E5M2: 1-byte codes.
  *            HALO_F32: test mode, q receives the rotated values themselves (fp32) and scale
  *            the absmax of each rotated vector.
@@ -93,7 +97,7 @@ typedef enum {
  *            input once; with ws NULL (or too small) the pass reads its input twice and gives
  *            the same codes and scales.  Calls that share one scratch must be ordered on one
  *            stream.
- * Rows-axis vectors are limited to L <= 16384 elements (one workgroup holds a whole row).
+ * Rows-axis vectors are limited to Lp <= 16384 elements (one workgroup holds a whole row).
  * Codes are decided in fp32: m = qmax / max|b| with b the un-normalised butterfly output and
  * code = round(b * m); the 1/sqrt(block) factor cancels between b and max|b|.
  */
@@ -138,8 +142,9 @@ halo_status halo_gemm_fp8(const void* a, halo_dtype a_type, int64_t lda, const f
 
 /*
  * Workspace bytes the layer calls need (codes + scales of every quantised operand, each
- * region 256-byte aligned).  backward = 0 for halo_linear_fwd, 1 for halo_linear_bwd.
- * Returns 0 for invalid sizes or types.
+ * region 256-byte aligned), for every block size (the largest over blocks 1 .. 4096; the
+ * block decides the padded contraction lengths).  backward = 0 for halo_linear_fwd, 1 for
+ * halo_linear_bwd.  Returns 0 for invalid sizes or types.
  */
 size_t halo_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, halo_dtype q_type,
                                    int backward);
@@ -151,8 +156,12 @@ size_t halo_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, halo_dtype q
  *   io_type  HALO_F32 or HALO_BF16 for x and w (dense, leading dimension k).
  *   q_type   HALO_I8 or HALO_E4M3.
  *   y_type   HALO_F32 or HALO_BF16 (dense, leading dimension n).
- *   ws       caller workspace of at least halo_linear_workspace_bytes(m, n, k, q_type, 0).
- * k must be a multiple of 32 (and of block); block as for halo_fwht_quant.
+ *   ws       caller workspace of at least halo_linear_workspace_bytes(m, n, k, q_type, 0)
+ *            (or halo_linear_workspace_bytes_ex(m, n, k, block, q_type, 0)).
+ * k must be a multiple of 8 and n a multiple of 16 bytes of y_type; block as for
+ * halo_fwht_quant.  When block does not divide k, X and W are padded with zeros along k (QWHA
+ * page s5) and the product runs over all padded positions, which equals the product of the
+ * padded operands.  The padded k (rounded up to a multiple of block and of 32) is at most 16384.
  */
 halo_status halo_linear_fwd(const void* x, const void* w, halo_dtype io_type, int64_t m,
                             int64_t n, int64_t k, int32_t block, halo_dtype q_type, void* y,
@@ -169,12 +178,95 @@ halo_status halo_linear_fwd(const void* x, const void* w, halo_dtype io_type, in
  *   grad_q_type  codes of dY: HALO_I8 (with q_type HALO_I8) or HALO_E5M2 / HALO_E4M3 (with
  *                q_type HALO_E4M3).
  *   dx, dw       outputs; either may be NULL to skip that product.
- * m, n and k must be multiples of 32 (and of block); block as for halo_fwht_quant.
+ *   ws           at least halo_linear_workspace_bytes(m, n, k, q_type, 1) bytes.
+ * n and k must be multiples of 8, m >= 1; block as for halo_fwht_quant.  Contraction
+ * dimensions that block does not divide are zero-padded as in halo_linear_fwd; the padded n
+ * is at most 16384 when dx is computed.
  */
 halo_status halo_linear_bwd(const void* dy, const void* x, const void* w, halo_dtype io_type,
                             int64_t m, int64_t n, int64_t k, int32_t block, halo_dtype q_type,
                             halo_dtype grad_q_type, void* dx, void* dw, void* ws,
                             size_t ws_bytes, void* stream);
+
+/*
+ * Options of the extended rotation calls.
+ *
+ * Randomised transform H D ("企业官网建设流程全解析", a HALO overview, s4.2: every node
+ * initialises the Hadamard matrix from one shared random seed): the vector is multiplied by
+ * a diagonal of signs before the transform, y = (I (x) H_block) D v / sqrt(block).  `signs`
+ * is a device array of ceil(Lp / 32) 32-bit words, bit (i mod 32) of word i / 32 set meaning
+ * d_i = -1; all callers that must agree (for instance every rank of a job) draw it from the
+ * same seed.  NULL means D = I.  16-byte aligned.
+ *
+ * Stochastic rounding (QWHA page s5: round down, then up with probability equal to the
+ * fraction, to remove the quantiser's bias), for the code types: t = y * qmax / a is clamped
+ * to [-qmax, qmax]; with s the grid step at t (1 for INT8; for FP8 the quantum of |t|'s
+ * binade, the subnormal quantum below the smallest normal) and r = t / s, the code is the
+ * grid value s (floor(r) + [u < r - floor(r)]) (zero takes the +0 code).  The uniform of the
+ * element at position p of vector v (its row index for the rows axis, its column index for
+ * the columns axis) is u = (w >> 8) / 2^24 with w word p mod 4 of Philox4x32-10 (Salmon et
+ * al., "Parallel random numbers: as easy as 1, 2, 3", SC'11) at counter (p / 4, v,
+ * counter[0], counter[1]) and key (seed[0], seed[1]).  The decision is taken in fp32 from
+ * t = fl32(b * m), b the un-normalised butterfly output and m = fl32(qmax / max|b|).  Draw a
+ * fresh counter (or seed) per call for independent rounding.
+ */
+typedef enum {
+    HALO_ROUND_NEAREST_EVEN = 0,
+    HALO_ROUND_STOCHASTIC = 1
+} halo_rounding;
+
+typedef struct {
+    const uint32_t* signs; /* sign bits of D along the rotated dimension, or NULL         */
+    int32_t rounding;      /* halo_rounding                                               */
+    uint32_t seed[2];      /* Philox key (stochastic rounding)                            */
+    uint32_t counter[2];   /* Philox counter words 2 and 3 (stochastic rounding)          */
+} halo_quant_opts;
+
+/*
+ * halo_fwht_quant with options (NULL opts = halo_fwht_quant).  Invalid options give
+ * HALO_ERR_OPTION (rounding not a halo_rounding, or stochastic with q_type HALO_F32) or
+ * HALO_ERR_ALIGN (signs not 16-byte aligned).
+ */
+halo_status halo_fwht_quant_ex(const void* x, halo_dtype x_type, int64_t rows, int64_t cols,
+                               int64_t ldx, halo_axis axis, int32_t block, halo_dtype q_type,
+                               void* q, int64_t ldq, float* scale, const halo_quant_opts* opts,
+                               void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Options of the extended layer calls: one sign array per contraction dimension (each covers
+ * that dimension's padded length; NULL = plain transform) and the rounding of the dY codes.
+ *   signs_k  D along k: the forward product (rows of X and of W).
+ *   signs_n  D along n: the dX product (rows of dY, columns of W).
+ *   signs_m  D along m: the dW product (columns of dY and of X).
+ *   grad_rounding, seed, counter: rounding of the dY codes, as in halo_quant_opts; the rows
+ *            of dY draw at counter words (counter[0], counter[1]) and its columns at
+ *            (counter[0], counter[1] ^ 0x80000000).  X and W are always rounded to nearest.
+ */
+typedef struct {
+    const uint32_t* signs_k;
+    const uint32_t* signs_n;
+    const uint32_t* signs_m;
+    int32_t grad_rounding;
+    uint32_t seed[2];
+    uint32_t counter[2];
+} halo_linear_opts;
+
+/* Workspace bytes of the layer calls for one block size (exact; the block decides the padded
+ * contraction lengths).  Returns 0 for invalid arguments. */
+size_t halo_linear_workspace_bytes_ex(int64_t m, int64_t n, int64_t k, int32_t block,
+                                      halo_dtype q_type, int backward);
+
+/* halo_linear_fwd / halo_linear_bwd with options (NULL opts = the plain calls).  Invalid
+ * options give HALO_ERR_OPTION, unaligned sign arrays HALO_ERR_ALIGN. */
+halo_status halo_linear_fwd_ex(const void* x, const void* w, halo_dtype io_type, int64_t m,
+                               int64_t n, int64_t k, int32_t block, halo_dtype q_type, void* y,
+                               halo_dtype y_type, const halo_linear_opts* opts, void* ws,
+                               size_t ws_bytes, void* stream);
+halo_status halo_linear_bwd_ex(const void* dy, const void* x, const void* w, halo_dtype io_type,
+                               int64_t m, int64_t n, int64_t k, int32_t block, halo_dtype q_type,
+                               halo_dtype grad_q_type, void* dx, void* dw,
+                               const halo_linear_opts* opts, void* ws, size_t ws_bytes,
+                               void* stream);
 
 /* Static description of a status code. */
 const char* halo_status_str(halo_status s);

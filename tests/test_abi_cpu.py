@@ -13,7 +13,7 @@ HEADER = os.path.join(ROOT, "include", "halo.h")
 
 import hadamard_rotated_precision_halo_amd as H  # noqa: E402
 
-OK, NULL, SHAPE, BLOCK, DTYPE, ALIGN, WORKSPACE, HIP = range(8)
+OK, NULL, SHAPE, BLOCK, DTYPE, ALIGN, WORKSPACE, HIP, OPTION = range(9)
 F32, BF16, I8, E4M3, E5M2, I32 = range(6)
 
 P = ctypes.c_void_p(0x10000)    # 16-byte aligned fake device pointer
@@ -55,7 +55,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_status_strings(L):
-    for s in range(8):
+    for s in range(9):
         assert L.halo_status_str(s)
     assert L.halo_status_str(0) == b"ok"
 
@@ -75,13 +75,15 @@ def test_fwht_quant_validation(L):
     assert fq(L, block=3) == BLOCK
     assert fq(L, block=0) == BLOCK
     assert fq(L, block=8192, cols=8192, ldx=8192, ldq=8192) == BLOCK
-    assert fq(L, block=512) == BLOCK             # 512 does not divide 256
-    assert fq(L, axis=1, block=128) == BLOCK     # cols axis rotates the 64 rows
+    assert fq(L, block=512) == SHAPE             # 256 padded to 512: codes need ldq >= 512
+    assert fq(L, axis=1, block=128, ldq=64) == SHAPE  # 64 rows padded to 128 codes per column
     assert fq(L, rows=-1) == SHAPE
     assert fq(L, ldx=128) == SHAPE
     assert fq(L, ldq=128) == SHAPE
     assert fq(L, axis=7) == SHAPE
     assert fq(L, block=4, cols=12, ldx=16, ldq=16) == SHAPE          # length not a multiple of 8
+    assert fq(L, axis=1, block=4, rows=12, ldq=16) == SHAPE  # padded length 12 not a multiple of 8
+    assert fq(L, block=64, cols=200, ldx=200, ldq=200) == SHAPE      # 200 padded to 256 codes
     assert fq(L, axis=1, block=16, rows=64, cols=12, ldx=16, ldq=64) == SHAPE  # 12 columns
     big = 1 << 20
     assert fq(L, cols=big, ldx=big, ldq=big, block=256) == SHAPE     # beyond the rows kernel
@@ -90,6 +92,26 @@ def test_fwht_quant_validation(L):
     assert fq(L, ldx=260, cols=256) == ALIGN  # 520 bytes per bf16 row
     assert fq(L, ldq=260) == ALIGN
     assert fq(L, ws=BAD, wsb=4096) == ALIGN
+
+
+def fqx(L, opts, **kw):
+    a = dict(x=P, xt=BF16, rows=64, cols=256, ldx=256, axis=0, block=256, qt=I8, q=P2, ldq=256,
+             scale=P3)
+    a.update(kw)
+    return L.halo_fwht_quant_ex(a["x"], a["xt"], a["rows"], a["cols"], a["ldx"], a["axis"],
+                                a["block"], a["qt"], a["q"], a["ldq"], a["scale"],
+                                ctypes.byref(opts) if opts is not None else None, None, 0, None)
+
+
+def test_fwht_quant_ex_validation(L):
+    def opts(signs=None, rounding=0):
+        return H.QuantOpts(signs, rounding, (ctypes.c_uint32 * 2)(1, 2), (ctypes.c_uint32 * 2)(3, 4))
+    assert fqx(L, opts(rounding=2)) == OPTION
+    assert fqx(L, opts(rounding=-1)) == OPTION
+    assert fqx(L, opts(rounding=1), qt=F32, ldq=256) == OPTION   # values are not rounded
+    assert fqx(L, opts(signs=BAD.value)) == ALIGN
+    assert fqx(L, opts(), x=NUL) == NULL                           # the plain checks still run
+    assert fqx(L, opts(rounding=1), block=3) == BLOCK
 
 
 def test_fwht_quant_workspace_bytes(L):
@@ -144,10 +166,21 @@ def test_gemm_fp8_validation(L):
 
 def test_workspace_bytes(L):
     r = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    pad = lambda d, b: -(-d // max(b, 32)) * max(b, 32)  # noqa: E731  contraction length
     m, n, k = 300, 520, 1024
-    assert L.halo_linear_workspace_bytes(m, n, k, I8, 0) == r(m * k) + r(4 * m) + r(n * k) + r(4 * n)
-    want = (r(m * n) + r(4 * m) + r(k * n) + r(4 * k) + r(n * m) + r(4 * n) + r(k * m) + r(4 * k))
-    assert L.halo_linear_workspace_bytes(m, n, k, E4M3, 1) == want
+    X = L.halo_linear_workspace_bytes_ex
+    for b in (1, 64, 256):
+        kq = pad(k, b)
+        assert X(m, n, k, b, I8, 0) == r(m * kq) + r(4 * m) + r(n * kq) + r(4 * n)
+    nq, mq = pad(n, 256), pad(m, 256)  # 768, 512
+    want = (r(m * nq) + r(4 * m) + r(k * nq) + r(4 * k) + r(n * mq) + r(4 * n) + r(k * mq)
+            + r(4 * k))
+    assert X(m, n, k, 256, E4M3, 1) == want
+    # the block-free query covers every block: the largest padding (block 4096) decides here
+    assert L.halo_linear_workspace_bytes(m, n, k, I8, 0) == X(m, n, k, 4096, I8, 0)
+    assert L.halo_linear_workspace_bytes(m, n, k, I8, 0) == max(X(m, n, k, 1 << i, I8, 0)
+                                                              for i in range(13))
+    assert X(m, n, k, 3, I8, 0) == 0
     # 4096^3 backward: the code matrices plus the columns passes' shared scratch
     big = 4096
     codes = 4 * (r(big * big) + r(4 * big))
@@ -170,8 +203,8 @@ def test_linear_fwd_validation(L):
     assert fwd(L, io=I8) == DTYPE
     assert fwd(L, qt=E5M2) == DTYPE
     assert fwd(L, yt=I32) == DTYPE
-    assert fwd(L, k=240) == SHAPE
-    assert fwd(L, block=512) == BLOCK
+    assert fwd(L, k=244) == SHAPE              # not a multiple of 8
+    assert fwd(L, k=20000) == SHAPE            # padded k beyond the rows kernel
     assert fwd(L, block=6) == BLOCK
     assert fwd(L, ws=NUL) == WORKSPACE
     assert fwd(L, wsb=1000) == WORKSPACE
@@ -190,9 +223,29 @@ def test_linear_bwd_validation(L):
     assert bwd(L, gqt=E5M2) == DTYPE          # INT8 operands need INT8 gradients
     assert bwd(L, qt=E4M3, gqt=I8) == DTYPE
     assert bwd(L, qt=E5M2, gqt=E5M2) == DTYPE
-    assert bwd(L, m=240) == SHAPE
+    assert bwd(L, n=244) == SHAPE              # not a multiple of 8
+    assert bwd(L, k=244) == SHAPE
     assert bwd(L, m=0) == SHAPE
-    assert bwd(L, block=512) == BLOCK
-    assert bwd(L, m=384, block=256) == BLOCK  # 256 does not divide 384 tokens
+    assert bwd(L, block=6) == BLOCK
     assert bwd(L, wsb=10) == WORKSPACE
     assert bwd(L, dx=BAD) == ALIGN
+
+
+def test_linear_ex_validation(L):
+    def lopts(rounding=0, sk=None, sn=None, sm=None):
+        return H.LinearOpts(sk, sn, sm, rounding, (ctypes.c_uint32 * 2)(1, 2),
+                            (ctypes.c_uint32 * 2)(3, 4))
+    m = n = k = 256
+    wsf = L.halo_linear_workspace_bytes_ex(m, n, k, 128, I8, 0)
+    wsb = L.halo_linear_workspace_bytes_ex(m, n, k, 128, I8, 1)
+    f = lambda o: L.halo_linear_fwd_ex(P, P2, BF16, m, n, k, 128, I8, P3, BF16,  # noqa: E731
+                                       ctypes.byref(o), P, wsf, None)
+    b = lambda o: L.halo_linear_bwd_ex(P, P2, P3, BF16, m, n, k, 128, I8, I8, P, P2,  # noqa: E731
+                                       ctypes.byref(o), P3, wsb, None)
+    assert f(lopts(rounding=5)) == OPTION
+    assert f(lopts(sk=BAD.value)) == ALIGN
+    assert b(lopts(rounding=5)) == OPTION
+    assert b(lopts(sn=BAD.value)) == ALIGN
+    assert b(lopts(sm=BAD.value)) == ALIGN
+    assert L.halo_linear_bwd_ex(P, P2, P3, BF16, m, n, k, 128, I8, I8, P, P2,
+                                ctypes.byref(lopts()), P3, wsb - 256, None) == WORKSPACE
