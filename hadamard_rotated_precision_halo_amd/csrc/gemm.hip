@@ -112,8 +112,16 @@ __device__ __forceinline__ void store4(void* c, int64_t ldc, int64_t row, int64_
 // k is not a multiple of the slab, or when the FP8 loop pads one extra slab).
 // WN: waves along N (2: four waves of 128 x 128, one per SIMD; 4: eight waves of 128 x 64, two
 // per SIMD, so one wave's stalls at the barrier or on loads are covered by the other's MFMAs).
+// One launch runs up to two products of the same kind and output type (gp.g[1] when
+// blockIdx.x >= gp.split): the second product's tiles fill the compute units as the first's
+// finish, so its operand loads overlap the first's output stores.
+struct GemmPair {
+  GemmArgs g[2];
+  int64_t split;  // workgroups of the first product
+};
+
 template <int KIND, int AF, int BF, int OUT, bool MASK, int BK, int WN>
-__global__ __launch_bounds__(128 * WN, 1) void gemm_kernel(GemmArgs g) {
+__global__ __launch_bounds__(128 * WN, 1) void gemm_kernel(GemmPair gp) {
   using SL = Slab<BK>;
   constexpr int NW = 2 * WN, NT = 64 * NW;         // waves, threads
   constexpr int TN = BN / WN;                      // output columns per wave
@@ -125,10 +133,12 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_kernel(GemmArgs g) {
   float* s_sa = reinterpret_cast<float*>(smem + RING_BYTES);
   float* s_sb = s_sa + 256;
 
-  // ---- tile of this workgroup -------------------------------------------------------
+  // ---- product and tile of this workgroup ---------------------------------------------
+  const bool second = (int64_t)blockIdx.x >= gp.split;
+  const GemmArgs g = second ? gp.g[1] : gp.g[0];
   const int tiles_m = (int)((g.m + BM - 1) / BM), tiles_n = (int)((g.n + BN - 1) / BN);
   const int T = tiles_m * tiles_n;
-  const int bid = blockIdx.x;
+  const int bid = (int)(blockIdx.x - (second ? gp.split : 0));
   const int q8 = T / 8, r8 = T % 8, xcd = bid % 8, slot = bid / 8;
   const int tile = xcd < r8 ? xcd * (q8 + 1) + slot : r8 * (q8 + 1) + (xcd - r8) * q8 + slot;
   constexpr int GROUP_M = 4;
@@ -404,7 +414,7 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_kernel(GemmArgs g) {
 }
 
 template <int KIND, int AF, int BF, int OUT, bool MASK, int BK>
-static hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
+static hipError_t launch_cfg(const GemmArgs& g0, const GemmArgs* g1, hipStream_t st) {
   constexpr int WN = HALO_GEMM_WN;
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
@@ -414,10 +424,21 @@ static hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
         hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
   });
   if (attr_err != hipSuccess) return attr_err;
-  const int64_t tiles = ((g.m + BM - 1) / BM) * ((g.n + BN - 1) / BN);
-  if (tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_kernel<KIND, AF, BF, OUT, MASK, BK, WN>), dim3((unsigned)tiles),
-                     dim3(128 * WN), LDS_BYTES, st, g);
+  GemmPair gp{};
+  gp.g[0] = g0;
+  gp.g[1] = g1 ? *g1 : g0;
+  gp.split = ((g0.m + BM - 1) / BM) * ((g0.n + BN - 1) / BN);
+  const int64_t t1 = g1 ? ((g1->m + BM - 1) / BM) * ((g1->n + BN - 1) / BN) : 0;
+  if (gp.split == 0) {  // keep the first slot filled: the kernel picks by workgroup index
+    gp.g[0] = gp.g[1];
+    gp.split = t1;
+    if (t1 == 0) return hipSuccess;
+    hipLaunchKernelGGL((gemm_kernel<KIND, AF, BF, OUT, MASK, BK, WN>), dim3((unsigned)t1),
+                       dim3(128 * WN), LDS_BYTES, st, gp);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((gemm_kernel<KIND, AF, BF, OUT, MASK, BK, WN>),
+                     dim3((unsigned)(gp.split + t1)), dim3(128 * WN), LDS_BYTES, st, gp);
   return hipGetLastError();
 }
 
@@ -425,30 +446,36 @@ static hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
 #define HALO_GEMM_BK 128
 #endif
 
-template <int KIND, int AF, int BF, int OUT>
-static hipError_t launch_t(const GemmArgs& g, hipStream_t st) {
-  constexpr int BK = HALO_GEMM_BK;
+template <int KIND, int BK>
+static bool needs_mask(const GemmArgs& g) {
   constexpr int KS = BK / (KIND == 0 ? 32 : 64);
   const int64_t nk = (g.k + BK - 1) / BK;
-  const bool mask = (g.k % BK) != 0 || (KS == 1 && (nk & 1));
-  return mask ? launch_cfg<KIND, AF, BF, OUT, true, BK>(g, st)
-              : launch_cfg<KIND, AF, BF, OUT, false, BK>(g, st);
+  return (g.k % BK) != 0 || (KS == 1 && (nk & 1));
 }
 
-hipError_t launch_gemm(const GemmArgs& g, int kind, int afmt, int bfmt, int out, hipStream_t st) {
+template <int KIND, int AF, int BF, int OUT>
+static hipError_t launch_t(const GemmArgs& g, const GemmArgs* g1, hipStream_t st) {
+  constexpr int BK = HALO_GEMM_BK;
+  const bool mask = needs_mask<KIND, BK>(g) || (g1 && needs_mask<KIND, BK>(*g1));
+  return mask ? launch_cfg<KIND, AF, BF, OUT, true, BK>(g, g1, st)
+              : launch_cfg<KIND, AF, BF, OUT, false, BK>(g, g1, st);
+}
+
+hipError_t launch_gemm_pair(const GemmArgs& g, const GemmArgs* g1, int kind, int afmt, int bfmt,
+                            int out, hipStream_t st) {
   if (kind == 0) {
     switch (out) {
-      case 0: return launch_t<0, 0, 0, 0>(g, st);
-      case 1: return launch_t<0, 0, 0, 1>(g, st);
-      case 2: return launch_t<0, 0, 0, 2>(g, st);
+      case 0: return launch_t<0, 0, 0, 0>(g, g1, st);
+      case 1: return launch_t<0, 0, 0, 1>(g, g1, st);
+      case 2: return launch_t<0, 0, 0, 2>(g, g1, st);
     }
     return hipErrorInvalidValue;
   }
   const int sel = afmt * 2 + bfmt;
 #define HALO_FP8_CASE(AFv, BFv)                                       \
   if (sel == AFv * 2 + BFv) {                                         \
-    if (out == 1) return launch_t<1, AFv, BFv, 1>(g, st);             \
-    if (out == 2) return launch_t<1, AFv, BFv, 2>(g, st);             \
+    if (out == 1) return launch_t<1, AFv, BFv, 1>(g, g1, st);         \
+    if (out == 2) return launch_t<1, AFv, BFv, 2>(g, g1, st);         \
   }
   HALO_FP8_CASE(0, 0)
   HALO_FP8_CASE(0, 1)
@@ -456,6 +483,10 @@ hipError_t launch_gemm(const GemmArgs& g, int kind, int afmt, int bfmt, int out,
   HALO_FP8_CASE(1, 1)
 #undef HALO_FP8_CASE
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm(const GemmArgs& g, int kind, int afmt, int bfmt, int out, hipStream_t st) {
+  return launch_gemm_pair(g, nullptr, kind, afmt, bfmt, out, st);
 }
 
 }  // namespace halo

@@ -516,6 +516,17 @@ halo_status halo_linear_bwd_ex(const void* dy, const void* x, const void* w, hal
       }
     }
   }
+  if (s == HALO_OK && dx && dw) {  // both products in one launch
+    const GemmArgs gx{qdy, nq, qwt, nq, sdy, swt, dx, k, m, k, nq};
+    const GemmArgs gw{qdyt, mq, qxt, mq, sdyt, sxt, dw, k, n, k, mq};
+    const int out = io_type == HALO_F32 ? 1 : 2;
+    if (grad_q_type == HALO_I8)
+      s = from_hip(launch_gemm_pair(gx, &gw, 0, 0, 0, out, st));
+    else
+      s = from_hip(launch_gemm_pair(gx, &gw, 1, gemm_kind_fmt(grad_q_type), gemm_kind_fmt(q_type),
+                                    out, st));
+    return s;
+  }
   if (s == HALO_OK && dx)
     s = gemm_any(qdy, grad_q_type, nq, sdy, qwt, q_type, nq, swt, m, k, nq, dx, io_type, k, st);
   if (s == HALO_OK && dw)

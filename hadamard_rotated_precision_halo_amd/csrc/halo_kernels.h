@@ -89,5 +89,8 @@ struct GemmArgs {
 
 // kind: 0 INT8, 1 FP8.  afmt/bfmt (FP8 only): 0 E4M3, 1 E5M2.  out: 0 int32, 1 fp32, 2 bf16.
 hipError_t launch_gemm(const GemmArgs& g, int kind, int afmt, int bfmt, int out, hipStream_t st);
+// Two products of the same kind, formats and output type in one launch (g1 may be NULL).
+hipError_t launch_gemm_pair(const GemmArgs& g, const GemmArgs* g1, int kind, int afmt, int bfmt,
+                            int out, hipStream_t st);
 
 }  // namespace halo
