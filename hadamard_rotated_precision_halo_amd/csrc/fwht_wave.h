@@ -546,10 +546,12 @@ __device__ __forceinline__ void cols_task(const ColsProb& pr, int64_t ltask, uin
       asm volatile("s_waitcnt vmcnt(0)" ::"v"(seen) : "memory");
       __syncthreads();
       if (t == 0) {
-        __hip_atomic_fetch_add(&arrive[strip], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t before =
+            __hip_atomic_fetch_add(&arrive[strip], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         // the other tasks of this strip are dispatched (workgroups start in index order), so
-        // the count reaches P; the bound only guards against a broken launch
-        for (uint32_t it = 0; it < (1u << 20); ++it) {
+        // the count reaches P; the bound only guards against a broken launch.  The last task
+        // to arrive has seen the full count already and does not poll.
+        for (uint32_t it = 0; before + 1 < (uint32_t)P && it < (1u << 20); ++it) {
           if (__hip_atomic_load(&arrive[strip], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >=
               (uint32_t)P)
             break;

@@ -137,13 +137,13 @@ __device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
                                                uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    const uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
-    const uint32_t lo2 = 0xCD9E8D57u * c2, hi2 = __umulhi(0xCD9E8D57u, c2);
-    const uint32_t n0 = hi2 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    // one 32 x 32 -> 64-bit product each (v_mad_u64_u32 gives both halves at once)
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0, p2 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p2 >> 32) ^ c1 ^ k0, n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
     c0 = n0;
-    c1 = lo2;
+    c1 = (uint32_t)p2;
     c2 = n2;
-    c3 = lo0;
+    c3 = (uint32_t)p0;
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
   }
