@@ -16,8 +16,8 @@ INT8 GEMM (the dominant kernel, MFMA-bound) and the rows / columns rotation pass
 (HBM-bound).  The CPU baseline times the oracle on one full step of the same layer.
 
 Other modes:
-  --kernels-only        launch each hot kernel --kernel-iters times next to a 64 MiB device
-                        copy (the counter calibration); run under rocprofv3.
+  --kernels-only        launch each hot kernel --kernel-iters times next to a 64 MiB
+                        elementwise read + write (the counter calibration); run under rocprofv3.
   --summarize-stats F   turn a rocprofv3 --stats kernel_stats.csv into a text summary.
   --summarize-pmc D1 D2 turn two rocprofv3 --pmc runs of --kernels-only (FETCH_SIZE in D1,
                         WRITE_SIZE in D2) into the per-launch HBM traffic of each kernel.
@@ -38,6 +38,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "HALO linear fwd+bwd effective TOP/s + FWHT-quant GB/s (% roofline), 4096x4096"
 PEAK_INT8_TOPS = 5000.0   # MI355X dense INT8 MFMA, TOP/s
+PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 MFMA, TFLOP/s
 PEAK_HBM_GBS = 8000.0     # MI355X HBM3E, GB/s
 M = N = K = 4096
 BLOCK = 256
@@ -46,7 +47,7 @@ STEP_GOP = 3 * 2 * M * N * K / 1e9
 GEMM_OPS = 2 * M * N * K
 FQ_BYTES = M * K * (2 + 1) + 4 * M          # bf16 in, one code byte out, one fp32 scale/vector
 GEMM_BYTES = 2 * M * K + 2 * M * N + 4 * (M + N)  # both code operands, bf16 output, scales
-COPY_BYTES = 64 << 20                       # calibration copy: 64 MiB read + 64 MiB written
+COPY_BYTES = 64 << 20                       # calibration: 64 MiB read + 64 MiB written
 KERNEL_SOURCES = ["hadamard_rotated_precision_halo_amd/csrc/gemm.hip",
                   "hadamard_rotated_precision_halo_amd/csrc/fwht_quant.hip",
                   "hadamard_rotated_precision_halo_amd/csrc/fwht_wave.h",
@@ -64,9 +65,10 @@ PASSES = {
     "fq_rows_4096": ["halo::fq_rows2_kernel<unsigned short, 256, 0, false>"],
     "fq_cols_4096": ["halo::fq_cols_kernel<unsigned short, 256, 0", "halo::fill_zero_kernel",
                      "halo::finalize_scale_kernel", "halo::fq_cols2_kernel<256, 0, false>"],
+    "gemm_fp8_4096": ["halo::gemm_kernel<1"],
     "fq_rows_opt_4096": ["halo::fq_rows2_kernel<unsigned short, 256, 0, true>"],
     "fq_cols_opt_4096": ["halo::fq_cols2_kernel<256, 0, true>"],
-    "copy_64MiB": ["__amd_rocclr_copyBuffer"],
+    "copy_64MiB": ["neg_kernel"],
 }
 
 
@@ -155,57 +157,94 @@ def make_inputs(torch):
 SEED64 = 0x0123456789ABCDEF  # Philox key of the stochastic-rounding legs
 
 
+def _c_launcher(H, name, arg_sets):
+    """Back-to-back launches through the C entry point `name` with argument lists marshalled
+    once (the benchmark times the kernels, not the binding's per-call Python work)."""
+    fn = getattr(H.lib(), name)
+
+    def run(i):
+        st = fn(*arg_sets[i % len(arg_sets)])
+        if st != 0:
+            raise RuntimeError(f"{name} failed with status {st}")
+    return run
+
+
 def measure_kernels(H, torch, sets, iters, with_copy=False):
     """Per-launch time (ms) of the dominant kernels, in the configuration the step launches
-    them: INT8 GEMM 4096^3 -> bf16, rows pass of X, columns pass of dY (block 256); and the
-    option legs: the rows and columns passes of dY with the randomised transform's signs and
-    stochastic rounding, and a rows pass over rows of 4000 elements zero-padded to 4096."""
+    them: INT8 GEMM 4096^3 -> bf16, rows pass of X, columns pass of dY (block 256); the FP8
+    GEMM 4096^3 (E4M3 codes); and the option legs: the rows and columns passes of dY with the
+    randomised transform's signs and stochastic rounding, and a rows pass over rows of 4000
+    elements zero-padded to 4096.  The calls go straight to the C entry points with their
+    arguments prepared beforehand."""
+    import ctypes
+    P, ld, code = H._ptr, H._ld, H._code
+    st = H._stream(None)
     codes = [H.fwht_quant(X, axis=H.ROWS, block=BLOCK) for (X, _, _) in sets[:2]]
     wcodes = [H.fwht_quant(W, axis=H.ROWS, block=BLOCK) for (_, W, _) in sets[:2]]
+    e4 = torch.float8_e4m3fn
+    f8x = [H.fwht_quant(X, axis=H.ROWS, block=BLOCK, q_dtype=e4) for (X, _, _) in sets[:2]]
+    f8w = [H.fwht_quant(W, axis=H.ROWS, block=BLOCK, q_dtype=e4) for (_, W, _) in sets[:2]]
     y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
     qbuf = torch.empty((M, K), dtype=torch.int8, device="cuda:0")
     sbuf = torch.empty(max(M, K), dtype=torch.float32, device="cuda:0")
     wsc = torch.empty(max(H.fwht_quant_workspace_bytes(M, N, H.COLS, BLOCK), 256),
                       dtype=torch.uint8, device="cuda:0")
-
-    def gemm(i):
-        H.gemm_i8(codes[i % 2][0], codes[i % 2][1], wcodes[i % 2][0], wcodes[i % 2][1], c=y)
-
-    def rows(i):
-        H.fwht_quant(sets[i % N_SETS][0], axis=H.ROWS, block=BLOCK, q=qbuf, scale=sbuf[:M])
-
-    def cols(i):
-        H.fwht_quant(sets[i % N_SETS][2], axis=H.COLS, block=BLOCK, q=qbuf, scale=sbuf[:N],
-                     workspace=wsc)
-
     signs = H.hadamard_signs(K, seed=2024, device="cuda:0")
-
-    def rows_opt(i):
-        H.fwht_quant(sets[i % N_SETS][2], axis=H.ROWS, block=BLOCK, q=qbuf, scale=sbuf[:M],
-                     signs=signs, rounding="stochastic", seed=SEED64, counter=i)
-
-    def cols_opt(i):
-        H.fwht_quant(sets[i % N_SETS][2], axis=H.COLS, block=BLOCK, q=qbuf, scale=sbuf[:N],
-                     workspace=wsc, signs=signs, rounding="stochastic", seed=SEED64, counter=i)
-
     padded = [X[:, :K_PAD].contiguous() for (X, _, _) in sets]
+    keep = []  # option structs referenced by the prepared argument lists
 
-    def rows_pad(i):
-        H.fwht_quant(padded[i % N_SETS], axis=H.ROWS, block=BLOCK, q=qbuf, scale=sbuf[:M])
+    def gemm_args(a, b, kind_code):
+        return (P(a[0]), ld(a[0]), P(a[1]), P(b[0]), ld(b[0]), P(b[1]), M, N, K, P(y),
+                code(y.dtype), ld(y), st)
 
-    for f in (gemm, rows, cols, rows_opt, cols_opt, rows_pad):
+    gemm = _c_launcher(H, "halo_gemm_i8", [gemm_args(codes[i], wcodes[i], 0) for i in range(2)])
+    gemm_fp8 = _c_launcher(H, "halo_gemm_fp8", [
+        (P(f8x[i][0]), code(e4), ld(f8x[i][0]), P(f8x[i][1]), P(f8w[i][0]), code(e4),
+         ld(f8w[i][0]), P(f8w[i][1]), M, N, K, P(y), code(y.dtype), ld(y), st) for i in range(2)])
+
+    def fq_args(x, axis, opts=None, ws=None):
+        rows_, cols_ = x.shape
+        nvec = rows_ if axis == H.ROWS else cols_
+        L = cols_ if axis == H.ROWS else rows_
+        lp = H.padded_len(L, BLOCK)
+        q = qbuf.view(-1)[:nvec * lp].view(nvec, lp)
+        if opts is not None:
+            keep.append(opts)
+        return (P(x), code(x.dtype), rows_, cols_, ld(x), axis, BLOCK, code(torch.int8), P(q),
+                ld(q), P(sbuf), ctypes.byref(opts) if opts is not None else None,
+                P(ws) if ws is not None else None, ws.numel() if ws is not None else 0, st)
+
+    def sr_opts(i):
+        return H.QuantOpts(P(signs), H.STOCHASTIC, H._u32x2(SEED64), H._u32x2(i))
+
+    fq = "halo_fwht_quant_ex"
+    rows = _c_launcher(H, fq, [fq_args(X, H.ROWS) for (X, _, _) in sets])
+    cols = _c_launcher(H, fq, [fq_args(DY, H.COLS, ws=wsc) for (_, _, DY) in sets])
+    rows_opt = _c_launcher(H, fq, [fq_args(sets[i][2], H.ROWS, sr_opts(i))
+                                   for i in range(N_SETS)])
+    cols_opt = _c_launcher(H, fq, [fq_args(sets[i][2], H.COLS, sr_opts(i), wsc)
+                                   for i in range(N_SETS)])
+    rows_pad = _c_launcher(H, fq, [fq_args(Xp, H.ROWS) for Xp in padded])
+
+    legs = {"gemm_i8_4096": gemm, "gemm_fp8_4096": gemm_fp8, "fq_rows_4096": rows,
+            "fq_cols_4096": cols, "fq_rows_opt_4096": rows_opt, "fq_cols_opt_4096": cols_opt,
+            "fq_rows_pad_4000": rows_pad}
+    for f in legs.values():
         for i in range(3):
             f(i)
-    out = {"gemm_i8_4096": time_events(gemm, iters, torch),
-           "fq_rows_4096": time_events(rows, iters, torch),
-           "fq_cols_4096": time_events(cols, iters, torch),
-           "fq_rows_opt_4096": time_events(rows_opt, iters, torch),
-           "fq_cols_opt_4096": time_events(cols_opt, iters, torch),
-           "fq_rows_pad_4000": time_events(rows_pad, iters, torch)}
+    # three rounds over all legs, the median per leg: the clock of a power-limited chip
+    # still wanders in the first few hundred milliseconds of load
+    runs = {k: [] for k in legs}
+    for _ in range(3):
+        for k, f in legs.items():
+            runs[k].append(time_events(f, iters, torch))
+    out = {k: float(np.median(v)) for k, v in runs.items()}
     if with_copy:
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0").normal_()
         dst = torch.empty_like(src)
-        out["copy_64MiB"] = time_events(lambda i: dst.copy_(src), iters, torch)
+        # the counter calibration: an elementwise kernel that reads and writes exactly 64 MiB,
+        # with a name no other launch of the run shares
+        out["copy_64MiB"] = time_events(lambda i: torch.neg(src, out=dst), iters, torch)
     return out
 
 
@@ -265,18 +304,19 @@ def _pmc_per_call(d, counter):
 def summarize_pmc(fetch_dir, write_dir, command):
     fetch = _pmc_per_call(fetch_dir, "FETCH_SIZE")
     write = _pmc_per_call(write_dir, "WRITE_SIZE")
-    # calibration: a device copy of COPY_BYTES reads and writes exactly COPY_BYTES
+    # calibration: the elementwise negation of COPY_BYTES reads and writes exactly COPY_BYTES
     f_scale = COPY_BYTES / (fetch["copy_64MiB"] * 1024.0)
     w_scale = COPY_BYTES / (write["copy_64MiB"] * 1024.0)
-    algo = {"gemm_i8_4096": GEMM_BYTES, "fq_rows_4096": FQ_BYTES, "fq_cols_4096": FQ_BYTES}
+    algo = {"gemm_i8_4096": GEMM_BYTES, "gemm_fp8_4096": GEMM_BYTES, "fq_rows_4096": FQ_BYTES,
+            "fq_cols_4096": FQ_BYTES, "fq_rows_opt_4096": FQ_BYTES, "fq_cols_opt_4096": FQ_BYTES}
     res = {"kernel_source_hash": source_hash(KERNEL_SOURCES), "command": command,
            "fetch_scale": f_scale, "write_scale": w_scale, "bytes_per_launch": {},
            "fetch_kib_raw": fetch, "write_kib_raw": write}
     lines = [f"command: {command}",
-             f"calibration ({COPY_BYTES >> 20} MiB device copy): FETCH_SIZE x{f_scale:.3f}, "
+             f"calibration ({COPY_BYTES >> 20} MiB elementwise read + write): FETCH_SIZE x{f_scale:.3f}, "
              f"WRITE_SIZE x{w_scale:.3f} -> bytes", "",
              f"{'pass':<14} {'read MB':>9} {'write MB':>9} {'total MB':>9} {'algorithmic MB':>15}"]
-    for key in ("gemm_i8_4096", "fq_rows_4096", "fq_cols_4096"):
+    for key in algo:
         if fetch[key] is None or write[key] is None:
             continue
         rd = fetch[key] * 1024.0 * f_scale
@@ -291,7 +331,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--kernel-iters", type=int, default=60)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernels-only", action="store_true")
@@ -423,6 +463,12 @@ def main():
                      "ms_per_launch": round(t_gemm, 5), "algorithmic_ops": GEMM_OPS},
         "fwht_quant": {"rows": hbm(rows_gbs, t_rows, "fq_rows_4096"),
                        "cols": hbm(cols_gbs, t_cols, "fq_cols_4096")},
+        "gemm_fp8": {"bound": "mfma", "achieved": round(GEMM_OPS / (t["gemm_fp8_4096"] * 1e-3) / 1e12, 2),
+                     "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(GEMM_OPS / (t["gemm_fp8_4096"] * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+                     "traffic": load_traffic("gemm_fp8_4096"),
+                     "kernel": "gemm_kernel<FP8 E4M3 x E4M3, bf16 out> 4096x4096x4096",
+                     "ms_per_launch": round(t["gemm_fp8_4096"], 5), "algorithmic_ops": GEMM_OPS},
         "options": {
             "step": {"ms": round(ms_opt, 4),
                      "effective_tops": round(STEP_GOP / (ms_opt * 1e-3) / 1e3, 3),
