@@ -459,8 +459,19 @@ __device__ __forceinline__ void cols_task(const ColsProb& pr, int64_t ltask, uin
   uint32_t* arrive = pr.arrive;
   const int64_t ncols = a.nvec;
   const uint16_t* __restrict__ xin = reinterpret_cast<const uint16_t*>(a.x);
-  const int64_t strip = ltask / P;
-  const int part = (int)(ltask % P);
+  // the P tasks of a strip are consecutive (see the launcher); with one task per strip the
+  // strips are spread so that each XCD (task i runs on XCD (i + offset) % 8) gets a contiguous
+  // run of them: neighbouring strips share 128-byte lines, which its L2 then fetches once
+  int64_t strip;
+  int part;
+  if (P == 1) {
+    const int64_t T = (a.nvec + C - 1) / C, q = T / 8, r = T % 8, x = ltask % 8, s = ltask / 8;
+    strip = x < r ? x * (q + 1) + s : r * (q + 1) + (x - r) * q + s;
+    part = 0;
+  } else {
+    strip = ltask / P;
+    part = (int)(ltask % P);
+  }
   const int64_t c0 = strip * C;
 
     // ---- load 8 rows x 8 columns, transpose, write to LDS ------------------------------
@@ -613,11 +624,17 @@ __global__ __launch_bounds__(1024) void fq_batch_kernel(FqBatch fb) {
 }
 
 // Rows per task for a column of `rows` elements; 0 when the shape is not covered.
+// Rows per task for a column of `rows` elements (a power of two in [64, 4096] dividing rows
+// and divisible by the block; 0 when the shape is not covered).  Columns of up to 4096 rows go
+// whole into one task (4096 x 16 columns, or a wider tile for shorter columns): no exchange of
+// partial maxima at all, and the strips' XCD-aware order keeps their 32-byte row segments
+// fetched once per 128-byte line.  Longer columns take 1024-row tasks (64-column strips, full
+// 128-byte row segments) and exchange their partial maxima.
 static int cols2_rows_per_task(int64_t rows, int block) {
-  int R;
-  if (block > 1024) R = block;
-  else if (rows >= 1024) R = 1024;
-  else R = (int)rows;
+  int R = rows <= 4096 ? 4096 : 1024;
+  if (block > R) R = block;
+  while (R > rows) R >>= 1;
+  while (R >= 64 && rows % R != 0) R >>= 1;
   if (R < 64 || R > 4096 || (R & (R - 1)) != 0) return 0;
   if (rows % R != 0 || R % block != 0) return 0;
   return R;

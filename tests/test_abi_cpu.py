@@ -115,11 +115,12 @@ def test_fwht_quant_ex_validation(L):
 
 
 def test_fwht_quant_workspace_bytes(L):
-    # single-read columns pass: per-strip arrival counters (64 strips of 64 columns, padded to
-    # 256 bytes) + one maximum per column
+    # single-read columns pass: per-strip arrival counters (padded to 256 bytes) + one maximum
+    # per column, for columns longer than one task (4096 rows: whole columns, no scratch)
     W = L.halo_fwht_quant_workspace_bytes
-    assert W(4096, 4096, 1, 256, BF16) == 256 + 4096 * 4
-    assert W(8192, 4096, 1, 128, BF16) == 256 + 4096 * 4
+    assert W(4096, 4096, 1, 256, BF16) == 0      # whole 4096-row columns per task
+    assert W(4000, 4096, 1, 256, BF16) == 0      # padded to 4096 rows: still whole columns
+    assert W(8192, 4096, 1, 128, BF16) == 256 + 4096 * 4      # 64 strips of 64 columns, 8 parts
     assert W(16384, 14336, 1, 512, BF16) == 1024 + 14336 * 4
     assert W(8192, 4096, 1, 4096, BF16) == 1024 + 4096 * 4      # 16-column strips of 4096 rows
     assert W(1024, 4096, 1, 256, BF16) == 0      # one part per column: no exchange
@@ -175,18 +176,26 @@ def test_workspace_bytes(L):
     nq, mq = pad(n, 256), pad(m, 256)  # 768, 512
     want = (r(m * nq) + r(4 * m) + r(k * nq) + r(4 * k) + r(n * mq) + r(4 * n) + r(k * mq)
             + r(4 * k))
+    # the W columns pass along n (768 rows) runs 256-row tasks in 3 parts: 4 strips of 256
+    # columns need arrival counters (256 bytes) and 1024 column maxima
+    want += r(r(4 * 4) + 4 * k)
     assert X(m, n, k, 256, E4M3, 1) == want
     # the block-free query covers every block: the largest padding (block 4096) decides here
     assert L.halo_linear_workspace_bytes(m, n, k, I8, 0) == X(m, n, k, 4096, I8, 0)
     assert L.halo_linear_workspace_bytes(m, n, k, I8, 0) == max(X(m, n, k, 1 << i, I8, 0)
                                                               for i in range(13))
     assert X(m, n, k, 3, I8, 0) == 0
-    # 4096^3 backward: the code matrices plus the columns passes' shared scratch
+    # 4096^3 backward: the code matrices only (4096-row columns go whole into one task, so the
+    # columns passes need no scratch for any block)
     big = 4096
     codes = 4 * (r(big * big) + r(4 * big))
-    # (one scratch per column pass: W, dY, X; sized for every block, and block 2048 needs the
-    # most: 128 strips of 32 columns, 2 parts)
-    assert L.halo_linear_workspace_bytes(big, big, big, I8, 1) == codes + 3 * r(512 + 4096 * 4)
+    assert L.halo_linear_workspace_bytes(big, big, big, I8, 1) == codes
+    # 8192 tokens: the columns passes along m exchange partial maxima (dY: 4096 columns, X:
+    # 4096 columns; block 4096 needs the most, 256 strips of 16 columns in 2 parts)
+    m8 = 8192
+    codes8 = (r(m8 * big) + r(4 * m8) + r(big * big) + r(4 * big) + r(big * m8) + r(4 * big)
+              + r(big * m8) + r(4 * big))
+    assert L.halo_linear_workspace_bytes(m8, big, big, I8, 1) == codes8 + 2 * r(1024 + 4096 * 4)
     assert L.halo_linear_workspace_bytes(-1, n, k, I8, 0) == 0
     assert L.halo_linear_workspace_bytes(m, n, k, BF16, 0) == 0
 

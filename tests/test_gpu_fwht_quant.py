@@ -88,12 +88,15 @@ COL_CASES = [
     ("bf16", 1024, 2048, 16, O.I8),
     ("bf16", 2048, 4096, 8, O.E4M3),
     ("bf16", 4096, 8192, 8, O.I8),
-    ("bf16", 256, 4096, 520, O.I8),       # 4 tasks per strip, partial last strip
-    ("bf16", 128, 8192, 72, O.E4M3),      # 8 tasks per strip
+    ("bf16", 256, 4096, 520, O.I8),       # whole 4096-row columns, 16-column strips, partial last
+    ("bf16", 128, 8192, 72, O.E4M3),      # 8 tasks per strip (1024-row parts)
     ("bf16", 512, 512, 136, O.E5M2),      # 512-row tiles of 128 columns
     ("bf16", 64, 256, 1032, O.I8),        # 256-row tiles, 5 strips
     ("bf16", 1024, 3072, 64, O.I8),       # 3 tasks per strip
     ("bf16", 256, 4096, 5120, O.I8),      # 320 tasks: more than one round of the persistent grid
+    ("bf16", 256, 768, 64, O.I8),         # 256-row parts, 3 per strip
+    ("bf16", 256, 2048, 96, O.E4M3),      # whole 2048-row columns, 32-column strips
+    ("bf16", 128, 8192, 200, O.I8),       # 8 parts per strip, partial last strip
 ]
 
 
