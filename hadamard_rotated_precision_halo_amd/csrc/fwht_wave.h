@@ -598,8 +598,9 @@ __global__ __launch_bounds__(1024) void fq_cols2_kernel(ColsProb c0, ColsProb c1
 }
 
 // The rotation passes of a layer backward in one launch: the rows of dY (codes QG) and the
-// columns of W (QW), dY (QG) and X (QW).  Workgroups [0, rows_wg) run the rows pass, 16 waves
-// each; the column passes follow in order, one task per workgroup.  All passes read bf16.
+// columns of W (QW), dY (QG) and X (QW).  The column passes come first, one task per
+// workgroup, in that order; the rows pass follows, 16 waves per workgroup: its shorter tasks
+// fill the tail of the launch.  All passes read bf16.
 struct FqBatch {
   FqArgs rows;
   int64_t rows_wg;
@@ -612,18 +613,18 @@ template <int B, int QG, int QW, bool SR>
 __global__ __launch_bounds__(1024) void fq_batch_kernel(FqBatch fb) {
   extern __shared__ __attribute__((aligned(16))) uint4 lds[];
   const int64_t bid = blockIdx.x;
-  if (bid < fb.rows_wg) {
-    rows_wave<uint16_t, B, QG, SR>(fb.rows, bid * 16 + (threadIdx.x >> 6), threadIdx.x & 63);
-  } else if (bid < fb.end_w) {
-    cols_task<B, QW, false>(fb.cw, bid - fb.rows_wg, lds);
+  if (bid < fb.end_w) {
+    cols_task<B, QW, false>(fb.cw, bid, lds);
   } else if (bid < fb.end_dy) {
     cols_task<B, QG, SR>(fb.cdy, bid - fb.end_w, lds);
-  } else {
+  } else if (bid < fb.end_x) {
     cols_task<B, QW, false>(fb.cx, bid - fb.end_dy, lds);
+  } else {
+    rows_wave<uint16_t, B, QG, SR>(fb.rows, (bid - fb.end_x) * 16 + (threadIdx.x >> 6),
+                                   threadIdx.x & 63);
   }
 }
 
-// Rows per task for a column of `rows` elements; 0 when the shape is not covered.
 // Rows per task for a column of `rows` elements (a power of two in [64, 4096] dividing rows
 // and divisible by the block; 0 when the shape is not covered).  Columns of up to 4096 rows go
 // whole into one task (4096 x 16 columns, or a wider tile for shorter columns): no exchange of
@@ -761,16 +762,17 @@ static hipError_t launch_batch_t(const FqArgs* rows, const FqArgs& cw, void* ws_
   fb.cw = cols2_prob(cw, ws_w, &tw, &scratch);
   fb.cdy = cols2_prob(cdy, ws_dy, &tdy, &scratch);
   fb.cx = cols2_prob(cx, ws_x, &tx, &scratch);
-  fb.end_w = fb.rows_wg + tw;
+  fb.end_w = tw;
   fb.end_dy = fb.end_w + tdy;
   fb.end_x = fb.end_dy + tx;
-  if (fb.end_x == 0) return hipSuccess;
+  const int64_t grid = fb.end_x + fb.rows_wg;
+  if (grid == 0) return hipSuccess;
   int P = fb.cw.P;
   if (fb.cdy.P > P) P = fb.cdy.P;
   if (fb.cx.P > P) P = fb.cx.P;
   if (P > 1 && cols2_capacity(reinterpret_cast<const void*>(fn)) < P)
     return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fq_batch_kernel<B, QG, QW, SR>), dim3((unsigned)fb.end_x), dim3(1024),
+  hipLaunchKernelGGL((fq_batch_kernel<B, QG, QW, SR>), dim3((unsigned)grid), dim3(1024),
                      kColsLdsBytes, st, fb);
   return hipGetLastError();
 }
