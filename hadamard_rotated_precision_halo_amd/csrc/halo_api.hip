@@ -163,6 +163,12 @@ size_t fq_ws_bytes_len(int64_t len, int64_t nvec, halo_axis axis, int32_t block,
   return fq_cols2_ws_bytes(len, nvec, block, xt == HALO_BF16 ? 1 : 0);
 }
 
+// The GEMM kernel addresses each code operand with 32-bit byte offsets: an operand of `rows`
+// rows (leading dimension ld bytes, k bytes used per row) must span less than 4 GiB.
+bool operand_fits(int64_t rows, int64_t ld, int64_t k) {
+  return rows <= 0 || (rows - 1) * ld + k <= (int64_t(1) << 32);
+}
+
 halo_status check_gemm(const void* a, int64_t lda, const void* b, int64_t ldb, int64_t m,
                        int64_t n, int64_t k, const void* c, halo_dtype ct, int64_t ldc,
                        const float* sa, const float* sb, int kmult) {
@@ -173,12 +179,14 @@ halo_status check_gemm(const void* a, int64_t lda, const void* b, int64_t ldb, i
   if (ct != HALO_I32 && ((m > 0 && !sa) || (n > 0 && !sb))) return HALO_ERR_NULL;
   if (k % kmult != 0) return HALO_ERR_SHAPE;
   if (lda < k || ldb < k || ldc < n || ldc < 1) return HALO_ERR_SHAPE;
+  if (!operand_fits(m, lda, k) || !operand_fits(n, ldb, k)) return HALO_ERR_SHAPE;
   if (!aligned16(a) || !aligned16(b) || !aligned16(c)) return HALO_ERR_ALIGN;
   if (lda % 16 != 0 || ldb % 16 != 0 || (ldc * esize(ct)) % 16 != 0) return HALO_ERR_ALIGN;
   return HALO_OK;
 }
 
 size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
+
 
 // Region sizes of the layer workspace, in carve order; the backward's last region is the
 // scratch of its three column passes (W, dY, X: one sub-region each, cleared together by the
@@ -345,6 +353,7 @@ halo_status halo_linear_fwd_ex(const void* x, const void* w, halo_dtype io_type,
   if (!valid_block(block)) return HALO_ERR_BLOCK;
   const int64_t kq = contraction_len(k, block);
   if (k % 8 != 0 || kq > fq_rows_max_len(block)) return HALO_ERR_SHAPE;
+  if (!operand_fits(m, kq, kq) || !operand_fits(n, kq, kq)) return HALO_ERR_SHAPE;
   if (opts && (opts->grad_rounding != HALO_ROUND_NEAREST_EVEN &&
                opts->grad_rounding != HALO_ROUND_STOCHASTIC))
     return HALO_ERR_OPTION;
@@ -406,6 +415,9 @@ halo_status halo_linear_bwd_ex(const void* dy, const void* x, const void* w, hal
   const int64_t nq = contraction_len(n, block), mq = contraction_len(m, block);
   if (n % 8 != 0 || k % 8 != 0) return HALO_ERR_SHAPE;
   if (dx && nq > fq_rows_max_len(block)) return HALO_ERR_SHAPE;
+  if (!operand_fits(m, nq, nq) || !operand_fits(k, nq, nq) || !operand_fits(n, mq, mq) ||
+      !operand_fits(k, mq, mq))
+    return HALO_ERR_SHAPE;
   if (opts && (opts->grad_rounding != HALO_ROUND_NEAREST_EVEN &&
                opts->grad_rounding != HALO_ROUND_STOCHASTIC))
     return HALO_ERR_OPTION;

@@ -120,7 +120,8 @@ size_t halo_fwht_quant_workspace_bytes(int64_t rows, int64_t cols, halo_axis axi
  *   c[i, j]   = acc[i, j] * sa[i] * sb[j] (c_type HALO_F32 or HALO_BF16, rounded to nearest even)
  *   c[i, j]   = acc[i, j]                 (c_type HALO_I32; sa and sb are not read and may be NULL)
  * a is [m x k] (lda), b is [n x k] (ldb), both contiguous along k; c is [m x n] (ldc).
- * k must be a positive multiple of 16; m and n are arbitrary (>= 0).
+ * k must be a positive multiple of 16; m and n are arbitrary (>= 0).  Each code operand must
+ * span less than 4 GiB ((m - 1) * lda + k <= 2^32, likewise for b; HALO_ERR_SHAPE otherwise).
  */
 halo_status halo_gemm_i8(const int8_t* a, int64_t lda, const float* sa, const int8_t* b,
                          int64_t ldb, const float* sb, int64_t m, int64_t n, int64_t k, void* c,
@@ -131,7 +132,8 @@ halo_status halo_gemm_i8(const int8_t* a, int64_t lda, const float* sa, const in
  * accumulation on the CDNA4 FP8 matrix cores and the same fused dequant:
  *   c[i, j] = (sum_t dec(a[i, t]) * dec(b[j, t])) * sa[i] * sb[j]
  * a_type, b_type: HALO_E4M3 or HALO_E5M2 each (any pair); c_type: HALO_F32 or HALO_BF16.
- * Shapes and layouts as for halo_gemm_i8; k must be a positive multiple of 32.
+ * Shapes, layouts and the 4 GiB operand span as for halo_gemm_i8; k must be a positive multiple
+ * of 32.
  * The fp32 sum's order is the matrix core's: the result lies within
  * k * 2^-24 / (1 - k * 2^-24) * sum_t |dec(a) dec(b)| of the exact sum before the dequant.
  */
@@ -161,7 +163,8 @@ size_t halo_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, halo_dtype q
  * k must be a multiple of 8 and n a multiple of 16 bytes of y_type; block as for
  * halo_fwht_quant.  When block does not divide k, X and W are padded with zeros along k (QWHA
  * page s5) and the product runs over all padded positions, which equals the product of the
- * padded operands.  The padded k (rounded up to a multiple of block and of 32) is at most 16384.
+ * padded operands.  The padded k (rounded up to a multiple of block and of 32) is at most 16384,
+ * and each code matrix (m or n rows of the padded k) spans less than 4 GiB.
  */
 halo_status halo_linear_fwd(const void* x, const void* w, halo_dtype io_type, int64_t m,
                             int64_t n, int64_t k, int32_t block, halo_dtype q_type, void* y,
@@ -181,7 +184,7 @@ halo_status halo_linear_fwd(const void* x, const void* w, halo_dtype io_type, in
  *   ws           at least halo_linear_workspace_bytes(m, n, k, q_type, 1) bytes.
  * n and k must be multiples of 8, m >= 1; block as for halo_fwht_quant.  Contraction
  * dimensions that block does not divide are zero-padded as in halo_linear_fwd; the padded n
- * is at most 16384 when dx is computed.
+ * is at most 16384 when dx is computed, and each code matrix spans less than 4 GiB.
  */
 halo_status halo_linear_bwd(const void* dy, const void* x, const void* w, halo_dtype io_type,
                             int64_t m, int64_t n, int64_t k, int32_t block, halo_dtype q_type,

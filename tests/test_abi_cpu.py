@@ -149,6 +149,10 @@ def test_gemm_i8_validation(L):
     assert gi8(L, lda=136, k=128) == ALIGN        # rows not 16-byte aligned
     assert gi8(L, ct=BF16, ldc=68) == ALIGN       # 136-byte output rows
     assert gi8(L, sa=BAD) == ALIGN
+    # the kernel addresses each operand with 32-bit byte offsets: spans up to 4 GiB only
+    big = (1 << 20) + 1                     # (big - 1) * 4096 + 4096 = 2^32 + 4096
+    assert gi8(L, m=big, lda=4096, ldb=4096, k=4096) == SHAPE
+    assert gi8(L, n=big, lda=4096, ldb=4096, k=4096) == SHAPE
 
 
 def gf8(L, a=P, at=E4M3, lda=128, sa=P2, b=P3, bt=E4M3, ldb=128, sb=P2, m=64, n=64, k=128, c=P,
@@ -214,6 +218,7 @@ def test_linear_fwd_validation(L):
     assert fwd(L, yt=I32) == DTYPE
     assert fwd(L, k=244) == SHAPE              # not a multiple of 8
     assert fwd(L, k=20000) == SHAPE            # padded k beyond the rows kernel
+    assert fwd(L, m=(1 << 20) + 1, k=4096, wsb=1 << 40) == SHAPE  # X codes span over 4 GiB
     assert fwd(L, block=6) == BLOCK
     assert fwd(L, ws=NUL) == WORKSPACE
     assert fwd(L, wsb=1000) == WORKSPACE
@@ -236,6 +241,8 @@ def test_linear_bwd_validation(L):
     assert bwd(L, k=244) == SHAPE
     assert bwd(L, m=0) == SHAPE
     assert bwd(L, block=6) == BLOCK
+    # dW only (no rows-length limit): the W column codes [k x padded n] span over 4 GiB
+    assert bwd(L, n=(1 << 20) + 8, k=4096, dx=NUL, wsb=1 << 40) == SHAPE
     assert bwd(L, wsb=10) == WORKSPACE
     assert bwd(L, dx=BAD) == ALIGN
 
