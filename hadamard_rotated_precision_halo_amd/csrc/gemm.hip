@@ -7,8 +7,8 @@
 // per-operand format select, then c[i, j] = (acc * sa[i]) * sb[j] in fp32, rounded to bf16 or
 // kept in fp32 (or the raw int32 accumulators).
 //
-// Tiling.  A 256-thread workgroup (4 wave64s, 2 x 2) owns a 256 x 256 output tile; each wave
-// owns 128 x 128 = 4 x 4 MFMA tiles of 32 x 32 with the accumulators resident in AGPRs.  K is
+// Tiling.  A 512-thread workgroup (8 wave64s, 2 x 4) owns a 256 x 256 output tile; each wave
+// owns 128 x 64 = 4 x 2 MFMA tiles of 32 x 32 with the accumulators resident in AGPRs.  K is
 // consumed in slabs of BK bytes: a slab (256 rows of each operand) is staged in LDS with
 // direct-to-LDS loads (global_load_lds_dwordx4: no VGPR staging, no ds_write) into a ring of
 // NSTAGE slabs filling 128 KB of the 160 KB LDS.  One barrier per slab, placed before the
@@ -26,7 +26,10 @@
 // The product is formed transposed (the MFMA's first operand is the b tile).  The epilogue
 // stages each wave's results in LDS and reads them back row-contiguous, so the stores are
 // full 256- or 512-byte row runs (bf16 output is dequantised and rounded before staging,
-// halving the staged bytes); the scales sa, sb were loaded into LDS at kernel start.
+// halving the staged bytes); the scales sa, sb were loaded into LDS at kernel start.  The
+// output is written once and never read back here, so its full 16-byte stores are
+// non-temporal: they stream past the caches instead of evicting the operand slabs that the
+// other workgroups on the XCD still read.
 // Workgroups are numbered so that each of the 8 XCDs (workgroup i runs on XCD i % 8) gets a
 // contiguous run of tiles, rastered in groups of 4 tile rows, for L2 reuse of both operands.
 #include "halo_device.h"
@@ -34,12 +37,12 @@
 
 #include <mutex>
 
+
 namespace halo {
 
 constexpr int BM = 256, BN = 256;
-#ifndef HALO_GEMM_WN
-#define HALO_GEMM_WN 4
-#endif
+constexpr int GEMM_WN = 4;                      // waves across a tile's columns (x 2 rows)
+constexpr int GEMM_BK = 128;                    // K bytes per slab: a 2-slab ring
 constexpr int RING_BYTES = 128 * 1024;          // K-slab ring; the scales follow it
 constexpr int LDS_BYTES = RING_BYTES + 2 * 256 * 4;
 
@@ -83,11 +86,12 @@ __device__ __forceinline__ void store4(void* c, int64_t ldc, int64_t row, int64_
                                        int64_t n, const float* v, const int* iv) {
   if (col + 3 < n) {
     if constexpr (OUT == 0) {
-      *reinterpret_cast<int4*>(reinterpret_cast<int*>(c) + row * ldc + col) =
-          make_int4(iv[0], iv[1], iv[2], iv[3]);
+      const v4i w = {iv[0], iv[1], iv[2], iv[3]};
+      __builtin_nontemporal_store(w, reinterpret_cast<v4i*>(reinterpret_cast<int*>(c) + row * ldc + col));
     } else if constexpr (OUT == 1) {
-      *reinterpret_cast<float4*>(reinterpret_cast<float*>(c) + row * ldc + col) =
-          make_float4(v[0], v[1], v[2], v[3]);
+      const v4i w = {(int)__float_as_uint(v[0]), (int)__float_as_uint(v[1]),
+                     (int)__float_as_uint(v[2]), (int)__float_as_uint(v[3])};
+      __builtin_nontemporal_store(w, reinterpret_cast<v4i*>(reinterpret_cast<float*>(c) + row * ldc + col));
     } else {
       uint2 w;
       w.x = pack_bf16x2(v[0], v[1]);
@@ -347,7 +351,8 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_kernel(GemmPair gp) {
         if (row >= g.m || col0 >= g.n) continue;
         uint16_t* dst = reinterpret_cast<uint16_t*>(g.c) + row * g.ldc + col0;
         if (col0 + 7 < g.n) {
-          *reinterpret_cast<uint4*>(dst) = w;
+          const v4i wv = {(int)w.x, (int)w.y, (int)w.z, (int)w.w};
+          __builtin_nontemporal_store(wv, reinterpret_cast<v4i*>(dst));
         } else {
           const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
           for (int e = 0; e < 8 && col0 + e < g.n; ++e)
@@ -415,7 +420,7 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_kernel(GemmPair gp) {
 
 template <int KIND, int AF, int BF, int OUT, bool MASK, int BK>
 static hipError_t launch_cfg(const GemmArgs& g0, const GemmArgs* g1, hipStream_t st) {
-  constexpr int WN = HALO_GEMM_WN;
+  constexpr int WN = GEMM_WN;
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
   std::call_once(once, [] {
@@ -442,10 +447,6 @@ static hipError_t launch_cfg(const GemmArgs& g0, const GemmArgs* g1, hipStream_t
   return hipGetLastError();
 }
 
-#ifndef HALO_GEMM_BK
-#define HALO_GEMM_BK 128
-#endif
-
 template <int KIND, int BK>
 static bool needs_mask(const GemmArgs& g) {
   constexpr int KS = BK / (KIND == 0 ? 32 : 64);
@@ -455,7 +456,7 @@ static bool needs_mask(const GemmArgs& g) {
 
 template <int KIND, int AF, int BF, int OUT>
 static hipError_t launch_t(const GemmArgs& g, const GemmArgs* g1, hipStream_t st) {
-  constexpr int BK = HALO_GEMM_BK;
+  constexpr int BK = GEMM_BK;
   const bool mask = needs_mask<KIND, BK>(g) || (g1 && needs_mask<KIND, BK>(*g1));
   return mask ? launch_cfg<KIND, AF, BF, OUT, true, BK>(g, g1, st)
               : launch_cfg<KIND, AF, BF, OUT, false, BK>(g, g1, st);
