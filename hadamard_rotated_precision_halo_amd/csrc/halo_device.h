@@ -137,9 +137,11 @@ __device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
                                                uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    // one 32 x 32 -> 64-bit product each (v_mad_u64_u32 gives both halves at once)
+    // one 32 x 32 -> 64-bit product each (v_mad_u64_u32 gives both halves at once); each
+    // three-way xor is one v_bitop3_b32 (truth table 0x96), the key word in a scalar register
     const uint64_t p0 = (uint64_t)0xD2511F53u * c0, p2 = (uint64_t)0xCD9E8D57u * c2;
-    const uint32_t n0 = (uint32_t)(p2 >> 32) ^ c1 ^ k0, n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p2 >> 32), c1, k0, 0x96);
+    const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, 0x96);
     c0 = n0;
     c1 = (uint32_t)p2;
     c2 = n2;
@@ -183,7 +185,7 @@ __device__ __forceinline__ void sr_words8(int64_t vec, int64_t pos, uint32_t k0,
 // rounds to 1.  The result is a grid value; a zero result is +0.
 template <int QT>
 __device__ __forceinline__ float sr_value(float t, uint32_t w, float qmax) {
-  t = __builtin_fminf(__builtin_fmaxf(t, -qmax), qmax);
+  t = __builtin_amdgcn_fmed3f(t, -qmax, qmax);  // the clamp in one v_med3_f32 (t is finite)
   float s = 1.f, inv = 1.f;
   if constexpr (QT != 0) {
     constexpr uint32_t MB = QT == 1 ? 3u : 2u;         // mantissa bits
