@@ -191,6 +191,7 @@ __global__ __launch_bounds__(256) void fq_rows_kernel(FqArgs a) {
   constexpr int G = Geo::G, U = Geo::U, E = Geo::E, IT = Geo::IT, NG = Geo::NGROUPS;
   __shared__ uint32_t s_max[Geo::MAXV];
   __shared__ float s_mul[Geo::MAXV];
+  __shared__ float s_pre[Geo::MAXV];  // factor the values take first (code_mul)
 
   const int tid = threadIdx.x;
   const int grp = tid / G, x = tid % G;
@@ -237,15 +238,16 @@ __global__ __launch_bounds__(256) void fq_rows_kernel(FqArgs a) {
   __syncthreads();
   for (int i = tid; i < nv; i += 256) {
     const float amax = __uint_as_float(s_max[i]);
-    float mul, sc;
+    float mul, sc, pre = 1.f;
     if (QT == 3) {
       mul = a.inv_sqrt_b;
       sc = amax * a.inv_sqrt_b;
     } else {
-      mul = amax > 0.f ? a.qmax / amax : 0.f;
+      mul = code_mul(a.qmax, amax, &pre);
       sc = amax / a.denom;
     }
     s_mul[i] = mul;
+    s_pre[i] = pre;
     a.scale[v0 + i] = sc;
   }
   __syncthreads();
@@ -256,7 +258,11 @@ __global__ __launch_bounds__(256) void fq_rows_kernel(FqArgs a) {
     const int item = grp + it * NG;
     if (item < nitems) {
       const int vec = item / items_per_vec, blk = item % items_per_vec;
-      const float m = s_mul[vec];
+      const float m = s_mul[vec], pre = s_pre[vec];
+      if (pre != 1.f) {
+#pragma unroll
+        for (int i = 0; i < U * 8; ++i) val[it][i] *= pre;
+      }
       const int64_t pos = (int64_t)blk * E + x * 8;
       char* p = qout + ((v0 + vec) * a.ldq + pos) * CS;
 #pragma unroll
@@ -362,7 +368,12 @@ __global__ __launch_bounds__(256) void fq_cols_kernel(FqArgs a) {
 #pragma unroll
     for (int c = 0; c < NV; ++c) {
       const float amax = __uint_as_float(colmax[c0 + c]);
-      const float m = QT == 3 ? a.inv_sqrt_b : (amax > 0.f ? a.qmax / amax : 0.f);
+      float m = a.inv_sqrt_b, pre = 1.f;
+      if constexpr (QT != 3) m = code_mul(a.qmax, amax, &pre);
+      if (pre != 1.f) {
+#pragma unroll
+        for (int i = 0; i < U * 8; ++i) val[c][i] *= pre;
+      }
       char* p = qout + ((c0 + c) * a.ldq + r0 + x * 8) * CS;
 #pragma unroll
       for (int u = 0; u < U; ++u)

@@ -307,6 +307,22 @@ __device__ __forceinline__ float quant_mul(const FqArgs& a, float mx) {
   if constexpr (QT == 3) return a.inv_sqrt_b;
   else return mx > 0.f ? a.qmax / mx : 0.f;
 }
+// The same for the lane's 64 values v of a vector: a vector of tiny values has them scaled
+// first (code_mul).
+template <int QT>
+__device__ __forceinline__ float quant_mul_v(const FqArgs& a, float mx, float* v) {
+  if constexpr (QT == 3) {
+    return a.inv_sqrt_b;
+  } else {
+    float pre;
+    const float m = code_mul(a.qmax, mx, &pre);
+    if (pre != 1.f) {
+#pragma unroll
+      for (int i = 0; i < 64; ++i) v[i] *= pre;
+    }
+    return m;
+  }
+}
 template <int QT>
 __device__ __forceinline__ float stored_scale(const FqArgs& a, float mx) {
   return QT == 3 ? mx * a.inv_sqrt_b : mx / a.denom;
@@ -339,7 +355,7 @@ __device__ __forceinline__ void rows_wave(const FqArgs& a, int64_t gw, int lane)
   const bool writer = (lane & ((1 << row_lanes_log2) - 1)) == 0;
   if (!valid) return;
   if (writer) a.scale[row] = stored_scale<QT>(a, mx);
-  const float mul = quant_mul<QT>(a, mx) * sgn;
+  const float mul = quant_mul_v<QT>(a, mx, v) * sgn;
   store_slice<B, QT, SR>(a, v, mul, row * a.ldq + col0, lane, row, col0);
 }
 
@@ -383,7 +399,7 @@ __global__ __launch_bounds__(1024) void fq_rows2_kernel(FqPair pp, int multi) {
   }
   if (w == 0 && lane == 0) a.scale[row] = stored_scale<QT>(a, mx);
   if (!valid) return;
-  const float mul = quant_mul<QT>(a, mx) * sgn;
+  const float mul = quant_mul_v<QT>(a, mx, v) * sgn;
   store_slice<B, QT, SR>(a, v, mul, row * a.ldq + col0, lane, row, col0);
 }
 
@@ -580,7 +596,7 @@ __device__ __forceinline__ void cols_task(const ColsProb& pr, int64_t ltask, uin
     // ---- quantise and store the transposed codes ------------------------------------------
     if (valid) {
       if (part == 0 && writer) a.scale[col] = stored_scale<QT>(a, mx);
-      const float mul = quant_mul<QT>(a, mx) * sgn;
+      const float mul = quant_mul_v<QT>(a, mx, v) * sgn;
       store_slice<B, QT, SR>(a, v, mul, col * a.ldq + pos0, lane, col, pos0);
     }
 }

@@ -152,6 +152,22 @@ __device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
   return make_uint4(c0, c1, c2, c3);
 }
 
+// Multiplier of the fp32 code decision, m = fl32(qmax / amax) (0 for a zero vector).  For a
+// vector of values so small that this overflows (amax below qmax / FLT_MAX) the decision is
+// taken on the vector scaled by 2^64: the scaling is exact for values this small, and the
+// butterflies (additions with gradual underflow) commute with it, so the codes are those of
+// the scaled vector, as absmax quantisation's scale invariance asks.  *pre receives the factor
+// the values take before the multiplier (1 or 2^64).
+__device__ __forceinline__ float code_mul(float qmax, float amax, float* pre) {
+  float m = amax > 0.f ? qmax / amax : 0.f;
+  *pre = 1.f;
+  if (m > __FLT_MAX__) {
+    *pre = 0x1p64f;
+    m = qmax / (amax * 0x1p64f);
+  }
+  return m;
+}
+
 // Chunk of 8 elements at position pos (a multiple of 8) of the vector whose element 0 is at
 // v0: zeros at and past in_len (the padding, never read), then the transform's signs.
 template <typename T>

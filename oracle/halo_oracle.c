@@ -61,7 +61,9 @@
  *   precision 32: the same butterflies in fp32 (same stage and pairing order), the code
  *                 decided in fp32 from the un-normalised butterfly output:
  *                 m = fl32(qmax / a), q = rne(y * m) with the product taken exactly
- *                 (INT8) or rounded to fp32 first (FP8).  The 1/sqrt(b) factor cancels
+ *                 (INT8) or rounded to fp32 first (FP8).  Where qmax / a overflows (a
+ *                 vector of values below about qmax / FLT_MAX) y and a are first scaled
+ *                 by 2^64, exactly, and the decision taken on the scaled vector.  The 1/sqrt(b) factor cancels
  *                 between y and max|y| in exact arithmetic, so both are evaluations of
  *                 the same formula; precision 32 is the one a single-precision device
  *                 takes its integer decisions in.  Stochastic rounding there starts from
@@ -384,10 +386,20 @@ static void quant_vec_f32(const float* yu, int64_t L, int64_t block, int qtype,
         *scale = 0.0;
         return;
     }
+    /* A vector so small that qmax / a overflows (a below qmax / FLT_MAX) takes its decision
+     * on the vector scaled by 2^64: exact for values this small, and the fp32 butterflies
+     * (additions only, with gradual underflow) commute with that scaling, so the codes are
+     * those of the scaled vector, as the scale invariance of absmax quantisation asks. */
+    float pre = 1.0f;
     float m = qmax / a;
+    if (isinf(m)) {
+        pre = 0x1p64f;
+        m = qmax / (a * pre);
+    }
     for (int64_t i = 0; i < L; ++i) {
+        const float yi = yu[i] * pre; /* exact */
         if (ro->stochastic) {
-            float t = yu[i] * m;
+            float t = yi * m;
             if (t == 0.0f) t = 0.0f;
             t = fminf(fmaxf(t, -qmax), qmax);
             float v = sr_float(t, qtype, sr_word(ro, vid, i));
@@ -396,12 +408,12 @@ static void quant_vec_f32(const float* yu, int64_t L, int64_t block, int qtype,
             continue;
         }
         if (qtype == OR_I8) {
-            long double n = rne((long double)yu[i] * (long double)m); /* exact product */
+            long double n = rne((long double)yi * (long double)m); /* exact product */
             if (n > 127.0L) n = 127.0L;
             if (n < -127.0L) n = -127.0L;
             ((int8_t*)q)[i] = (int8_t)n;
         } else {
-            float t = yu[i] * m; /* rounded to fp32, then to the fp8 grid */
+            float t = yi * m; /* rounded to fp32, then to the fp8 grid */
             if (t == 0.0f) t = 0.0f; /* exact zero: the +0 code */
             ((uint8_t*)q)[i] = fp8_encode((long double)t, fmt_of(qtype));
         }

@@ -213,3 +213,73 @@ def test_invalid_call_leaves_outputs_untouched():
         H.fwht_quant(x, axis=H.ROWS, block=512, q=q, scale=s)
     torch.cuda.synchronize()
     assert (q == 7).all() and (s == 3.0).all()
+
+
+# ---------------------------------------------------------------------------
+# vectors of tiny values and gradual underflow
+# ---------------------------------------------------------------------------
+
+def _tiny_mix(nvec, L, io, seed):
+    """[nvec x L] vectors of three kinds, cycling: tiny vectors (every element subnormal, so
+    fp32 qmax / absmax overflows and the decision runs on the vector scaled by 2^64), vectors
+    with subnormal elements among normal ones (the butterflies must keep gradual underflow),
+    and ordinary vectors.  Returns the input (bf16 bits or fp32) and the same input times
+    2^64 (exact)."""
+    rng = np.random.default_rng(seed)
+    g = rng.standard_normal((nvec, L))
+    if io == "bf16":
+        tiny = np.rint(np.clip(g, -3, 3)) * 2.0 ** -133       # bf16 subnormals
+    else:
+        tiny = np.rint(g * 2.0 ** 15) * 2.0 ** -149            # fp32 subnormals
+    mixed = g * np.where(rng.random((nvec, L)) < 0.5, 2.0 ** -130, 1.0)
+    kind = (np.arange(nvec) % 3)[:, None]
+    x = np.where(kind == 0, tiny, np.where(kind == 1, mixed, g)).astype(np.float32)
+    if io == "bf16":
+        x = synth.bf16_bits(x)
+        xf = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        big = synth.bf16_bits((xf * 2.0 ** 64).astype(np.float32))
+        assert np.array_equal((big.astype(np.uint32) << 16).view(np.float32), xf * 2.0 ** 64)
+    else:
+        big = (x.astype(np.float64) * 2.0 ** 64).astype(np.float32)
+        assert np.array_equal(big.astype(np.float64), x.astype(np.float64) * 2.0 ** 64)
+    return x, big
+
+
+TINY_CASES = [
+    # (axis, io, L): L = vector length; bf16 takes the wave kernels, fp32 the older ones
+    (H.ROWS, "bf16", 512), (H.ROWS, "bf16", 4096), (H.ROWS, "f32", 512),
+    (H.COLS, "bf16", 256), (H.COLS, "bf16", 4096), (H.COLS, "f32", 512),
+]
+
+
+@pytest.mark.parametrize("qtype", [O.I8, O.E4M3, O.E5M2])
+@pytest.mark.parametrize("axis,io,L", TINY_CASES)
+def test_tiny_and_subnormal_vectors(axis, io, L, qtype):
+    nvec = 24
+    x, big = _tiny_mix(nvec, L, io, seed=L + qtype)
+    if axis == H.COLS:  # the vectors are the matrix's columns
+        x, big = np.ascontiguousarray(x.T), np.ascontiguousarray(big.T)
+    oax = O.ROWS if axis == H.ROWS else O.COLS
+    q, s = _run(x, axis, 256, qtype)
+    r32, s32 = O.fwht_quant(x, oax, 256, qtype, precision=32)
+    assert np.array_equal(q, r32), f"{int((q != r32).sum())} codes differ from the fp32 decision"
+    assert np.array_equal(s, s32)
+    # scale invariance on the GPU itself: the tiny vectors' codes are the scaled vectors' codes
+    qb, _ = _run(big, axis, 256, qtype)
+    tiny_rows = np.arange(nvec) % 3 == 0
+    assert np.array_equal(q[tiny_rows], qb[tiny_rows])
+    assert (q[tiny_rows] != 0).any()
+
+
+@pytest.mark.parametrize("axis", [H.ROWS, H.COLS])
+def test_tiny_vectors_stochastic(axis):
+    x, _ = _tiny_mix(24, 4096, "bf16", seed=5)
+    if axis == H.COLS:
+        x = np.ascontiguousarray(x.T)
+    q, s = H.fwht_quant(to_dev(x), axis=axis, block=256, q_dtype=Q_TORCH[O.E5M2],
+                        rounding="stochastic", seed=(9 << 32) | 4, counter=(3 << 32) | 8)
+    torch.cuda.synchronize()
+    r32, s32 = O.fwht_quant(x, O.ROWS if axis == H.ROWS else O.COLS, 256, O.E5M2, precision=32,
+                            rounding=O.STOCHASTIC, key=(4, 9), ctr_hi=(8, 3))
+    assert np.array_equal(codes_to_np(q), r32)
+    assert np.array_equal(s.cpu().numpy().astype(np.float64), s32)

@@ -358,3 +358,54 @@ def test_layer_sr_uses_distinct_draws_for_rows_and_columns_of_dy():
     assert np.array_equal(dw, O.dequant(O.gemm_i8(qa, qb).astype(np.float64), sa, sb))
     qr, _ = O.fwht_quant(dy, O.COLS, 64, O.I8, rounding=O.STOCHASTIC, key=key, ctr_hi=chi)
     assert not np.array_equal(qr, qa)
+
+
+# ---------------------------------------------------------------------------
+# vectors of tiny values (absmax scale invariance)
+# ---------------------------------------------------------------------------
+
+def _tiny_and_scaled(seed, rows=3, cols=512):
+    """fp32 inputs v_big = integer * 2^-85 (normal, about 2^-70) and v_tiny = v_big * 2^-64
+    (integer multiples of 2^-149: subnormal, exact).  A rotated tiny vector's absmax is about
+    2^-124, so fp32 qmax / absmax overflows for every code type."""
+    rng = np.random.default_rng(seed)
+    ints = np.rint(rng.standard_normal((rows, cols)) * 2.0 ** 15)
+    big = (ints * 2.0 ** -85).astype(np.float32)
+    tiny = (ints * 2.0 ** -149).astype(np.float32)
+    assert np.array_equal(tiny.astype(np.float64) * 2.0 ** 64, big.astype(np.float64))
+    assert np.abs(tiny).max() < np.finfo(np.float32).tiny
+    return tiny, big
+
+
+@pytest.mark.parametrize("qtype", [O.I8, O.E4M3, O.E5M2])
+@pytest.mark.parametrize("axis", [O.ROWS, O.COLS])
+def test_tiny_vector_codes_equal_those_of_the_scaled_vector(qtype, axis):
+    # Absmax quantisation is invariant under scaling a vector: its codes are those of the same
+    # vector times 2^64.  That holds in exact arithmetic (the fp64 path) and must hold in the
+    # fp32 decision too, even where fp32 qmax / absmax overflows for the tiny vector.
+    tiny, big = _tiny_and_scaled(11)
+    if axis == O.COLS:
+        tiny, big = np.ascontiguousarray(tiny.T), np.ascontiguousarray(big.T)
+    qmax = {O.I8: 127.0, O.E4M3: 448.0, O.E5M2: 57344.0}[qtype]
+    for precision in (64, 32):
+        qt, st = O.fwht_quant(tiny, axis, 256, qtype, precision=precision)
+        qb, sb = O.fwht_quant(big, axis, 256, qtype, precision=precision)
+        assert np.array_equal(qt, qb), f"precision {precision}"
+        assert (np.abs(qb.astype(np.int64)) > 0).any()  # not the zero vector's codes
+        # scales: absmax / qmax, scaled back by 2^-64 (the tiny scales are subnormal in fp32)
+        np.testing.assert_allclose(st, sb * 2.0 ** -64, rtol=1e-6, atol=2.0 ** -149)
+    # the tiny vector really is in the range where fp32 qmax / absmax overflows
+    y = O.fwht_quant(tiny, axis, 256, O.F64, precision=32)[1] * 16.0  # absmax of unnormalised y
+    with np.errstate(over="ignore"):
+        assert (np.float32(qmax) / y.astype(np.float32) == np.inf).all()
+
+
+@pytest.mark.parametrize("qtype", [O.I8, O.E4M3, O.E5M2])
+def test_tiny_vector_stochastic_codes_equal_those_of_the_scaled_vector(qtype):
+    # with stochastic rounding the same uniforms meet the same scaled values
+    tiny, big = _tiny_and_scaled(12)
+    kw = dict(rounding=O.STOCHASTIC, key=(7, 8), ctr_hi=(1, 2))
+    for precision in (64, 32):
+        qt, _ = O.fwht_quant(tiny, O.ROWS, 256, qtype, precision=precision, **kw)
+        qb, _ = O.fwht_quant(big, O.ROWS, 256, qtype, precision=precision, **kw)
+        assert np.array_equal(qt, qb), f"precision {precision}"
