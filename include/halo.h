@@ -27,6 +27,11 @@
  *   - Scales are fp32 dequant multipliers: the vector's absmax after the orthonormal
  *     rotation divided by qmax (127 for INT8, 448 for E4M3, 57344 for E5M2).  A zero vector
  *     gets scale 0 and all-zero codes.
+ *   - Codes are decided in fp32: the un-normalised rotated value y times m = fl32(qmax /
+ *     absmax), rounded to the code grid (INT8: from the exact product; FP8: from its fp32
+ *     rounding).  A vector so small that m overflows (absmax below about qmax / FLT_MAX,
+ *     e.g. subnormal inputs) is first scaled by 2^64, exactly, so its codes are those of the
+ *     scaled vector.  Inputs whose fp32 block sums overflow are outside the supported range.
  *   - FP8 is the OCP format pair E4M3 ("FN": max 448, no infinities) and E5M2 (max 57344);
  *     codes are rounded to nearest even and never exceed the format's largest finite value.
  */
