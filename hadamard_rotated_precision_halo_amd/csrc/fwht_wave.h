@@ -44,6 +44,7 @@
 #include "halo_device.h"
 #include "halo_kernels.h"
 
+#include <atomic>
 #include <mutex>
 
 namespace halo {
@@ -658,19 +659,22 @@ static int cols2_rows_per_task(int64_t rows, int block) {
 }
 
 // Workgroups that can be resident at once (one per compute unit: the tile takes 128 KB of
-// LDS), queried once per device.
+// LDS), queried once per device.  Every kernel asking has the same 1024-thread, 128 KB LDS
+// shape, so one cache serves them; concurrent first calls may both query and store the same
+// value.
 static int cols2_capacity(const void* fn) {
-  static int cap[64];
+  static std::atomic<int> cap[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cap[dev] > 0) return cap[dev];
+  const int known = cap[dev].load(std::memory_order_relaxed);
+  if (known > 0) return known;
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 1024, kColsLdsBytes) != hipSuccess)
     return 0;
-  cap[dev] = cus * per_cu;
-  return cap[dev];
+  cap[dev].store(cus * per_cu, std::memory_order_relaxed);
+  return cus * per_cu;
 }
 
 // Scratch layout of one pass: arrival counters (padded to 256 bytes), then the column maxima.

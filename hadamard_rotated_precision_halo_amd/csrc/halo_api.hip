@@ -74,7 +74,7 @@ halo_status check_fq(const void* x, halo_dtype xt, int64_t rows, int64_t cols, i
   if (xt != HALO_F32 && xt != HALO_BF16) return HALO_ERR_DTYPE;
   if (qt_index(qt) < 0) return HALO_ERR_DTYPE;
   if (axis != HALO_ALONG_ROWS && axis != HALO_ALONG_COLS) return HALO_ERR_SHAPE;
-  if (rows < 0 || cols < 0 || rows >= kMaxDim || cols >= kMaxDim) return HALO_ERR_SHAPE;
+  if (rows >= kMaxDim || cols >= kMaxDim) return HALO_ERR_SHAPE;
   if (ldx < cols || ldx < 1) return HALO_ERR_SHAPE;
   if (!valid_block(block)) return HALO_ERR_BLOCK;
   const int64_t L = axis == HALO_ALONG_ROWS ? cols : rows;
