@@ -421,6 +421,24 @@ def main():
         step_opt(i)
     ms_opt = time_events(step_opt, args.steps, torch)
 
+    # ---- the backward again with block 4096: one block over the whole contraction ----
+    ws_b4 = torch.empty(H.linear_workspace_bytes(M, N, K, torch.int8, True, block=4096),
+                        dtype=torch.uint8, device="cuda:0")
+
+    def bwd_4096(i):
+        X, W, DY = sets[i % N_SETS]
+        H.linear_bwd(DY, X, W, 4096, dx=dx, dw=dw, workspace=ws_b4)
+
+    def bwd_256(i):
+        X, W, DY = sets[i % N_SETS]
+        H.linear_bwd(DY, X, W, BLOCK, dx=dx, dw=dw, workspace=ws_b)
+
+    for i in range(3):
+        bwd_4096(i)
+        bwd_256(i)
+    ms_bwd4096 = time_events(bwd_4096, args.steps, torch)
+    ms_bwd256 = time_events(bwd_256, args.steps, torch)
+
     # ---- per-kernel measurements (same kernels, same shapes, HIP events on the stream) ----
     t = measure_kernels(H, torch, sets, args.kernel_iters)
     t_gemm, t_rows, t_cols = t["gemm_i8_4096"], t["fq_rows_4096"], t["fq_cols_4096"]
@@ -477,6 +495,13 @@ def main():
             "rows_signs_sr": hbm_pass("fq_rows_opt_4096"),
             "cols_signs_sr": hbm_pass("fq_cols_opt_4096"),
             "rows_padded_4000_to_4096": hbm_pass("fq_rows_pad_4000", FQ_PAD_BYTES),
+        },
+        "bwd_block_4096": {
+            "ms": round(ms_bwd4096, 4),
+            "effective_tops": round(2 * GEMM_OPS / (ms_bwd4096 * 1e-3) / 1e12, 3),
+            "ms_block_256": round(ms_bwd256, 4),
+            "what": "halo_linear_bwd alone (dX and dW) with block 4096 on N and M, beside the "
+                    "same call with the step's block 256",
         },
     }
     if not args.no_cpu_baseline:

@@ -87,8 +87,12 @@ WORKLOADS = {
     "c5_fwdbwd_16384x14336x4096_bf16_b512_fp8": dict(m=16384, n=14336, k=4096, block=512,
                                                      io=BF16, q="e4m3", gq="e5m2", fwd=True,
                                                      bwd=True),
+    # the 4096^3 backward again with one block over the whole 4096-long contraction
+    "c3_bwd_4096x4096x4096_bf16_b4096_i8": dict(m=4096, n=4096, k=4096, block=4096, io=BF16,
+                                                q="i8", gq="i8", fwd=False, bwd=True),
 }
 SEEDS = {name: 1000 + i for i, name in enumerate(WORKLOADS)}
+SEEDS["c3_bwd_4096x4096x4096_bf16_b4096_i8"] = SEEDS["c3_bwd_4096x4096x4096_bf16_b256_i8"]
 
 
 def workload(name, with_grad=None):
