@@ -28,6 +28,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -72,11 +73,19 @@ PASSES = {
 }
 
 
+def code_text(src):
+    """C++ source without its comments and with whitespace runs collapsed: what the compiler
+    sees, so that a comment edit does not mark the kernels as changed."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def source_hash(paths):
     h = hashlib.sha256()
     for p in paths:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 

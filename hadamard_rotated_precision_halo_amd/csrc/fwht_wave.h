@@ -21,18 +21,19 @@
 // (no barrier), or a workgroup of ceil(L / 4096) waves per row with one LDS exchange of wave
 // maxima.
 //
-// Columns kernel.  A workgroup of 16 waves owns a tile of C = 65536 / R columns by R rows
-// (R = 1024 for long columns): each lane loads 8 consecutive rows of 8 adjacent columns with
-// full 128-byte row segments, transposes them in registers with v_perm_b32 (8 rows of one
-// column in one 16-byte word) and writes them to LDS in the order the compute waves read them
-// (bank-conflict-free by an XOR swizzle); the waves then run the slice computation on column
-// segments of R rows.  When a column is longer than R, the P = rows / R workgroups of one
-// column strip combine their partial maxima through device-scope atomics: each max-reduces
-// its maxima into the strip's column maxima, increments the strip's arrival counter, and
-// waits until all P have arrived.  The
-// P tasks of a strip are consecutive workgroups and workgroups are dispatched in index order,
-// so the wait always ends (see the launcher); a bounded spin guards it regardless.  The input
-// is read once and the codes written once.
+// Columns kernel.  A workgroup of 16 waves owns a tile of C = 65536 / R columns by R rows:
+// whole columns (R = 4096, C = 16: 32-byte row segments, no exchange) for columns of up to
+// 4096 rows, R = 1024 (C = 64: full 128-byte row segments) for longer ones.  Each lane loads 8
+// consecutive rows of 8 adjacent columns, transposes them in registers with v_perm_b32 (8 rows
+// of one column in one 16-byte word) and writes them to LDS in the order the compute waves
+// read them (bank-conflict-free by an XOR swizzle); the waves then run the slice computation
+// on column segments of R rows.  When a column is longer than R, the P = rows / R workgroups
+// of one column strip combine their partial maxima through device-scope atomics: each
+// max-reduces its maxima into the strip's column maxima, increments the strip's arrival
+// counter, and waits until all P have arrived.  The P tasks of a strip are consecutive
+// workgroups and workgroups are dispatched in index order, so the wait always ends (see the
+// launcher); a bounded spin guards it regardless.  The input is read once and the codes
+// written once.
 //
 // Options (every kernel here): the randomised transform's signs ("企业官网建设流程全解析" s4.2,
 // one bit per element, applied before the butterflies), zero padding of vectors whose length
