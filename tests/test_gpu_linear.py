@@ -143,6 +143,54 @@ def test_repeat_runs_bit_identical():
         assert torch.equal(dx, dx0) and torch.equal(dw, dw0)
 
 
+def test_concurrent_host_threads():
+    # Calls are documented as thread-safe: four host threads, each on its own stream, run
+    # forward + backward on their own inputs at the same time (ctypes releases the GIL around
+    # the C calls); every result equals the same call made alone, bit for bit.
+    import threading
+    m, n, k, b = 512, 512, 1024, 256
+    cases = []
+    for t in range(4):
+        x, w, dy = synth.layer(m, n, k, seed=60 + t)
+        cases.append((to_dev(x), to_dev(w), to_dev(dy)))
+    ref = []
+    for X, W, DY in cases:
+        y = H.linear_fwd(X, W, b)
+        dx, dw = H.linear_bwd(DY, X, W, b)
+        ref.append((y, dx, dw))
+    torch.cuda.synchronize()
+    out, errs = [None] * len(cases), []
+    start = threading.Barrier(len(cases))
+
+    def work(i):
+        try:
+            s = torch.cuda.Stream()
+            X, W, DY = cases[i]
+            start.wait(timeout=30)
+            res = []
+            with torch.cuda.stream(s):
+                for _ in range(3):
+                    y = H.linear_fwd(X, W, b)
+                    dx, dw = H.linear_bwd(DY, X, W, b)
+                    res.append((y, dx, dw))
+            s.synchronize()
+            out[i] = res
+        except Exception as e:  # reported below, in the test's own thread
+            errs.append(e)
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=60)
+    assert not errs, errs
+    for i, res in enumerate(out):
+        assert res is not None, f"thread {i} did not finish"
+        for y, dx, dw in res:
+            assert torch.equal(y, ref[i][0])
+            assert torch.equal(dx, ref[i][1]) and torch.equal(dw, ref[i][2])
+
+
 def test_non_default_stream():
     m, n, k, b = 256, 256, 1024, 256
     x, w, _ = synth.layer(m, n, k, seed=41, with_grad=False)
