@@ -30,10 +30,10 @@
 // on column segments of R rows.  When a column is longer than R, the P = rows / R workgroups
 // of one column strip combine their partial maxima through device-scope atomics: each
 // max-reduces its maxima into the strip's column maxima, increments the strip's arrival
-// counter, and waits until all P have arrived.  The P tasks of a strip are consecutive
-// workgroups and workgroups are dispatched in index order, so the wait always ends (see the
-// launcher); a bounded spin guards it regardless.  The input is read once and the codes
-// written once.
+// counter, and waits until all P have arrived.  The tasks of a group of up to 8 strips are
+// consecutive workgroups, the parts of each strip 8 apart (one XCD), and workgroups are
+// dispatched in index order, so the wait always ends (see the launcher); a bounded spin guards
+// it regardless.  The input is read once and the codes written once.
 //
 // Options (every kernel here): the randomised transform's signs ("企业官网建设流程全解析" s4.2,
 // one bit per element, applied before the butterflies), zero padding of vectors whose length
@@ -459,6 +459,7 @@ struct ColsProb {
   float* colmax;
   uint32_t* arrive;
   int R, P, C;
+  int gs;  // strips per task group (see cols_task), 1 or 8
 };
 
 // One task (one R-row part of one column strip) of a column pass, run by a whole workgroup of
@@ -477,7 +478,7 @@ __device__ __forceinline__ void cols_task(const ColsProb& pr, int64_t ltask, uin
   uint32_t* arrive = pr.arrive;
   const int64_t ncols = a.nvec;
   const uint16_t* __restrict__ xin = reinterpret_cast<const uint16_t*>(a.x);
-  // the P tasks of a strip are consecutive (see the launcher); with one task per strip the
+  // the tasks of a strip group are consecutive (see the launcher); with one task per strip the
   // strips are spread so that each XCD (task i runs on XCD (i + offset) % 8) gets a contiguous
   // run of them: neighbouring strips share 128-byte lines, which its L2 then fetches once
   int64_t strip;
@@ -487,8 +488,14 @@ __device__ __forceinline__ void cols_task(const ColsProb& pr, int64_t ltask, uin
     strip = x < r ? x * (q + 1) + s : r * (q + 1) + (x - r) * q + s;
     part = 0;
   } else {
-    strip = ltask / P;
-    part = (int)(ltask % P);
+    // groups of gs strips, gs P tasks: part p of strip x of a group is task x + n p (n = the
+    // group's strips), so with gs = 8 the P parts of a strip are 8 workgroups apart, on one
+    // XCD, and their exchange stays in that XCD (measured faster than parts spread over
+    // XCDs); gs = 1 makes them consecutive
+    const int64_t gp = (int64_t)pr.gs * P, g = ltask / gp, j = ltask - g * gp;
+    const int64_t T = (a.nvec + C - 1) / C, n = T - g * pr.gs < pr.gs ? T - g * pr.gs : pr.gs;
+    strip = g * pr.gs + j % n;
+    part = (int)(j / n);
   }
   const int64_t c0 = strip * C;
 
@@ -678,6 +685,11 @@ static int cols2_capacity(const void* fn) {
   return cus * per_cu;
 }
 
+// Strips per task group of a pass with P parts per strip: 8 (one XCD per strip) when 8 P
+// workgroups fit on the device at once, so that a group's waits can all end (the argument of
+// the launchers below, with groups in place of strips); else 1.
+static int cols2_group(int P, int capacity) { return P > 1 && 8 * P <= capacity ? 8 : 1; }
+
 // Scratch layout of one pass: arrival counters (padded to 256 bytes), then the column maxima.
 static void cols2_scratch(void* ws, int64_t strips, float** colmax, uint32_t** arrive,
                           int64_t* words) {
@@ -694,6 +706,7 @@ static ColsProb cols2_prob(const FqArgs& a, void* ws, int64_t* tasks, int64_t* s
   pr.R = cols2_rows_per_task(a.len, a.block);
   pr.P = (int)(a.len / pr.R);
   pr.C = 65536 / pr.R;
+  pr.gs = 1;
   const int64_t strips = (a.nvec + pr.C - 1) / pr.C;
   *tasks = (a.nvec == 0 || a.len == 0) ? 0 : strips * pr.P;
   *scratch_words = 0;
@@ -735,14 +748,18 @@ static hipError_t launch_cols2_t(const FqArgs& a0, void* ws0, const FqArgs* a1, 
   }
   const int64_t tasks = t0 + t1;
   if (tasks == 0) return hipSuccess;
-  // one task per workgroup; the P tasks of a strip are consecutive workgroups.  A waiting
-  // workgroup only waits for the other members of its own group, and the hardware dispatches
-  // workgroups in index order on each XCD: every group below the lowest undispatched
-  // workgroup is fully dispatched and finishes, freeing room for the rest, so every wait ends
-  // as long as one group fits on the device at once.
+  // one task per workgroup; the tasks of a group of gs strips (gs P tasks) are consecutive
+  // workgroups.  A waiting workgroup only waits for the other members of its own group, and
+  // the hardware dispatches workgroups in index order on each XCD: every group below the
+  // lowest undispatched workgroup is fully dispatched and finishes, freeing room for the
+  // rest, so every wait ends as long as one group fits on the device at once (gs P <= the
+  // capacity, which cols2_group ensures).
   const int P = p0.P > p1.P ? p0.P : p1.P;
-  if (P > 1 && cols2_capacity(reinterpret_cast<const void*>(fn)) < P)
-    return hipErrorInvalidConfiguration;
+  if (P > 1) {
+    const int cap = cols2_capacity(reinterpret_cast<const void*>(fn));
+    if (cap < P) return hipErrorInvalidConfiguration;
+    p0.gs = p1.gs = cols2_group(P, cap);
+  }
   hipLaunchKernelGGL((fq_cols2_kernel<B, QT, SR>), dim3((unsigned)tasks), dim3(1024),
                      kColsLdsBytes, st, p0, p1, t0, tasks);
   return hipGetLastError();
@@ -791,8 +808,13 @@ static hipError_t launch_batch_t(const FqArgs* rows, const FqArgs& cw, void* ws_
   int P = fb.cw.P;
   if (fb.cdy.P > P) P = fb.cdy.P;
   if (fb.cx.P > P) P = fb.cx.P;
-  if (P > 1 && cols2_capacity(reinterpret_cast<const void*>(fn)) < P)
-    return hipErrorInvalidConfiguration;
+  if (P > 1) {
+    const int cap = cols2_capacity(reinterpret_cast<const void*>(fn));
+    if (cap < P) return hipErrorInvalidConfiguration;
+    fb.cw.gs = cols2_group(fb.cw.P, cap);
+    fb.cdy.gs = cols2_group(fb.cdy.P, cap);
+    fb.cx.gs = cols2_group(fb.cx.P, cap);
+  }
   hipLaunchKernelGGL((fq_batch_kernel<B, QG, QW, SR>), dim3((unsigned)grid), dim3(1024),
                      kColsLdsBytes, st, fb);
   return hipGetLastError();
