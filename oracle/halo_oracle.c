@@ -63,10 +63,10 @@
  *                 m = fl32(qmax / a), q = rne(y * m) with the product taken exactly
  *                 (INT8) or rounded to fp32 first (FP8).  Where qmax / a overflows (a
  *                 vector of values below about qmax / FLT_MAX) y and a are first scaled
- *                 by 2^64, exactly, and the decision taken on the scaled vector.  The 1/sqrt(b) factor cancels
- *                 between y and max|y| in exact arithmetic, so both are evaluations of
- *                 the same formula; precision 32 is the one a single-precision device
- *                 takes its integer decisions in.  Stochastic rounding there starts from
+ *                 by 2^64, exactly, and the decision taken on the scaled vector.  The
+ *                 1/sqrt(b) factor cancels between y and max|y| in exact arithmetic, so
+ *                 both are evaluations of the same formula; precision 32 is the one a
+ *                 single-precision device takes its integer decisions in.  Stochastic rounding there starts from
  *                 t = fl32(y * m) and forms r, floor(r), the fraction and the comparison
  *                 with u in fp32 (each of these steps is exact except where the fraction
  *                 of a negative t below 2^-24 in magnitude rounds to 1).
