@@ -336,6 +336,67 @@ def summarize_pmc(fetch_dir, write_dir, command):
     return res, "\n".join(lines) + "\n"
 
 
+def bench_workload(name, args):
+    """One named workload (fwd and / or bwd, as its configuration lists) on the inputs of the
+    full-size parity tests (same seeded generator): one JSON line with times and rates.  These
+    are the parity workloads, not the benchmark's headline line."""
+    import torch
+    import hadamard_rotated_precision_halo_amd as H
+    import synth
+
+    torch.cuda.set_device(0)
+    print(f"{name}: generating the inputs", file=sys.stderr, flush=True)
+    cfg, x, w, dy = synth.workload(name)
+    print(f"{name}: inputs ready, timing", file=sys.stderr, flush=True)
+    m, n, k, b = cfg["m"], cfg["n"], cfg["k"], cfg["block"]
+    codes = {"i8": torch.int8, "e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
+    qd, gqd = codes[cfg["q"]], codes[cfg["gq"]]
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return to_dev(a, torch)
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda:0")
+
+    X, W = dev(x), dev(w)
+    DY = dev(dy) if cfg["bwd"] else None
+    del x, w, dy
+    io = torch.float32 if cfg["io"] == synth.F32 else torch.bfloat16
+    out = {"metric": "HALO linear effective TOP/s", "unit": "TOP/s", "workload": name,
+           "m": m, "n": n, "k": k, "block": b, "codes": [cfg["q"], cfg["gq"]],
+           "data": "synthetic", "steps": args.steps, "warmup": args.warmup}
+    gop = 2.0 * m * n * k / 1e9
+    total_ms, total_gop = 0.0, 0.0
+    if cfg["fwd"]:
+        y = torch.empty((m, n), dtype=io, device="cuda:0")
+        ws_f = torch.empty(H.linear_workspace_bytes(m, n, k, qd, False, block=b),
+                           dtype=torch.uint8, device="cuda:0")
+
+        def fwd(i):
+            H.linear_fwd(X, W, b, q_dtype=qd, y=y, workspace=ws_f)
+        for i in range(args.warmup):
+            fwd(i)
+        ms = time_events(fwd, args.steps, torch)
+        out["fwd_ms"], out["fwd_tops"] = round(ms, 4), round(gop / ms, 1)
+        total_ms, total_gop = total_ms + ms, total_gop + gop
+    if cfg["bwd"]:
+        dx = torch.empty((m, k), dtype=io, device="cuda:0")
+        dw = torch.empty((n, k), dtype=io, device="cuda:0")
+        ws_b = torch.empty(H.linear_workspace_bytes(m, n, k, qd, True, block=b),
+                           dtype=torch.uint8, device="cuda:0")
+
+        def bwd(i):
+            H.linear_bwd(DY, X, W, b, q_dtype=qd, grad_q_dtype=gqd, dx=dx, dw=dw,
+                         workspace=ws_b)
+        for i in range(args.warmup):
+            bwd(i)
+        ms = time_events(bwd, args.steps, torch)
+        out["bwd_ms"], out["bwd_tops"] = round(ms, 4), round(2 * gop / ms, 1)
+        total_ms, total_gop = total_ms + ms, total_gop + 2 * gop
+    out["ms_per_step"] = round(total_ms, 4)
+    out["value"] = round(total_gop / total_ms, 1)  # GOP per ms = TOP/s
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -349,6 +410,7 @@ def main():
     ap.add_argument("--command", default="", help="profiling command recorded in a summary")
     ap.add_argument("--out", help="summary file to write")
     ap.add_argument("--last", type=int, default=0, help="trace calls per pass to average")
+    ap.add_argument("--workload", help="time one named parity workload instead (see synth)")
     args = ap.parse_args()
 
     if args.summarize_stats:
@@ -372,6 +434,10 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload:
+        bench_workload(args.workload, args)
+        return
 
     import torch
     import hadamard_rotated_precision_halo_amd as H
