@@ -95,3 +95,36 @@ def bf16_round_np(x):
     """fp64 -> nearest-even bf16 value (through fp32), as float64."""
     import synth
     return synth.bf16_to_f32(synth.bf16_bits(np.asarray(x, dtype=np.float32))).astype(np.float64)
+
+
+# Philox key and counter words 2-3 of the stochastic-rounding tests, as the oracle takes them
+# and as the binding's 64-bit seed / counter
+KEY, CTR = (0x3C6EF372, 0xA54FF53A), (0x510E527F, 0x9B05688C)
+SEED64 = KEY[0] | (KEY[1] << 32)
+COUNTER64 = CTR[0] | (CTR[1] << 32)
+
+
+def signs_dev(words):
+    """Packed sign words (uint32) as the int32 device tensor the binding takes."""
+    return torch.from_numpy(np.ascontiguousarray(words).view(np.int32)).to(DEV)
+
+
+def fp8_extra(a, aax, at, b, bax, bt, block, aopt=None, bopt=None):
+    """Accumulation bound of the FP8 matrix cores for the product of the oracle's codes of
+    operand a (vectors along axis aax, options aopt) and operand b, in output units."""
+    qa, sa = O.fwht_quant(a, aax, block, at, precision=32, **(aopt or {}))
+    qb, sb = O.fwht_quant(b, bax, block, bt, precision=32, **(bopt or {}))
+    absum = O.matmul_f64(np.abs(O.fp8_table(at)[qa]), np.abs(O.fp8_table(bt)[qb]))
+    return fp8_acc_bound(absum, qa.shape[1]) * np.outer(sa, sb) * (1 + 1e-6)
+
+
+def bound_ok(got, ref, rel, extra=0.0):
+    """Elementwise |got - ref| <= rel |ref| (+ a floor of 1e-6 max |ref|) + extra; returns
+    (all within, number outside)."""
+    scale = np.abs(ref) + 1e-6 * np.abs(ref).max()
+    bad = np.abs(got - ref) > rel * scale + extra
+    return not bad.any(), int(bad.sum())
+
+
+def to_np64(t):
+    return t.float().cpu().numpy().astype(np.float64)

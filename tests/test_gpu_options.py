@@ -17,19 +17,14 @@ import torch
 import hadamard_rotated_precision_halo_amd as H
 import oracle as O
 import synth
-from parity_util import DEV, Q_TORCH, assert_codes_close_to_fp64, codes_to_np, fp8_acc_bound, \
-    rel_fro, to_dev
+from parity_util import COUNTER64, CTR, DEV, KEY, Q_TORCH, SEED64, assert_codes_close_to_fp64, \
+    codes_to_np, rel_fro, to_dev
+from parity_util import bound_ok as _bound_ok, fp8_extra as _fp8_extra, signs_dev as _signs_dev, \
+    to_np64 as _np
 
 pytestmark = pytest.mark.gpu
 
-KEY, CTR = (0x3C6EF372, 0xA54FF53A), (0x510E527F, 0x9B05688C)
-SEED64 = KEY[0] | (KEY[1] << 32)
-COUNTER64 = CTR[0] | (CTR[1] << 32)
 QT = {"i8": O.I8, "e4m3": O.E4M3, "e5m2": O.E5M2}
-
-
-def _signs_dev(words):
-    return torch.from_numpy(np.ascontiguousarray(words).view(np.int32)).to(DEV)
 
 
 def _input(rows, cols, io, seed):
@@ -120,23 +115,6 @@ def test_signs_from_a_seed_are_shared_and_orthogonal():
     prod = (yx.double() @ yw.double().T).cpu().numpy()
     exact = x.astype(np.float64) @ w.astype(np.float64).T
     assert rel_fro(prod, exact) < 1e-6
-
-
-def _fp8_extra(a, aax, at, b, bax, bt, block, aopt, bopt):
-    qa, sa = O.fwht_quant(a, aax, block, at, precision=32, **aopt)
-    qb, sb = O.fwht_quant(b, bax, block, bt, precision=32, **bopt)
-    absum = O.matmul_f64(np.abs(O.fp8_table(at)[qa]), np.abs(O.fp8_table(bt)[qb]))
-    return fp8_acc_bound(absum, qa.shape[1]) * np.outer(sa, sb) * (1 + 1e-6)
-
-
-def _bound_ok(got, ref, rel, extra=0.0):
-    scale = np.abs(ref) + 1e-6 * np.abs(ref).max()
-    bad = np.abs(got - ref) > rel * scale + extra
-    return not bad.any(), int(bad.sum())
-
-
-def _np(t):
-    return t.float().cpu().numpy().astype(np.float64)
 
 
 FWD = [  # m, n, k, block, io, q, signs
