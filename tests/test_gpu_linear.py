@@ -12,29 +12,16 @@ import torch
 import hadamard_rotated_precision_halo_amd as H
 import oracle as O
 import synth
-from parity_util import Q_TORCH, fp8_acc_bound, rel_fro, to_dev
+from parity_util import Q_TORCH, bound_ok, rel_fro, to_dev
+from parity_util import fp8_extra as _fp8_extra, to_np64 as _np
 
 pytestmark = pytest.mark.gpu
 
 QT = {"i8": O.I8, "e4m3": O.E4M3, "e5m2": O.E5M2}
 
 
-def _np(t):
-    return t.float().cpu().numpy().astype(np.float64)
-
-
 def _elementwise_bound(got, ref, rel, extra=0.0):
-    scale = np.abs(ref) + 1e-6 * np.abs(ref).max()
-    return (np.abs(got - ref) <= rel * scale + extra).all()
-
-
-def _fp8_extra(a, aax, at, b, bax, bt, block):
-    """Accumulation bound of the FP8 matrix cores for the product of the oracle's codes of
-    operand a (vectors along axis aax) and operand b, in output units (scales applied)."""
-    qa, sa = O.fwht_quant(a, aax, block, at, precision=32)
-    qb, sb = O.fwht_quant(b, bax, block, bt, precision=32)
-    absum = O.matmul_f64(np.abs(O.fp8_table(at)[qa]), np.abs(O.fp8_table(bt)[qb]))
-    return fp8_acc_bound(absum, qa.shape[1]) * np.outer(sa, sb) * (1 + 1e-6)
+    return bound_ok(got, ref, rel, extra)[0]
 
 
 FWD = [  # m, n, k, block, io, q
