@@ -56,6 +56,9 @@ KERNEL_SOURCES = ["hadamard_rotated_precision_halo_amd/csrc/gemm.hip",
                   "hadamard_rotated_precision_halo_amd/csrc/fwht_wave_sr.hip",
                   "hadamard_rotated_precision_halo_amd/csrc/halo_device.h"]
 K_PAD = 4000                                # rows of 4000 elements, padded to 4096 codes
+# algorithmic bytes of the rotation passes over a 16384 x 14336 bf16 gradient (codes + scales)
+LARGE_BYTES = 16384 * 14336 * 3 + 4 * 16384
+LARGE_COLS_BYTES = 16384 * 14336 * 3 + 4 * 14336
 FQ_PAD_BYTES = M * K_PAD * 2 + M * K + 4 * M
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic_4096.json")
 
@@ -336,6 +339,38 @@ def summarize_pmc(fetch_dir, write_dir, command):
     return res, "\n".join(lines) + "\n"
 
 
+def measure_large_passes(H, torch, iters):
+    """The rotation passes at the largest gradient shape (16384 x 14336 bf16, block 512, E5M2
+    codes, as in the 16384-token MLP-up workload): per-launch time (ms) of the rows pass (along
+    14336) and of the columns pass (along 16384 tokens, partial maxima exchanged), through the
+    C entry point.  Inputs drawn on the GPU: a memory-bound pass's speed does not depend on
+    the values."""
+    P, ld, code = H._ptr, H._ld, H._code
+    st = H._stream(None)
+    rows_, cols_, blk = 16384, 14336, 512
+    e5 = torch.float8_e5m2
+    xs = [(torch.randn(rows_, cols_, device="cuda:0") * 1e-3).to(torch.bfloat16)
+          for _ in range(2)]
+    q = torch.empty(rows_ * cols_, dtype=torch.uint8, device="cuda:0")
+    sc = torch.empty(max(rows_, cols_), dtype=torch.float32, device="cuda:0")
+    ws = torch.empty(max(H.fwht_quant_workspace_bytes(rows_, cols_, H.COLS, blk), 256),
+                     dtype=torch.uint8, device="cuda:0")
+
+    def args(x, axis):
+        nvec, lp = (rows_, cols_) if axis == H.ROWS else (cols_, rows_)
+        return (P(x), code(x.dtype), rows_, cols_, ld(x), axis, blk, code(e5), P(q), lp,
+                P(sc), None, P(ws), ws.numel(), st)
+
+    out = {}
+    for key, axis in (("rows", H.ROWS), ("cols", H.COLS)):
+        f = _c_launcher(H, "halo_fwht_quant_ex", [args(x, axis) for x in xs])
+        for i in range(3):
+            f(i)
+        out[key] = float(np.median([time_events(f, iters, torch) for _ in range(3)]))
+    del xs, q
+    return out
+
+
 def bench_workload(name, args):
     """One named workload (fwd and / or bwd, as its configuration lists) on the inputs of the
     full-size parity tests (same seeded generator): one JSON line with times and rates.  These
@@ -516,6 +551,7 @@ def main():
 
     # ---- per-kernel measurements (same kernels, same shapes, HIP events on the stream) ----
     t = measure_kernels(H, torch, sets, args.kernel_iters)
+    t_large = measure_large_passes(H, torch, max(5, args.kernel_iters // 6))
     t_gemm, t_rows, t_cols = t["gemm_i8_4096"], t["fq_rows_4096"], t["fq_cols_4096"]
     gemm_tops = GEMM_OPS / (t_gemm * 1e-3) / 1e12
     rows_gbs = FQ_BYTES / (t_rows * 1e-3) / 1e9
@@ -570,6 +606,15 @@ def main():
             "rows_signs_sr": hbm_pass("fq_rows_opt_4096"),
             "cols_signs_sr": hbm_pass("fq_cols_opt_4096"),
             "rows_padded_4000_to_4096": hbm_pass("fq_rows_pad_4000", FQ_PAD_BYTES),
+        },
+        "fwht_quant_16384x14336": {
+            "what": "the rotation passes at the largest gradient shape: 16384 x 14336 bf16, "
+                    "block 512, E5M2 codes; rows along 14336, columns along the 16384 tokens "
+                    "(16 parts per column, partial maxima exchanged)",
+            "rows": hbm(LARGE_BYTES / (t_large["rows"] * 1e-3) / 1e9, t_large["rows"],
+                        "fq_rows_16384x14336", LARGE_BYTES),
+            "cols": hbm(LARGE_COLS_BYTES / (t_large["cols"] * 1e-3) / 1e9, t_large["cols"],
+                        "fq_cols_16384x14336", LARGE_COLS_BYTES),
         },
         "bwd_block_4096": {
             "ms": round(ms_bwd4096, 4),
