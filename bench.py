@@ -54,7 +54,8 @@ KERNEL_SOURCES = ["hadamard_rotated_precision_halo_amd/csrc/gemm.hip",
                   "hadamard_rotated_precision_halo_amd/csrc/fwht_wave.h",
                   "hadamard_rotated_precision_halo_amd/csrc/fwht_wave.hip",
                   "hadamard_rotated_precision_halo_amd/csrc/fwht_wave_sr.hip",
-                  "hadamard_rotated_precision_halo_amd/csrc/halo_device.h"]
+                  "hadamard_rotated_precision_halo_amd/csrc/halo_device.h",
+                  "hadamard_rotated_precision_halo_amd/csrc/halo_kernels.h"]
 K_PAD = 4000                                # rows of 4000 elements, padded to 4096 codes
 # algorithmic bytes of the rotation passes over a 16384 x 14336 bf16 gradient (codes + scales)
 LARGE_BYTES = 16384 * 14336 * 3 + 4 * 16384
