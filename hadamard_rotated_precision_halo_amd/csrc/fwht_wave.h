@@ -32,8 +32,10 @@
 // max-reduces its maxima into the strip's column maxima, increments the strip's arrival
 // counter, and waits until all P have arrived.  The tasks of a group of up to 8 strips are
 // consecutive workgroups, the parts of each strip 8 apart (one XCD), and workgroups are
-// dispatched in index order, so the wait always ends (see the launcher); a bounded spin guards
-// it regardless.  The input is read once and the codes written once.
+// dispatched in index order, so within one launch the wait always ends (see the launcher).
+// The wait is bounded all the same: where other waiting work holds the compute units, the
+// strip is given up as a whole and its columns get NaN scales (see cols_task).  The input is
+// read once and the codes written once.
 //
 // Options (every kernel here): the randomised transform's signs ("企业官网建设流程全解析" s4.2,
 // one bit per element, applied before the butterflies), zero padding of vectors whose length
@@ -46,6 +48,7 @@
 #include "halo_kernels.h"
 
 #include <atomic>
+#include <cstdlib>
 #include <mutex>
 
 namespace halo {
@@ -461,7 +464,8 @@ struct ColsProb {
   float* colmax;
   uint32_t* arrive;
   int R, P, C;
-  int gs;  // strips per task group (see cols_task), 1 or 8
+  int gs;         // strips per task group (see cols_task), 1 or 8
+  uint32_t spins; // polls of a waiting task before it gives the strip up (see cols_task)
 };
 
 // One task (one R-row part of one column strip) of a column pass, run by a whole workgroup of
@@ -583,23 +587,44 @@ __device__ __forceinline__ void cols_task(const ColsProb& pr, int64_t ltask, uin
       // and an unused return value would let the compiler drop the wait
       asm volatile("s_waitcnt vmcnt(0)" ::"v"(seen) : "memory");
       __syncthreads();
+      // The count word's top bit marks a strip given up.  A task that has polled pr.spins
+      // times without seeing all P sets it, by compare-and-swap and only on a count below P,
+      // so the mark is never set on a complete strip: every task of the strip sees either the
+      // full unmarked count or the mark, never both, and a strip given up is given up by all of
+      // its tasks.  They store NaN scales and zero codes for its columns, a failure the caller
+      // sees, in place of codes from partial maxima.  This happens only when the tasks of a strip
+      // cannot all be resident at once, i.e. when other work that waits (another such pass on
+      // another stream) holds the compute units; within one launch the wait always ends.
+      __shared__ uint32_t s_lost;
       if (t == 0) {
-        const uint32_t before =
-            __hip_atomic_fetch_add(&arrive[strip], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        // the other tasks of this strip are dispatched (workgroups start in index order), so
-        // the count reaches P; the bound only guards against a broken launch.  The last task
-        // to arrive has seen the full count already and does not poll.
-        for (uint32_t it = 0; before + 1 < (uint32_t)P && it < (1u << 20); ++it) {
-          if (__hip_atomic_load(&arrive[strip], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >=
-              (uint32_t)P)
+        constexpr uint32_t kMark = 0x80000000u;
+        uint32_t c =
+            __hip_atomic_fetch_add(&arrive[strip], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) +
+            1u;
+        // c < P: neither complete nor marked (a marked count is >= 2^31 > P).  The last task to
+        // arrive sees the full count at once and does not poll.
+        for (uint32_t it = 0; c < (uint32_t)P; ++it) {
+          if (it >= pr.spins) {
+            // each failed swap returns a changed count (arrivals only add, up to P), so this
+            // ends: marked here (c stays below P), complete, or marked by another task
+            while (c < (uint32_t)P &&
+                   !__hip_atomic_compare_exchange_strong(&arrive[strip], &c, c | kMark,
+                                                         __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT)) {
+            }
+            if (c < (uint32_t)P) c = kMark;
             break;
+          }
           __builtin_amdgcn_s_sleep(2);
+          c = __hip_atomic_load(&arrive[strip], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
+        s_lost = c >= kMark ? 1u : 0u;
       }
       __syncthreads();
       if (t < C && c0 + t < ncols)
-        s_cmax[t] = __uint_as_float(
-            __hip_atomic_load(&cm[c0 + t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        s_cmax[t] = s_lost ? __builtin_nanf("")
+                           : __uint_as_float(__hip_atomic_load(&cm[c0 + t], __ATOMIC_RELAXED,
+                                                               __HIP_MEMORY_SCOPE_AGENT));
       __syncthreads();
       if (valid) mx = s_cmax[w * cpw + seg];
     }
@@ -701,6 +726,17 @@ static void cols2_scratch(void* ws, int64_t strips, float** colmax, uint32_t** a
   *words = (int64_t)(cnt / 4);
 }
 
+// Polls a waiting task of an exchanging column pass makes before it gives its strip up:
+// 2^20 (over a second), or the value of the environment variable HALO_EXCHANGE_SPINS, read at
+// each launch of such a pass (tests set it to 0 to take the give-up path).
+static uint32_t exchange_spins() {
+  const char* e = std::getenv("HALO_EXCHANGE_SPINS");
+  if (e == nullptr || *e == 0) return 1u << 20;
+  char* end = nullptr;
+  const unsigned long long v = std::strtoull(e, &end, 10);
+  return (*end == 0 && v <= 0xffffffffull) ? (uint32_t)v : (1u << 20);
+}
+
 // Geometry and scratch of one column pass (rows = a.len); tasks = 0 for an empty pass.
 static ColsProb cols2_prob(const FqArgs& a, void* ws, int64_t* tasks, int64_t* scratch_words) {
   ColsProb pr{};
@@ -715,6 +751,7 @@ static ColsProb cols2_prob(const FqArgs& a, void* ws, int64_t* tasks, int64_t* s
   if (pr.P > 1 && *tasks > 0) {
     cols2_scratch(ws, strips, &pr.colmax, &pr.arrive, scratch_words);
     *scratch_words += a.nvec;
+    pr.spins = exchange_spins();
   }
   return pr;
 }
