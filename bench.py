@@ -68,8 +68,7 @@ TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic_4096.json")
 PASSES = {
     "gemm_i8_4096": ["halo::gemm_kernel<0"],
     "fq_rows_4096": ["halo::fq_rows2_kernel<unsigned short, 256, 0, false>"],
-    "fq_cols_4096": ["halo::fq_cols_kernel<unsigned short, 256, 0", "halo::fill_zero_kernel",
-                     "halo::finalize_scale_kernel", "halo::fq_cols2_kernel<256, 0, false>"],
+    "fq_cols_4096": ["halo::fq_cols2_kernel<256, 0, false>"],
     "gemm_fp8_4096": ["halo::gemm_kernel<1"],
     "fq_rows_opt_4096": ["halo::fq_rows2_kernel<unsigned short, 256, 0, true>"],
     "fq_cols_opt_4096": ["halo::fq_cols2_kernel<256, 0, true>"],

@@ -48,8 +48,8 @@ def _counter_csv(d, counter, values):
 
 def test_summarize_pmc_calibrates_and_sums_each_pass(tmp_path):
     # the calibration copy reads FETCH 32768 KiB (scale 2) and writes WRITE 65536 KiB
-    # (scale 1); the GEMM pass has two dispatches per call averaged; the columns pass sums
-    # the two kernels it launches
+    # (scale 1); the GEMM pass has two dispatches per call averaged; the columns pass is its
+    # one kernel, not the scratch fill (cols[0]) that longer column passes launch
     gemm = "void halo::gemm_kernel<0, 0, 0, 2, false, 128, 4>(halo::GemmPair)"
     cols = ["void halo::fill_zero_kernel(float*, long)",
             "void halo::fq_cols2_kernel<256, 0, false>(halo::ColsProb, halo::ColsProb, long, long)"]
@@ -64,7 +64,7 @@ def test_summarize_pmc_calibrates_and_sums_each_pass(tmp_path):
     assert res["fetch_scale"] == pytest.approx(2.0) and res["write_scale"] == pytest.approx(1.0)
     b = res["bytes_per_launch"]
     assert b["gemm_i8_4096"] == int(round(2000.0 * 1024 * 2 + 500.0 * 1024))
-    assert b["fq_cols_4096"] == int(round(100.0 * 1024 * 2 + 50.0 * 1024))
+    assert b["fq_cols_4096"] == int(round(99.0 * 1024 * 2 + 48.0 * 1024))
     assert "fq_rows_4096" not in b  # no counters for it: left out, never zero
     assert res["kernel_source_hash"] == bench.source_hash(bench.KERNEL_SOURCES)
     assert text.startswith("command: cmd")
