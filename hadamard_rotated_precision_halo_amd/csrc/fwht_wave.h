@@ -49,7 +49,6 @@
 
 #include <atomic>
 #include <cstdlib>
-#include <mutex>
 
 namespace halo {
 
@@ -756,22 +755,11 @@ static ColsProb cols2_prob(const FqArgs& a, void* ws, int64_t* tasks, int64_t* s
   return pr;
 }
 
-template <typename K>
-static hipError_t set_cols_lds(K* fn) {
-  static std::once_flag once;
-  static hipError_t attr_err = hipSuccess;
-  std::call_once(once, [fn] {
-    attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, kColsLdsBytes);
-  });
-  return attr_err;
-}
-
 template <int B, int QT, bool SR>
 static hipError_t launch_cols2_t(const FqArgs& a0, void* ws0, const FqArgs* a1, void* ws1,
                                  int prezeroed, hipStream_t st) {
   auto* fn = &fq_cols2_kernel<B, QT, SR>;
-  hipError_t e = set_cols_lds(fn);
+  hipError_t e = allow_dynamic_lds<&fq_cols2_kernel<B, QT, SR>>(kColsLdsBytes);
   if (e != hipSuccess) return e;
   int64_t t0 = 0, t1 = 0, w0 = 0, w1 = 0;
   ColsProb p0 = cols2_prob(a0, ws0, &t0, &w0);
@@ -827,7 +815,7 @@ static hipError_t launch_batch_t(const FqArgs* rows, const FqArgs& cw, void* ws_
                                  const FqArgs& cdy, void* ws_dy, const FqArgs& cx, void* ws_x,
                                  hipStream_t st) {
   auto* fn = &fq_batch_kernel<B, QG, QW, SR>;
-  hipError_t e = set_cols_lds(fn);
+  hipError_t e = allow_dynamic_lds<&fq_batch_kernel<B, QG, QW, SR>>(kColsLdsBytes);
   if (e != hipSuccess) return e;
   FqBatch fb{};
   int64_t tw = 0, tdy = 0, tx = 0, scratch = 0;

@@ -35,7 +35,6 @@
 #include "halo_device.h"
 #include "halo_kernels.h"
 
-#include <mutex>
 
 
 namespace halo {
@@ -421,13 +420,8 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_kernel(GemmPair gp) {
 template <int KIND, int AF, int BF, int OUT, bool MASK, int BK>
 static hipError_t launch_cfg(const GemmArgs& g0, const GemmArgs* g1, hipStream_t st) {
   constexpr int WN = GEMM_WN;
-  static std::once_flag once;
-  static hipError_t attr_err = hipSuccess;
-  std::call_once(once, [] {
-    attr_err = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&gemm_kernel<KIND, AF, BF, OUT, MASK, BK, WN>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
-  });
+  const hipError_t attr_err =
+      allow_dynamic_lds<&gemm_kernel<KIND, AF, BF, OUT, MASK, BK, WN>>(LDS_BYTES);
   if (attr_err != hipSuccess) return attr_err;
   GemmPair gp{};
   gp.g[0] = g0;

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace halo {
 
 // Arguments of one fused rotation + quantisation pass.
@@ -92,5 +94,22 @@ hipError_t launch_gemm(const GemmArgs& g, int kind, int afmt, int bfmt, int out,
 // Two products of the same kind, formats and output type in one launch (g1 may be NULL).
 hipError_t launch_gemm_pair(const GemmArgs& g, const GemmArgs* g1, int kind, int afmt, int bfmt,
                             int out, hipStream_t st);
+
+// Let `Kernel` launch with `bytes` of dynamic LDS on the current device.  The attribute belongs
+// to one kernel on one device, so it is set once per kernel and device (concurrent first calls
+// may both set it); a failure is returned, and tried again on the next call.
+template <auto Kernel>
+hipError_t allow_dynamic_lds(int bytes) {
+  static std::atomic<bool> done[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const bool cached = dev >= 0 && dev < 64;
+  if (cached && done[dev].load(std::memory_order_acquire)) return hipSuccess;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(Kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && cached) done[dev].store(true, std::memory_order_release);
+  return e;
+}
 
 }  // namespace halo
