@@ -96,3 +96,36 @@ def test_backward_gives_up_loudly(monkeypatch):
     print(f"call {attempt}: {int(bad_rows.sum())} rows, {int(bad_cols.sum())} columns of dW "
           f"given up", flush=True)
     assert bad.any(), f"no strip was given up in {ATTEMPTS} calls with a spin limit of 0"
+
+
+def test_two_exchanging_passes_on_two_streams(monkeypatch):
+    # The case the bound is for: two such passes overlapping on two streams, whose partly
+    # dispatched strips can together fill the compute units.  With 4096 polls (far above the
+    # few that a strip straddling a wave needs, far below the default) any such stall ends in
+    # milliseconds; every call must still give either the oracle's columns or whole strips
+    # given up.
+    rows, cols, b = 49152, 384, 256
+    rng = np.random.default_rng(1212)
+    x_np = synth.bf16_bits(synth.grads(rng, rows, cols))
+    ref_q, ref_s = O.fwht_quant(x_np, O.COLS, b, O.I8, precision=32)
+    x = to_dev(x_np)
+    nbytes = H.fwht_quant_workspace_bytes(rows, cols, H.COLS, b)
+    ws = [torch.empty(nbytes, dtype=torch.uint8, device=x.device) for _ in range(2)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    monkeypatch.setenv("HALO_EXCHANGE_SPINS", "4096")
+    torch.cuda.synchronize()
+    lost_total = 0
+    for _ in range(8):
+        res = []
+        for i, st in enumerate(streams):
+            with torch.cuda.stream(st):
+                res.append(H.fwht_quant(x, axis=H.COLS, block=b, workspace=ws[i], stream=st))
+        torch.cuda.synchronize()
+        for q, s in res:
+            got_q, got_s = codes_to_np(q), s.cpu().numpy().astype(np.float64)
+            lost = _given_up_or_exact(got_q, got_s, ref_q, ref_s)
+            assert np.array_equal(lost.reshape(-1, 64).all(axis=1),
+                                  lost.reshape(-1, 64).any(axis=1))
+            assert not (q.view(torch.uint8).cpu().numpy()[lost] & 0x7F).any()
+            lost_total += int(lost.sum())
+    print(f"{lost_total} columns given up over 16 overlapping passes", flush=True)
