@@ -725,9 +725,10 @@ static void cols2_scratch(void* ws, int64_t strips, float** colmax, uint32_t** a
   *words = (int64_t)(cnt / 4);
 }
 
-// Polls a waiting task of an exchanging column pass makes before it gives its strip up:
-// 2^20 (over a second), or the value of the environment variable HALO_EXCHANGE_SPINS, read at
-// each launch of such a pass (tests set it to 0 to take the give-up path).
+// Polls a waiting task of an exchanging column pass makes before it gives its strip up (each
+// poll an atomic load and s_sleep 2): 2^20, or the value of the environment variable
+// HALO_EXCHANGE_SPINS, read at each launch of such a pass (tests set it low to take the
+// give-up path).
 static uint32_t exchange_spins() {
   const char* e = std::getenv("HALO_EXCHANGE_SPINS");
   if (e == nullptr || *e == 0) return 1u << 20;

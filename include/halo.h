@@ -26,10 +26,11 @@
  *     the backward pass when m > 4096) are split over workgroups that wait for each other
  *     to combine their maxima.  Within one launch that wait always ends.  Where other work
  *     that waits holds the compute units (e.g. two such passes overlapping on two streams),
- *     it is bounded: after 2^20 polls (over a second; the environment variable
- *     HALO_EXCHANGE_SPINS, read at each launch, sets another count) the workgroups give
- *     their column strip up together, and its columns get NaN scales and zero codes, never
- *     codes from partial maxima.  Order such passes on one stream to avoid it.
+ *     it is bounded: after 2^20 polls (each a device-scope load and a short sleep; the
+ *     environment variable HALO_EXCHANGE_SPINS, read at each launch, sets another count) the
+ *     workgroups give their column strip up together, and its columns get NaN scales and
+ *     zero codes, never codes from partial maxima.  Order such passes on one stream to
+ *     avoid it.
  *   - Alignment: every pointer 16-byte aligned, every leading dimension a multiple of 16
  *     bytes (HALO_ERR_ALIGN otherwise).
  *   - Scales are fp32 dequant multipliers: the vector's absmax after the orthonormal
