@@ -36,14 +36,16 @@ EXPORTS = ("halo_fwht_quant", "halo_fwht_quant_ex", "halo_fwht_quant_workspace_b
 class QuantOpts(ctypes.Structure):
     """halo_quant_opts of include/halo.h."""
     _fields_ = [("signs", ctypes.c_void_p), ("rounding", ctypes.c_int32),
-                ("seed", ctypes.c_uint32 * 2), ("counter", ctypes.c_uint32 * 2)]
+                ("seed", ctypes.c_uint32 * 2), ("counter", ctypes.c_uint32 * 2),
+                ("exchange_polls", ctypes.c_uint32)]
 
 
 class LinearOpts(ctypes.Structure):
     """halo_linear_opts of include/halo.h."""
     _fields_ = [("signs_k", ctypes.c_void_p), ("signs_n", ctypes.c_void_p),
                 ("signs_m", ctypes.c_void_p), ("grad_rounding", ctypes.c_int32),
-                ("seed", ctypes.c_uint32 * 2), ("counter", ctypes.c_uint32 * 2)]
+                ("seed", ctypes.c_uint32 * 2), ("counter", ctypes.c_uint32 * 2),
+                ("exchange_polls", ctypes.c_uint32)]
 
 _TORCH_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.int8: I8,
                torch.float8_e4m3fn: E4M3, torch.float8_e5m2: E5M2, torch.int32: I32}
@@ -172,7 +174,8 @@ def fwht_quant_workspace_bytes(rows, cols, axis, block, x_dtype=torch.bfloat16):
 
 
 def fwht_quant(x, axis=ROWS, block=256, q_dtype=torch.int8, q=None, scale=None, workspace=None,
-               stream=None, signs=None, rounding="nearest", seed=0, counter=0):
+               stream=None, signs=None, rounding="nearest", seed=0, counter=0,
+               exchange_polls=0):
     """Rotate + quantise the rows (axis ROWS) or columns (axis COLS) of x.
 
     Returns (q, scale): q is [rows x Lp] (ROWS) or [cols x Lp] (COLS) of q_dtype
@@ -183,6 +186,8 @@ def fwht_quant(x, axis=ROWS, block=256, q_dtype=torch.int8, q=None, scale=None, 
     pass False to run without it.  `signs`: the randomised transform's packed sign words (an
     int32 device tensor, see hadamard_signs) or None.  `rounding`: "nearest" or "stochastic"
     (Philox key `seed`, counter words 2-3 `counter`, each a 64-bit integer).
+    `exchange_polls`: for columns longer than 4096 rows, the polls a waiting workgroup makes
+    before its strip is given up (NaN scales, zero codes); 0 = the library's default.
     """
     rows, cols = x.shape
     nvec, L = (rows, cols) if axis == ROWS else (cols, rows)
@@ -202,8 +207,8 @@ def fwht_quant(x, axis=ROWS, block=256, q_dtype=torch.int8, q=None, scale=None, 
             ws_ptr, ws_bytes = _ptr(workspace), workspace.numel()
     opts = None
     rnd = _rounding(rounding)
-    if signs is not None or rnd != NEAREST:
-        opts = QuantOpts(_ptr(signs), rnd, _u32x2(seed), _u32x2(counter))
+    if signs is not None or rnd != NEAREST or exchange_polls:
+        opts = QuantOpts(_ptr(signs), rnd, _u32x2(seed), _u32x2(counter), int(exchange_polls))
     st = lib().halo_fwht_quant_ex(_ptr(x), _code(x.dtype), rows, cols, _ld(x), axis, int(block),
                                   _code(q.dtype), _ptr(q), _ld(q), _ptr(scale),
                                   ctypes.byref(opts) if opts is not None else None, ws_ptr,
@@ -273,12 +278,13 @@ def linear_fwd(x, w, block, q_dtype=torch.int8, y=None, y_dtype=None, workspace=
 
 def linear_bwd(dy, x, w, block, q_dtype=torch.int8, grad_q_dtype=None, want_dx=True,
                want_dw=True, dx=None, dw=None, workspace=None, stream=None, signs_n=None,
-               signs_m=None, grad_rounding="nearest", seed=0, counter=0):
+               signs_m=None, grad_rounding="nearest", seed=0, counter=0, exchange_polls=0):
     """dX = dY W (rotated along N) and dW = dY^T X (rotated along M), 8-bit products.
 
     signs_n / signs_m: the randomised transform's sign words along N / M (or None).
     grad_rounding: "nearest" or "stochastic" rounding of the dY codes (Philox key `seed`,
-    counter words 2-3 `counter`; the columns of dY draw with counter word 3 ^ 2^31)."""
+    counter words 2-3 `counter`; the columns of dY draw with counter word 3 ^ 2^31).
+    exchange_polls: as in fwht_quant, for the columns along m."""
     m, k = x.shape
     n = w.shape[0]
     grad_q_dtype = grad_q_dtype or q_dtype
@@ -290,9 +296,9 @@ def linear_bwd(dy, x, w, block, q_dtype=torch.int8, grad_q_dtype=None, want_dx=T
     ws = _workspace(need, x.device, workspace)
     rnd = _rounding(grad_rounding)
     opts = None
-    if signs_n is not None or signs_m is not None or rnd != NEAREST:
+    if signs_n is not None or signs_m is not None or rnd != NEAREST or exchange_polls:
         opts = LinearOpts(None, _ptr(signs_n), _ptr(signs_m), rnd, _u32x2(seed),
-                          _u32x2(counter))
+                          _u32x2(counter), int(exchange_polls))
     st = lib().halo_linear_bwd_ex(_ptr(dy), _ptr(x), _ptr(w), _code(x.dtype), m, n, k,
                                   int(block), _code(q_dtype), _code(grad_q_dtype),
                                   _ptr(dx) if want_dx else None, _ptr(dw) if want_dw else None,

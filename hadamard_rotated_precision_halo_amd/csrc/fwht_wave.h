@@ -48,7 +48,6 @@
 #include "halo_kernels.h"
 
 #include <atomic>
-#include <cstdlib>
 
 namespace halo {
 
@@ -725,18 +724,6 @@ static void cols2_scratch(void* ws, int64_t strips, float** colmax, uint32_t** a
   *words = (int64_t)(cnt / 4);
 }
 
-// Polls a waiting task of an exchanging column pass makes before it gives its strip up (each
-// poll an atomic load and s_sleep 2): 2^20, or the value of the environment variable
-// HALO_EXCHANGE_SPINS, read at each launch of such a pass (tests set it low to take the
-// give-up path).
-static uint32_t exchange_spins() {
-  const char* e = std::getenv("HALO_EXCHANGE_SPINS");
-  if (e == nullptr || *e == 0) return 1u << 20;
-  char* end = nullptr;
-  const unsigned long long v = std::strtoull(e, &end, 10);
-  return (*end == 0 && v <= 0xffffffffull) ? (uint32_t)v : (1u << 20);
-}
-
 // Geometry and scratch of one column pass (rows = a.len); tasks = 0 for an empty pass.
 static ColsProb cols2_prob(const FqArgs& a, void* ws, int64_t* tasks, int64_t* scratch_words) {
   ColsProb pr{};
@@ -751,7 +738,9 @@ static ColsProb cols2_prob(const FqArgs& a, void* ws, int64_t* tasks, int64_t* s
   if (pr.P > 1 && *tasks > 0) {
     cols2_scratch(ws, strips, &pr.colmax, &pr.arrive, scratch_words);
     *scratch_words += a.nvec;
-    pr.spins = exchange_spins();
+    // polls a waiting task makes before it gives its strip up (each an atomic load and
+    // s_sleep 2): the caller's count, else 2^20
+    pr.spins = a.polls != 0 ? a.polls : (1u << 20);
   }
   return pr;
 }

@@ -101,6 +101,7 @@ struct PassOpts {
   const uint32_t* signs = nullptr;
   int sr = 0;
   uint32_t key0 = 0, key1 = 0, ctr2 = 0, ctr3 = 0;
+  uint32_t polls = 0;
 };
 
 PassOpts pass_opts(const halo_quant_opts* o) {
@@ -112,6 +113,7 @@ PassOpts pass_opts(const halo_quant_opts* o) {
   p.key1 = o->seed[1];
   p.ctr2 = o->counter[0];
   p.ctr3 = o->counter[1];
+  p.polls = o->exchange_polls;
   return p;
 }
 
@@ -139,6 +141,7 @@ FqArgs make_fq(const void* x, int64_t rows, int64_t cols, int64_t ldx, halo_axis
   a.key1 = po.key1;
   a.ctr2 = po.ctr2;
   a.ctr3 = po.ctr3;
+  a.polls = po.polls;
   return a;
 }
 
@@ -449,6 +452,7 @@ halo_status halo_linear_bwd_ex(const void* dy, const void* x, const void* w, hal
     gn.ctr2 = gm.ctr2 = opts->counter[0];
     gn.ctr3 = opts->counter[1];
     gm.ctr3 = opts->counter[1] ^ 0x80000000u;
+    on.polls = om.polls = gn.polls = gm.polls = opts->exchange_polls;
   }
   void* qdy = base + p.off[0];
   float* sdy = reinterpret_cast<float*>(base + p.off[1]);

@@ -27,10 +27,9 @@
  *     to combine their maxima.  Within one launch that wait always ends.  Where other work
  *     that waits holds the compute units (e.g. two such passes overlapping on two streams),
  *     it is bounded: after 2^20 polls (each a device-scope load and a short sleep; the
- *     environment variable HALO_EXCHANGE_SPINS, read at each launch, sets another count) the
- *     workgroups give their column strip up together, and its columns get NaN scales and
- *     zero codes, never codes from partial maxima.  Order such passes on one stream to
- *     avoid it.
+ *     exchange_polls option of the _ex calls sets another count) the workgroups give their
+ *     column strip up together, and its columns get NaN scales and zero codes, never codes
+ *     from partial maxima.  Order such passes on one stream to avoid it.
  *   - Alignment: every pointer 16-byte aligned, every leading dimension a multiple of 16
  *     bytes (HALO_ERR_ALIGN otherwise).
  *   - Scales are fp32 dequant multipliers: the vector's absmax after the orthonormal
@@ -237,6 +236,8 @@ typedef struct {
     int32_t rounding;      /* halo_rounding                                               */
     uint32_t seed[2];      /* Philox key (stochastic rounding)                            */
     uint32_t counter[2];   /* Philox counter words 2 and 3 (stochastic rounding)          */
+    uint32_t exchange_polls; /* columns longer than 4096 rows: polls a waiting workgroup  */
+                             /* makes before its strip is given up (0 = 2^20)             */
 } halo_quant_opts;
 
 /*
@@ -266,6 +267,7 @@ typedef struct {
     int32_t grad_rounding;
     uint32_t seed[2];
     uint32_t counter[2];
+    uint32_t exchange_polls;  /* as in halo_quant_opts (the backward's columns along m) */
 } halo_linear_opts;
 
 /* Workspace bytes of the layer calls for one block size (exact; the block decides the padded

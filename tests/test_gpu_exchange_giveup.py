@@ -1,15 +1,15 @@
 """The bounded wait of the single-read columns pass over columns longer than 4096 rows.
 
 The tasks of one column strip wait for each other to combine their partial maxima.  A task
-that polls HALO_EXCHANGE_SPINS times (read at each launch; 2^20 by default) without seeing
+that polls `exchange_polls` times (an option of the _ex calls; 2^20 by default) without seeing
 the whole strip gives the strip up, and then every task of that strip does: its columns get a
 NaN scale and codes that decode to zero, never codes from partial maxima.  A task gives up by
 a compare-and-swap that only succeeds when no other task of its strip arrives during its round
-trip, so a limit of 0 alone rarely gives anything up: the tasks of a strip arrive together.
+trip, so a limit of 1 alone rarely gives anything up: the tasks of a strip arrive together.
 The shapes here make one strip straddle the first wave of workgroups (one 1024-thread
 workgroup per compute unit, 256 of them): columns of 49152 rows split into 48 tasks, so the
 first tasks of the straddling strip arrive a whole task's time before the rest can start, and
-with the limit at 0 they give it up.  Every column must then be either exactly the oracle's
+with the limit at 1 they give it up.  Every column must then be either exactly the oracle's
 (or, for the layer, the same call's with the default limit) or wholly given up, and the pass
 is repeated, up to ATTEMPTS times, until some strip is.  With the default limit, and on the
 same workspace right after, every column is the oracle's.
@@ -37,7 +37,7 @@ def _given_up_or_exact(got_q, got_s, ref_q, ref_s):
 
 
 @pytest.mark.parametrize("qt", [O.I8, O.E4M3])
-def test_columns_pass_gives_up_whole_strips(qt, monkeypatch):
+def test_columns_pass_gives_up_whole_strips(qt):
     # 48 tasks per 64-column strip, 6 strips: tasks 240-287 (strip 5) straddle the first wave
     rows, cols, b = 49152, 384, 256
     rng = np.random.default_rng(808)
@@ -47,9 +47,9 @@ def test_columns_pass_gives_up_whole_strips(qt, monkeypatch):
     ws = torch.empty(H.fwht_quant_workspace_bytes(rows, cols, H.COLS, b), dtype=torch.uint8,
                      device=x.device)
     assert ws.numel() > 0
-    monkeypatch.setenv("HALO_EXCHANGE_SPINS", "0")
     for attempt in range(ATTEMPTS):
-        q, s = H.fwht_quant(x, axis=H.COLS, block=b, q_dtype=Q_TORCH[qt], workspace=ws)
+        q, s = H.fwht_quant(x, axis=H.COLS, block=b, q_dtype=Q_TORCH[qt], workspace=ws,
+                            exchange_polls=1)
         torch.cuda.synchronize()
         got_q, got_s = codes_to_np(q), s.cpu().numpy().astype(np.float64)
         lost = _given_up_or_exact(got_q, got_s, ref_q, ref_s)
@@ -60,16 +60,15 @@ def test_columns_pass_gives_up_whole_strips(qt, monkeypatch):
         if lost.any():
             break
     print(f"call {attempt}: {int(lost.sum())} of {cols} columns given up", flush=True)
-    assert lost.any(), f"no strip was given up in {ATTEMPTS} calls with a spin limit of 0"
+    assert lost.any(), f"no strip was given up in {ATTEMPTS} calls with a limit of 1"
 
-    monkeypatch.delenv("HALO_EXCHANGE_SPINS")
     q, s = H.fwht_quant(x, axis=H.COLS, block=b, q_dtype=Q_TORCH[qt], workspace=ws)
     torch.cuda.synchronize()
     assert np.array_equal(codes_to_np(q), ref_q)
     assert np.array_equal(s.cpu().numpy().astype(np.float64), ref_s)
 
 
-def test_backward_gives_up_loudly(monkeypatch):
+def test_backward_gives_up_loudly():
     # dW = dY^T X contracts over m = 49152 rows: its dY and X column passes exchange maxima,
     # 48 tasks per strip.  The launch runs W's columns (2 tasks), dY's (4 strips, 192 tasks),
     # then X's (8 strips): X's second strip, tasks 242-289, straddles the first wave.
@@ -80,9 +79,8 @@ def test_backward_gives_up_loudly(monkeypatch):
     torch.cuda.synchronize()
     dx_ref, dw_ref = dx_ref.float().cpu().numpy(), dw_ref.float().cpu().numpy()
     assert np.isfinite(dw_ref).all()
-    monkeypatch.setenv("HALO_EXCHANGE_SPINS", "0")
     for attempt in range(ATTEMPTS):
-        dx, dw = H.linear_bwd(dy, x, w, b)
+        dx, dw = H.linear_bwd(dy, x, w, b, exchange_polls=1)
         torch.cuda.synchronize()
         dx, dw = dx.float().cpu().numpy(), dw.float().cpu().numpy()
         assert np.array_equal(dx, dx_ref)  # W's columns (n = 256 rows) do not exchange
@@ -95,10 +93,10 @@ def test_backward_gives_up_loudly(monkeypatch):
             break
     print(f"call {attempt}: {int(bad_rows.sum())} rows, {int(bad_cols.sum())} columns of dW "
           f"given up", flush=True)
-    assert bad.any(), f"no strip was given up in {ATTEMPTS} calls with a spin limit of 0"
+    assert bad.any(), f"no strip was given up in {ATTEMPTS} calls with a limit of 1"
 
 
-def test_two_exchanging_passes_on_two_streams(monkeypatch):
+def test_two_exchanging_passes_on_two_streams():
     # The case the bound is for: two such passes overlapping on two streams, whose partly
     # dispatched strips can together fill the compute units.  With 4096 polls (far above the
     # few that a strip straddling a wave needs, far below the default) any such stall ends in
@@ -112,14 +110,14 @@ def test_two_exchanging_passes_on_two_streams(monkeypatch):
     nbytes = H.fwht_quant_workspace_bytes(rows, cols, H.COLS, b)
     ws = [torch.empty(nbytes, dtype=torch.uint8, device=x.device) for _ in range(2)]
     streams = [torch.cuda.Stream(), torch.cuda.Stream()]
-    monkeypatch.setenv("HALO_EXCHANGE_SPINS", "4096")
     torch.cuda.synchronize()
     lost_total = 0
     for _ in range(8):
         res = []
         for i, st in enumerate(streams):
             with torch.cuda.stream(st):
-                res.append(H.fwht_quant(x, axis=H.COLS, block=b, workspace=ws[i], stream=st))
+                res.append(H.fwht_quant(x, axis=H.COLS, block=b, workspace=ws[i], stream=st,
+                                        exchange_polls=4096))
         torch.cuda.synchronize()
         for q, s in res:
             got_q, got_s = codes_to_np(q), s.cpu().numpy().astype(np.float64)
