@@ -320,64 +320,68 @@ __global__ __launch_bounds__(256) void fq_cols_kernel(FqArgs a) {
   const int tid = threadIdx.x;
   const int grp = tid / G, x = tid % G;
   const int64_t c0 = (int64_t)blockIdx.x * Geo::COLS + grp * NV;  // first column of the lane
-  const int64_t r0 = (int64_t)blockIdx.y * E;                     // first row of the block
   const bool live = c0 < a.nvec;
   const Tin* __restrict__ xin = reinterpret_cast<const Tin*>(a.x);
-
-  float val[NV][U * 8];
-  if (live) {
+  // blocks of E rows, grid-strided over y (the launcher caps the grid's y size)
+  const int64_t nyb = a.len / E;
+  for (int64_t yb = blockIdx.y; yb < nyb; yb += gridDim.y) {
+    const int64_t r0 = yb * E;  // first row of the block
+    float val[NV][U * 8];
+    if (live) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float t[NV][8];
-      const int64_t rb = r0 + u * 8 * G + x * 8;  // first row of the chunk
-      load_cols<Tin, NV>(xin + rb * a.ldx + c0, a.ldx, a.in_len - rb, t);
+      for (int u = 0; u < U; ++u) {
+        float t[NV][8];
+        const int64_t rb = r0 + u * 8 * G + x * 8;  // first row of the chunk
+        load_cols<Tin, NV>(xin + rb * a.ldx + c0, a.ldx, a.in_len - rb, t);
+#pragma unroll
+        for (int c = 0; c < NV; ++c) {
+          if (a.signs) apply_signs8(t[c], a.signs, rb);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) val[c][u * 8 + e] = t[c][e];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < NV; ++c)
+#pragma unroll
+        for (int i = 0; i < U * 8; ++i) val[c][i] = 0.f;
+    }
+#pragma unroll
+    for (int c = 0; c < NV; ++c) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) chunk_butterflies<B>(&val[c][u * 8]);
+      lane_butterflies<G>(val[c], U * 8, x);
+      chunk_stages<U>(val[c]);
+    }
+    uint32_t* colmax = reinterpret_cast<uint32_t*>(a.scale);
+    if constexpr (MODE == 0) {
 #pragma unroll
       for (int c = 0; c < NV; ++c) {
-        if (a.signs) apply_signs8(t[c], a.signs, rb);
+        float mx = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) val[c][u * 8 + e] = t[c][e];
+        for (int i = 0; i < U * 8; ++i) mx = fmaxf(mx, fabsf(val[c][i]));
+        mx = group_max<G>(mx);
+        if (live && x == 0) atomicMax(&colmax[c0 + c], __float_as_uint(mx));
       }
-    }
-  } else {
+    } else {
+      if (!live) return;
+      constexpr int CS = CodeSize<QT>::value;
+      char* qout = reinterpret_cast<char*>(a.q);
 #pragma unroll
-    for (int c = 0; c < NV; ++c)
+      for (int c = 0; c < NV; ++c) {
+        const float amax = __uint_as_float(colmax[c0 + c]);
+        float m = a.inv_sqrt_b, pre = 1.f;
+        if constexpr (QT != 3) m = code_mul(a.qmax, amax, &pre);
+        if (pre != 1.f) {
 #pragma unroll
-      for (int i = 0; i < U * 8; ++i) val[c][i] = 0.f;
-  }
+          for (int i = 0; i < U * 8; ++i) val[c][i] *= pre;
+        }
+        char* p = qout + ((c0 + c) * a.ldq + r0 + x * 8) * CS;
 #pragma unroll
-  for (int c = 0; c < NV; ++c) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) chunk_butterflies<B>(&val[c][u * 8]);
-    lane_butterflies<G>(val[c], U * 8, x);
-    chunk_stages<U>(val[c]);
-  }
-  uint32_t* colmax = reinterpret_cast<uint32_t*>(a.scale);
-  if constexpr (MODE == 0) {
-#pragma unroll
-    for (int c = 0; c < NV; ++c) {
-      float mx = 0.f;
-#pragma unroll
-      for (int i = 0; i < U * 8; ++i) mx = fmaxf(mx, fabsf(val[c][i]));
-      mx = group_max<G>(mx);
-      if (live && x == 0) atomicMax(&colmax[c0 + c], __float_as_uint(mx));
-    }
-  } else {
-    if (!live) return;
-    constexpr int CS = CodeSize<QT>::value;
-    char* qout = reinterpret_cast<char*>(a.q);
-#pragma unroll
-    for (int c = 0; c < NV; ++c) {
-      const float amax = __uint_as_float(colmax[c0 + c]);
-      float m = a.inv_sqrt_b, pre = 1.f;
-      if constexpr (QT != 3) m = code_mul(a.qmax, amax, &pre);
-      if (pre != 1.f) {
-#pragma unroll
-        for (int i = 0; i < U * 8; ++i) val[c][i] *= pre;
+        for (int u = 0; u < U; ++u)
+          store_chunk_opt<QT>(p + u * 8 * G * CS, &val[c][u * 8], m, a, c0 + c,
+                              r0 + x * 8 + u * 8 * G);
       }
-      char* p = qout + ((c0 + c) * a.ldq + r0 + x * 8) * CS;
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        store_chunk_opt<QT>(p + u * 8 * G * CS, &val[c][u * 8], m, a, c0 + c, r0 + x * 8 + u * 8 * G);
     }
   }
 }
@@ -426,7 +430,9 @@ static hipError_t launch_cols_t(const FqArgs& a, hipStream_t st) {
   const unsigned zb = (unsigned)((ncol + 255) / 256);
   hipLaunchKernelGGL(fill_zero_kernel, dim3(zb), dim3(256), 0, st, a.scale, ncol);
   if (a.len > 0) {
-    dim3 grid((unsigned)((ncol + Geo::COLS - 1) / Geo::COLS), (unsigned)(a.len / Geo::E));
+    const int64_t nyb = a.len / Geo::E;  // the kernel strides over the rest
+    dim3 grid((unsigned)((ncol + Geo::COLS - 1) / Geo::COLS),
+              (unsigned)(nyb < 65535 ? nyb : 65535));
     hipLaunchKernelGGL((fq_cols_kernel<Tin, B, QT, 0>), grid, dim3(256), 0, st, a);
     hipLaunchKernelGGL((fq_cols_kernel<Tin, B, QT, 1>), grid, dim3(256), 0, st, a);
   }

@@ -27,7 +27,11 @@ bool fq_cols2_supported(int64_t rows, int64_t cols, int block, int in_bf16, size
   if (!in_bf16 || rows <= 0 || cols <= 0) return false;
   const int R = cols2_rows_per_task(rows, block);
   if (R == 0) return false;
-  return rows / R == 1 || ws_bytes >= fq_cols2_ws_bytes(rows, cols, block, in_bf16);
+  if (rows / R == 1) return true;
+  // the parts of a strip wait for each other, so all of them must fit on the device at once;
+  // longer columns take the two-sweep kernel, which never waits
+  const int cap = cols2_capacity(reinterpret_cast<const void*>(&fq_cols2_kernel<256, 0, false>));
+  return rows / R <= cap && ws_bytes >= fq_cols2_ws_bytes(rows, cols, block, in_bf16);
 }
 
 bool fq_batch_rows_ok(int64_t len) { return len >= 64 && len <= 4096 && 4096 % len == 0; }

@@ -283,3 +283,18 @@ def test_tiny_vectors_stochastic(axis):
                             rounding=O.STOCHASTIC, key=(4, 9), ctr_hi=(8, 3))
     assert np.array_equal(codes_to_np(q), r32)
     assert np.array_equal(s.cpu().numpy().astype(np.float64), s32)
+
+
+@pytest.mark.parametrize("rows,cols,block", [(263168, 16, 256), (525312, 8, 8)])
+def test_very_long_columns(rows, cols, block):
+    # Columns too long for all 1024-row parts of a strip to be resident at once (257 and 513
+    # parts, on 256 compute units) take the two-sweep kernel even with a workspace; the
+    # second shape also needs more than 65535 blocks of 8 rows, which that kernel
+    # grid-strides over.
+    x_np = _input(rows, cols, "bf16", seed=rows % 1000, kind="grad")
+    print(f"columns {rows} x {cols}, block {block}", flush=True)
+    assert H.fwht_quant_workspace_bytes(rows, cols, H.COLS, block) > 0
+    q, s = _run(x_np, H.COLS, block, O.I8)
+    r32, s32 = O.fwht_quant(x_np, O.COLS, block, O.I8, precision=32)
+    assert np.array_equal(q, r32), f"{int((q != r32).sum())} codes differ"
+    assert np.array_equal(s, s32)
