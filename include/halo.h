@@ -198,6 +198,8 @@ halo_status halo_linear_fwd(const void* x, const void* w, halo_dtype io_type, in
  * n and k must be multiples of 8, m >= 1; block as for halo_fwht_quant.  Contraction
  * dimensions that block does not divide are zero-padded as in halo_linear_fwd; the padded n
  * is at most 16384 when dx is computed, and each code matrix spans less than 4 GiB.
+ * With INT8 codes, dW's int32 sums run over the padded m: exact while every partial sum
+ * stays within int32, which |codes| <= 127 guarantee up to 133144 terms (as halo_gemm_i8).
  */
 halo_status halo_linear_bwd(const void* dy, const void* x, const void* w, halo_dtype io_type,
                             int64_t m, int64_t n, int64_t k, int32_t block, halo_dtype q_type,
