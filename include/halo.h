@@ -20,8 +20,9 @@
  *   - A pointer may be NULL only when the matrix it describes is empty (a zero size).
  *   - All arguments are validated on the host before anything is launched.  On any error
  *     the call returns a non-zero status, launches nothing and writes no output.  A failed
- *     launch returns HALO_ERR_HIP.  Nothing is printed and no global state is kept, so calls
- *     are thread-safe; calls on one stream run in order.
+ *     launch returns HALO_ERR_HIP.  Nothing is printed, and the only state kept between calls
+ *     is a per-device cache of launch attributes and occupancy (set once, atomically), so
+ *     calls are thread-safe; calls on one stream run in order.
  *   - Columns longer than 4096 rows (halo_fwht_quant's columns axis with a workspace, and
  *     the backward pass when m > 4096) are split over workgroups that wait for each other
  *     to combine their maxima.  Within one launch that wait always ends.  Where other work
