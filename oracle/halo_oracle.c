@@ -56,10 +56,11 @@
  *     padded vector.
  *
  * Two precisions are offered for the transform + quantisation step:
- *   precision 64: fp64 butterflies, divide by sqrt(b), q = rne(y * qmax / a) with the
- *                 quotient taken in long double (a real tie stays a tie).
- *   precision 32: the same butterflies in fp32 (same stage and pairing order), the code
- *                 decided in fp32 from the un-normalised butterfly output:
+ *   precision 64: the Kronecker factors of H_b in fp64, from the highest index bit down,
+ *                 divide by sqrt(b), q = rne(y * qmax / a) with the quotient taken in long
+ *                 double (a real tie stays a tie).
+ *   precision 32: the factors in fp32 from index bit 0 up (each sum rounded to fp32), the
+ *                 code decided in fp32 from the un-normalised transform output:
  *                 m = fl32(qmax / a), q = rne(y * m) with the product taken exactly
  *                 (INT8) or rounded to fp32 first (FP8).  Where qmax / a overflows (a
  *                 vector of values below about qmax / FLT_MAX) y and a are first scaled
@@ -174,37 +175,62 @@ uint8_t hor_fp8_encode(double v, int fmt) { return fp8_encode((long double)v, fm
 double hor_fp8_decode(uint8_t c, int fmt) { return fp8_decode(c, fmt_of(fmt)); }
 
 /* ------------------------------------------------------------------------- */
-/* Walsh-Hadamard transform: [QWHA] s2.2 butterfly, blockwise per s3.1        */
+/* Walsh-Hadamard transform: [QWHA] s2.1 definition, s2.2 normalisation,      */
+/* blockwise per s3.1                                                         */
 /* ------------------------------------------------------------------------- */
 
-/* One block of length b (a power of two), fp64: butterflies, then divide by sqrt(b). */
+/* The Sylvester matrix of order b = 2^n is the n-fold Kronecker power of
+ * H_2 = [[1, 1], [1, -1]] ([QWHA] s2.1 builds it level by level), so entry (i, j) is
+ * (-1)^popcount(i & j) and H_b v is the product of n commuting factors, the factor of index
+ * bit s acting on every pair of positions that differ only in bit s:
+ *     (v_lo, v_hi) <- (v_lo + v_hi, v_lo - v_hi),   lo = i with bit s clear, hi = lo + 2^s.
+ * Every factor is exact in real arithmetic and they commute, so any order of the bits gives
+ * H_b v; only the rounding of the floating-point sums depends on the order. */
+static int log2_of(int64_t b)
+{
+    int n = 0;
+    while (((int64_t)1 << n) < b) ++n;
+    return n;
+}
+
+static void kron_factor_f64(double* v, int64_t b, int s)
+{
+    const int64_t d = (int64_t)1 << s;
+    for (int64_t lo = 0; lo < b; ++lo) {
+        if (lo & d) continue;
+        const double a = v[lo], c = v[lo + d];
+        v[lo] = a + c;
+        v[lo + d] = a - c;
+    }
+}
+
+static void kron_factor_f32(float* v, int64_t b, int s)
+{
+    const int64_t d = (int64_t)1 << s;
+    for (int64_t lo = 0; lo < b; ++lo) {
+        if (lo & d) continue;
+        const float a = v[lo], c = v[lo + d];
+        v[lo] = a + c;
+        v[lo + d] = a - c;
+    }
+}
+
+/* One block of length b (a power of two), fp64: the factors from the highest index bit down,
+ * then the orthonormal scaling 1/sqrt(b) ([QWHA] s2.1: 1/sqrt(2) per level; s2.2: divide by
+ * sqrt(n)). */
 static void fwht_block_f64(double* v, int64_t b)
 {
-    for (int64_t h = 1; h < b; h *= 2) {
-        for (int64_t i = 0; i < b; i += 2 * h) {
-            for (int64_t t = i; t < i + h; ++t) {
-                double p = v[t], q = v[t + h];
-                v[t] = p + q;
-                v[t + h] = p - q;
-            }
-        }
-    }
+    for (int s = log2_of(b) - 1; s >= 0; --s) kron_factor_f64(v, b, s);
     double root = sqrt((double)b);
     for (int64_t t = 0; t < b; ++t) v[t] = v[t] / root;
 }
 
-/* The same butterflies in fp32, without the final normalisation. */
+/* The same product in fp32, without the scaling, the factors from index bit 0 up (the order
+ * of [QWHA] s2.2, whose half-width doubles from 1): the order a single-precision device that
+ * rounds after every sum reproduces exactly. */
 static void fwht_block_f32_unnorm(float* v, int64_t b)
 {
-    for (int64_t h = 1; h < b; h *= 2) {
-        for (int64_t i = 0; i < b; i += 2 * h) {
-            for (int64_t t = i; t < i + h; ++t) {
-                float p = v[t], q = v[t + h];
-                v[t] = p + q;
-                v[t + h] = p - q;
-            }
-        }
-    }
+    for (int s = 0; s < log2_of(b); ++s) kron_factor_f32(v, b, s);
 }
 
 /* malloc size for n elements, never zero */

@@ -1,8 +1,8 @@
 """Pins of the CPU oracle against what the pages and the mathematics fix.
 
 Nothing here re-types the oracle's own formulas: each test checks it against an independent
-construction (the Kronecker definition of the Hadamard matrix, the other page's recursive
-transform, hand-worked fixtures under tests/golden/, closed forms, invariants, brute force,
+construction (the Kronecker definition of the Hadamard matrix and its closed-form entries,
+the other page's recursive transform written out as its matrix, hand-worked fixtures under tests/golden/, closed forms, invariants, brute force,
 torch's float8 conversions).
 """
 import os
@@ -29,16 +29,18 @@ def sylvester(n):
     return h
 
 
-def recursive_fht(x):
-    """Even/odd recursive transform as described on the HALO blog page (dpshk.com, s2.1):
-    transform the even- and odd-indexed halves, then concatenate their sum and difference.
-    Unnormalised."""
-    x = np.asarray(x, dtype=np.float64)
-    if x.shape[0] == 1:
-        return x.copy()
-    ev = recursive_fht(x[0::2])
-    od = recursive_fht(x[1::2])
-    return np.concatenate([ev + od, ev - od])
+def bit_reversed_sylvester(n):
+    """Matrix of the recursive even/odd transform described on the HALO overview page
+    ("企业官网建设流程全解析", s2.1): the two halves of its output are the sum and the
+    difference of the transforms of the even- and odd-indexed inputs, so the output's top
+    index bit pairs with the input's lowest bit, and so on down; written out, entry (i, j) is
+    (-1)^popcount(rev(i) & j) with rev the reversal of i's log2(n) bits.  Unnormalised."""
+    bits = n.bit_length() - 1
+    rev = bit_reverse_perm(n)
+    i = rev[:, None]
+    j = np.arange(n)[None, :]
+    pc = np.vectorize(lambda v: bin(int(v)).count("1"))(i & j)
+    return np.where(pc % 2 == 0, 1, -1).astype(np.int64) if bits else np.ones((1, 1), np.int64)
 
 
 def bit_reverse_perm(n):
@@ -79,13 +81,21 @@ def test_fwht_equals_sylvester_matrix(n):
     np.testing.assert_allclose(y, ref, rtol=0, atol=1e-13 * max(1.0, np.abs(ref).max()))
 
 
+@pytest.mark.parametrize("n", [1, 2, 4, 8, 16, 32, 64])
+def test_kronecker_power_entries(n):
+    # the Kronecker recursion of the QWHA page (s2.1) has entries (-1)^popcount(i & j)
+    i, j = np.meshgrid(np.arange(n), np.arange(n), indexing="ij")
+    pc = np.vectorize(lambda v: bin(int(v)).count("1"))(i & j)
+    assert np.array_equal(sylvester(n), np.where(pc % 2 == 0, 1, -1))
+
+
 @pytest.mark.parametrize("n", [2, 4, 8, 16, 32, 64])
 def test_recursive_page_transform_is_bit_reversed_sylvester(n):
-    # cross-pin between two pages: the blog's recursive even/odd transform gives the
+    # cross-pin between two pages: the overview page's recursive even/odd transform gives the
     # Sylvester (natural-order) result in bit-reversed order, unnormalised.
     rng = np.random.default_rng(100 + n)
     x = rng.standard_normal(n)
-    rec = recursive_fht(x)
+    rec = bit_reversed_sylvester(n).astype(np.float64) @ x
     nat = O.fwht(x, n) * np.sqrt(n)
     np.testing.assert_allclose(rec, nat[bit_reverse_perm(n)], rtol=0, atol=1e-12)
 
@@ -249,18 +259,21 @@ def test_signed_zeros(precision):
     assert not np.signbit(y[0, :8]).any()
 
 
-def test_precision32_agrees_with_precision64():
+@pytest.mark.parametrize("block", [16, 128, 256, 1024, 4096])
+def test_precision32_agrees_with_precision64(block):
+    # the fp32 decision against the plain fp64 definition, at the code bar: |dq| <= 1 and at
+    # most 1e-4 of the codes off by one; scales far inside 1e-5 relative
     rng = np.random.default_rng(8)
-    x = synth.bf16_bits(synth.activations(rng, 64, 1024))
+    x = synth.bf16_bits(synth.activations(rng, 128, 4096))
     for qt in (O.I8, O.E4M3, O.E5M2):
-        q64, s64 = O.fwht_quant(x, O.ROWS, 256, qt, precision=64)
-        q32, s32 = O.fwht_quant(x, O.ROWS, 256, qt, precision=32)
-        np.testing.assert_allclose(s32, s64, rtol=2e-7)
+        q64, s64 = O.fwht_quant(x, O.ROWS, block, qt, precision=64)
+        q32, s32 = O.fwht_quant(x, O.ROWS, block, qt, precision=32)
+        np.testing.assert_allclose(s32, s64, rtol=1e-6)
         if qt == O.I8:
             d = np.abs(q64.astype(np.int32) - q32.astype(np.int32))
         else:
             d = np.abs(_fp8_ordinal(q64) - _fp8_ordinal(q32))
-        assert d.max() <= 1 and (d == 1).mean() <= 1e-3
+        assert d.max() <= 1 and (d == 1).mean() <= 1e-4
 
 
 def _fp8_ordinal(c):
