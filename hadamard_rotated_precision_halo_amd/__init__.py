@@ -187,7 +187,8 @@ def fwht_quant(x, axis=ROWS, block=256, q_dtype=torch.int8, q=None, scale=None, 
     int32 device tensor, see hadamard_signs) or None.  `rounding`: "nearest" or "stochastic"
     (Philox key `seed`, counter words 2-3 `counter`, each a 64-bit integer).
     `exchange_polls`: for columns longer than 4096 rows, the polls a waiting workgroup makes
-    before its strip is given up (NaN scales, zero codes); 0 = the library's default.
+    before it stops waiting (the strip is then stored by a follow-up launch, with the same
+    codes); 0 = the library's default.
     """
     rows, cols = x.shape
     nvec, L = (rows, cols) if axis == ROWS else (cols, rows)

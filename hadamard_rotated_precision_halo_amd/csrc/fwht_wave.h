@@ -31,11 +31,11 @@
 // of one column strip combine their partial maxima through device-scope atomics: each
 // max-reduces its maxima into the strip's column maxima, increments the strip's arrival
 // counter, and waits until all P have arrived.  The tasks of a group of up to 8 strips are
-// consecutive workgroups, the parts of each strip 8 apart (one XCD), and workgroups are
-// dispatched in index order, so within one launch the wait always ends (see the launcher).
-// The wait is bounded all the same: where other waiting work holds the compute units, the
-// strip is given up as a whole and its columns get NaN scales (see cols_task).  The input is
-// read once and the codes written once.
+// consecutive workgroups, the parts of each strip 8 apart (one XCD), so the parts of a strip
+// normally run side by side and the input is read once and the codes written once.  No
+// result depends on that: the wait is bounded, and a task that reaches the bound computes
+// its strip's maxima itself from the input (see cols_task), so every call ends with the
+// same codes whatever else occupies the device.
 //
 // Options (every kernel here): the randomised transform's signs ("企业官网建设流程全解析" s4.2,
 // one bit per element, applied before the butterflies), zero padding of vectors whose length
@@ -461,27 +461,88 @@ struct ColsProb {
   FqArgs a;
   float* colmax;
   uint32_t* arrive;
+  uint32_t* late;  // count of tasks that computed their strip's maxima themselves
   int R, P, C;
-  int gs;         // strips per task group (see cols_task), 1 or 8
-  uint32_t spins; // polls of a waiting task before it gives the strip up (see cols_task)
+  int gs;          // strips per task group (see cols_task), 1 or 8
+  uint32_t spins;  // polls of a waiting task before it stops waiting (see cols_task)
 };
+
+// Load part `part` (rows [part R, (part + 1) R)) of the column strip starting at column c0
+// into the LDS tile: each thread reads 8 rows of 8 adjacent columns (16 bytes per row),
+// transposes them in registers and writes 8 words of 8 rows of one column each.
+template <int B>
+__device__ __forceinline__ void cols_load(const ColsProb& pr, int64_t c0, int part, int t,
+                                          uint4* lds) {
+  using S = Slice<B>;
+  const FqArgs& a = pr.a;
+  const int R = pr.R, C = pr.C;
+  const int CC = C / 8;                      // 16-byte column chunks per row of the tile
+  const int cpw = 4096 / R;                  // column segments per wave
+  const int cc = t % CC, rg = t / CC;        // column chunk, group of 8 rows
+  const uint16_t* __restrict__ xin = reinterpret_cast<const uint16_t*>(a.x);
+  const int64_t col = c0 + cc * 8;
+  const bool cvalid = col < a.nvec;
+  const int64_t r0 = (int64_t)part * R + rg * 8;  // first row of the group
+  const uint16_t* p = xin + r0 * a.ldx + (cvalid ? col : 0);
+  uint4 raw[8];
+  // unconditional loads (a row of the zero padding, at and past in_len, reads row 0 instead);
+  // only passes with padding then zero those rows
+  const uint16_t* p0 = xin + (cvalid ? col : 0);
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    raw[i] = *reinterpret_cast<const uint4*>(r0 + i < a.in_len ? p + i * a.ldx : p0);
+  if (a.in_len < a.len) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (r0 + i >= a.in_len) raw[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  if (a.signs) {  // the transform's signs: one bit per row, on the bf16 sign bits
+    const uint32_t b = a.signs[r0 >> 5] >> (r0 & 31);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t f = ((b >> i) & 1u) ? 0x80008000u : 0u;
+      raw[i].x ^= f; raw[i].y ^= f; raw[i].z ^= f; raw[i].w ^= f;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int cl = cc * 8 + e;             // column within the tile
+    const int wr = cl / cpw, ciw = cl % cpw;
+    int ln, j;
+    S::where(ciw * R + rg * 8, ln, j);
+    uint32_t d0, d1, d2, d3;
+    if ((e >> 1) == 0) {
+      d0 = bf16_pair(raw[0].x, raw[1].x, e & 1); d1 = bf16_pair(raw[2].x, raw[3].x, e & 1);
+      d2 = bf16_pair(raw[4].x, raw[5].x, e & 1); d3 = bf16_pair(raw[6].x, raw[7].x, e & 1);
+    } else if ((e >> 1) == 1) {
+      d0 = bf16_pair(raw[0].y, raw[1].y, e & 1); d1 = bf16_pair(raw[2].y, raw[3].y, e & 1);
+      d2 = bf16_pair(raw[4].y, raw[5].y, e & 1); d3 = bf16_pair(raw[6].y, raw[7].y, e & 1);
+    } else if ((e >> 1) == 2) {
+      d0 = bf16_pair(raw[0].z, raw[1].z, e & 1); d1 = bf16_pair(raw[2].z, raw[3].z, e & 1);
+      d2 = bf16_pair(raw[4].z, raw[5].z, e & 1); d3 = bf16_pair(raw[6].z, raw[7].z, e & 1);
+    } else {
+      d0 = bf16_pair(raw[0].w, raw[1].w, e & 1); d1 = bf16_pair(raw[2].w, raw[3].w, e & 1);
+      d2 = bf16_pair(raw[4].w, raw[5].w, e & 1); d3 = bf16_pair(raw[6].w, raw[7].w, e & 1);
+    }
+    lds[lds_slot<B>(wr, ln, j)] = make_uint4(d0, d1, d2, d3);
+  }
+}
 
 // One task (one R-row part of one column strip) of a column pass, run by a whole workgroup of
 // 16 waves.
-template <int B, int QT, bool SR>
+// REPAIR: the second launch of an exchanging pass (see below): only the tasks of strips marked
+// late run, with the column maxima complete by then.
+template <int B, int QT, bool SR, bool REPAIR = false>
 __device__ __forceinline__ void cols_task(const ColsProb& pr, int64_t ltask, uint4* lds) {
   using S = Slice<B>;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const FqArgs& a = pr.a;
   const int R = pr.R, P = pr.P, C = pr.C;
-  const int CC = C / 8;                      // 16-byte column chunks per row of the tile
   const int cpw = 4096 / R;                  // column segments per wave
-  const int cc = t % CC, rg = t / CC;        // loader: column chunk, group of 8 rows
   const int row_lanes_log2 = 31 - __builtin_clz((unsigned)(R / 64));
   float* colmax = pr.colmax;
   uint32_t* arrive = pr.arrive;
   const int64_t ncols = a.nvec;
-  const uint16_t* __restrict__ xin = reinterpret_cast<const uint16_t*>(a.x);
   // the tasks of a strip group are consecutive (see the launcher); with one task per strip the
   // strips are spread so that each XCD (task i runs on XCD (i + offset) % 8) gets a contiguous
   // run of them: neighbouring strips share 128-byte lines, which its L2 then fetches once
@@ -502,147 +563,106 @@ __device__ __forceinline__ void cols_task(const ColsProb& pr, int64_t ltask, uin
     part = (int)(j / n);
   }
   const int64_t c0 = strip * C;
-
-    // ---- load 8 rows x 8 columns, transpose, write to LDS ------------------------------
-    {
-      const int64_t col = c0 + cc * 8;
-      const bool cvalid = col < ncols;
-      const int64_t r0 = (int64_t)part * R + rg * 8;  // first row of the group
-      const uint16_t* p = xin + r0 * a.ldx + (cvalid ? col : 0);
-      uint4 raw[8];
-      // unconditional loads (a row of the zero padding, at and past in_len, reads row 0
-      // instead); only passes with padding then zero those rows
-      const uint16_t* p0 = xin + (cvalid ? col : 0);
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        raw[i] = *reinterpret_cast<const uint4*>(r0 + i < a.in_len ? p + i * a.ldx : p0);
-      if (a.in_len < a.len) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          if (r0 + i >= a.in_len) raw[i] = make_uint4(0u, 0u, 0u, 0u);
-      }
-      if (a.signs) {  // the transform's signs: one bit per row, on the bf16 sign bits
-        const uint32_t b = a.signs[r0 >> 5] >> (r0 & 31);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint32_t f = ((b >> i) & 1u) ? 0x80008000u : 0u;
-          raw[i].x ^= f; raw[i].y ^= f; raw[i].z ^= f; raw[i].w ^= f;
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int cl = cc * 8 + e;             // column within the tile
-        const int wr = cl / cpw, ciw = cl % cpw;
-        int ln, j;
-        S::where(ciw * R + rg * 8, ln, j);
-        uint32_t d0, d1, d2, d3;
-        if ((e >> 1) == 0) {
-          d0 = bf16_pair(raw[0].x, raw[1].x, e & 1); d1 = bf16_pair(raw[2].x, raw[3].x, e & 1);
-          d2 = bf16_pair(raw[4].x, raw[5].x, e & 1); d3 = bf16_pair(raw[6].x, raw[7].x, e & 1);
-        } else if ((e >> 1) == 1) {
-          d0 = bf16_pair(raw[0].y, raw[1].y, e & 1); d1 = bf16_pair(raw[2].y, raw[3].y, e & 1);
-          d2 = bf16_pair(raw[4].y, raw[5].y, e & 1); d3 = bf16_pair(raw[6].y, raw[7].y, e & 1);
-        } else if ((e >> 1) == 2) {
-          d0 = bf16_pair(raw[0].z, raw[1].z, e & 1); d1 = bf16_pair(raw[2].z, raw[3].z, e & 1);
-          d2 = bf16_pair(raw[4].z, raw[5].z, e & 1); d3 = bf16_pair(raw[6].z, raw[7].z, e & 1);
-        } else {
-          d0 = bf16_pair(raw[0].w, raw[1].w, e & 1); d1 = bf16_pair(raw[2].w, raw[3].w, e & 1);
-          d2 = bf16_pair(raw[4].w, raw[5].w, e & 1); d3 = bf16_pair(raw[6].w, raw[7].w, e & 1);
-        }
-        lds[lds_slot<B>(wr, ln, j)] = make_uint4(d0, d1, d2, d3);
-      }
-    }
+  constexpr uint32_t kMark = 0x80000000u;  // top bit of a strip's arrival count: marked late
+  if constexpr (REPAIR) {
+    // every task of the exchanging launch has finished, so every part's maxima are in colmax;
+    // the tasks of strips marked late quantise and store their part again from them
+    if (P == 1) return;
+    __shared__ uint32_t s_mark;
+    if (t == 0)
+      s_mark = __hip_atomic_load(&arrive[strip], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kMark;
     __syncthreads();
+    if (!s_mark) return;
+  }
 
-    // ---- rotate the wave's column segments ------------------------------------------------
-    const int seg = S::off(lane, 0) / R;       // column segment of this lane within the wave
-    const int64_t pos0 = (int64_t)part * R - (int64_t)seg * R;  // + off(lane, j): row index
-    float v[64];
+  // ---- load R rows x C columns, transposed into LDS ---------------------------------------
+  cols_load<B>(pr, c0, part, t, lds);
+  __syncthreads();
+
+  // ---- rotate the wave's column segments --------------------------------------------------
+  const int seg = S::off(lane, 0) / R;       // column segment of this lane within the wave
+  const int64_t pos0 = (int64_t)part * R - (int64_t)seg * R;  // + off(lane, j): row index
+  float v[64];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) unpack_bf16x8(lds[lds_slot<B>(w, lane, j)], &v[j * 8]);
-    const float sgn = rotate64<B>(v, lane);
-    const int64_t col = c0 + w * cpw + seg;
-    const bool valid = col < ncols;
-    float mx = lane_max(absmax64(v), row_lanes_log2);
-    const bool writer = (lane & ((1 << row_lanes_log2) - 1)) == 0;
+  for (int j = 0; j < 8; ++j) unpack_bf16x8(lds[lds_slot<B>(w, lane, j)], &v[j * 8]);
+  const float sgn = rotate64<B>(v, lane);
+  const int64_t col = c0 + w * cpw + seg;
+  const bool valid = col < ncols;
+  float mx = lane_max(absmax64(v), row_lanes_log2);
+  const bool writer = (lane & ((1 << row_lanes_log2) - 1)) == 0;
 
-    // ---- column maxima of a strip split over P tasks ---------------------------------------
-    // Device-scope atomics only (they are performed at the device's coherence point, across
-    // XCDs): each task max-reduces its partial maxima into colmax (non-negative floats order
-    // like their bit patterns) and waits for their returned values; one thread then counts the task
-    // in and waits for all P; one thread per column reads the final maximum back with an
-    // atomic load and shares it through LDS.  No cache-wide fence is needed.
-    if (P > 1) {
-      __shared__ float s_cmax[1024];
-      uint32_t* cm = reinterpret_cast<uint32_t*>(colmax);
+  // ---- column maxima of a strip split over P tasks -----------------------------------------
+  // Device-scope atomics only (they are performed at the device's coherence point, across
+  // XCDs): each task max-reduces its partial maxima into colmax (non-negative floats order
+  // like their bit patterns) and waits for their returned values; one thread then counts the
+  // task in and waits for all P; one thread per column reads the final maximum back with an
+  // atomic load and shares it through LDS.  No cache-wide fence is needed.
+  if (P > 1) {
+    __shared__ float s_cmax[1024];
+    uint32_t* cm = reinterpret_cast<uint32_t*>(colmax);
+    if constexpr (!REPAIR) {
+      __shared__ uint32_t s_late;
       uint32_t seen = 0;
       if (valid && writer)
         seen = __hip_atomic_fetch_max(&cm[col], __float_as_uint(mx), __ATOMIC_RELAXED,
                                       __HIP_MEMORY_SCOPE_AGENT);
       // every wave waits for the values its atomics return (so they have been performed at
       // the coherence point) before it reaches the barrier, so the arrival counted below
-      // covers them: a workgroup barrier alone does not wait for outstanding memory operations,
-      // and an unused return value would let the compiler drop the wait
+      // covers them: a workgroup barrier alone does not wait for outstanding memory
+      // operations, and an unused return value would let the compiler drop the wait
       asm volatile("s_waitcnt vmcnt(0)" ::"v"(seen) : "memory");
       __syncthreads();
-      // The count word's top bit marks a strip given up.  A task that has polled pr.spins
-      // times without seeing all P sets it, by compare-and-swap and only on a count below P,
-      // so the mark is never set on a complete strip: every task of the strip sees either the
-      // full unmarked count or the mark, never both, and a strip given up is given up by all of
-      // its tasks.  They store NaN scales and zero codes for its columns, a failure the caller
-      // sees, in place of codes from partial maxima.  This happens only when the tasks of a strip
-      // cannot all be resident at once, i.e. when other work that waits (another such pass on
-      // another stream) holds the compute units; within one launch the wait always ends.
-      __shared__ uint32_t s_lost;
+      // The wait is bounded by pr.spins polls.  The parts of a strip are close together in
+      // the launch order and normally all resident at once, so the count completes long
+      // before the bound; the bound matters only when other work holds the compute units
+      // (another such pass on another stream whose tasks wait too).  A task that reaches it
+      // marks the strip late and stops without storing; so does every task that finds the
+      // mark.  The repair launch that follows on the stream stores every part of a marked
+      // strip from the complete maxima: the same codes as an exchange that completes.
       if (t == 0) {
-        constexpr uint32_t kMark = 0x80000000u;
-        uint32_t c =
-            __hip_atomic_fetch_add(&arrive[strip], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) +
-            1u;
-        // c < P: neither complete nor marked (a marked count is >= 2^31 > P).  The last task to
-        // arrive sees the full count at once and does not poll.
-        for (uint32_t it = 0; c < (uint32_t)P; ++it) {
-          if (it >= pr.spins) {
-            // each failed swap returns a changed count (arrivals only add, up to P), so this
-            // ends: marked here (c stays below P), complete, or marked by another task
-            while (c < (uint32_t)P &&
-                   !__hip_atomic_compare_exchange_strong(&arrive[strip], &c, c | kMark,
-                                                         __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                         __HIP_MEMORY_SCOPE_AGENT)) {
-            }
-            if (c < (uint32_t)P) c = kMark;
-            break;
-          }
+        uint32_t c = __hip_atomic_fetch_add(&arrive[strip], 1u, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT) + 1u;
+        // the last task to arrive sees the full count at once and does not poll
+        for (uint32_t it = 0; (c & ~kMark) < (uint32_t)P && !(c & kMark) && it < pr.spins; ++it) {
           __builtin_amdgcn_s_sleep(2);
           c = __hip_atomic_load(&arrive[strip], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        s_lost = c >= kMark ? 1u : 0u;
+        const bool late = (c & kMark) || (c & ~kMark) < (uint32_t)P;
+        if (late) {
+          if (!(c & kMark))
+            __hip_atomic_fetch_or(&arrive[strip], kMark, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_fetch_add(pr.late, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        s_late = late ? 1u : 0u;
       }
       __syncthreads();
-      if (t < C && c0 + t < ncols)
-        s_cmax[t] = s_lost ? __builtin_nanf("")
-                           : __uint_as_float(__hip_atomic_load(&cm[c0 + t], __ATOMIC_RELAXED,
-                                                               __HIP_MEMORY_SCOPE_AGENT));
-      __syncthreads();
-      if (valid) mx = s_cmax[w * cpw + seg];
+      if (s_late) return;
     }
+    if (t < C && c0 + t < ncols)
+      s_cmax[t] = __uint_as_float(__hip_atomic_load(&cm[c0 + t], __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT));
+    __syncthreads();
+    if (valid) mx = s_cmax[w * cpw + seg];
+  }
 
-    // ---- quantise and store the transposed codes ------------------------------------------
-    if (valid) {
-      if (part == 0 && writer) a.scale[col] = stored_scale<QT>(a, mx);
-      const float mul = quant_mul_v<QT>(a, mx, v) * sgn;
-      store_slice<B, QT, SR>(a, v, mul, col * a.ldq + pos0, lane, col, pos0);
-    }
+  // ---- quantise and store the transposed codes ----------------------------------------------
+  if (valid) {
+    if (part == 0 && writer) a.scale[col] = stored_scale<QT>(a, mx);
+    const float mul = quant_mul_v<QT>(a, mx, v) * sgn;
+    store_slice<B, QT, SR>(a, v, mul, col * a.ldq + pos0, lane, col, pos0);
+  }
 }
 
-template <int B, int QT, bool SR>
+// REPAIR: the follow-up launch of a pass whose strips are split over several tasks; it
+// stores the parts of strips marked late (see cols_task) and returns at once for the rest.
+template <int B, int QT, bool SR, bool REPAIR = false>
 __global__ __launch_bounds__(1024) void fq_cols2_kernel(ColsProb c0, ColsProb c1, int64_t split,
                                                         int64_t tasks) {
   extern __shared__ __attribute__((aligned(16))) uint4 lds[];
   for (int64_t task = blockIdx.x; task < tasks; task += gridDim.x) {
     const bool second = task >= split;
     const ColsProb pr = second ? c1 : c0;
-    cols_task<B, QT, SR>(pr, task - (second ? split : 0), lds);
+    cols_task<B, QT, SR, REPAIR>(pr, task - (second ? split : 0), lds);
     __syncthreads();  // the next task overwrites the LDS tile
   }
 }
@@ -659,17 +679,18 @@ struct FqBatch {
 };
 
 // SR: stochastic rounding of the dY codes (the W and X codes are rounded to nearest).
-template <int B, int QG, int QW, bool SR>
+// REPAIR: the follow-up launch of the column passes (rows tasks excluded from its grid).
+template <int B, int QG, int QW, bool SR, bool REPAIR = false>
 __global__ __launch_bounds__(1024) void fq_batch_kernel(FqBatch fb) {
   extern __shared__ __attribute__((aligned(16))) uint4 lds[];
   const int64_t bid = blockIdx.x;
   if (bid < fb.end_w) {
-    cols_task<B, QW, false>(fb.cw, bid, lds);
+    cols_task<B, QW, false, REPAIR>(fb.cw, bid, lds);
   } else if (bid < fb.end_dy) {
-    cols_task<B, QG, SR>(fb.cdy, bid - fb.end_w, lds);
+    cols_task<B, QG, SR, REPAIR>(fb.cdy, bid - fb.end_w, lds);
   } else if (bid < fb.end_x) {
-    cols_task<B, QW, false>(fb.cx, bid - fb.end_dy, lds);
-  } else {
+    cols_task<B, QW, false, REPAIR>(fb.cx, bid - fb.end_dy, lds);
+  } else if constexpr (!REPAIR) {
     rows_wave<uint16_t, B, QG, SR>(fb.rows, (bid - fb.end_x) * 16 + (threadIdx.x >> 6),
                                    threadIdx.x & 63);
   }
@@ -715,13 +736,18 @@ static int cols2_capacity(const void* fn) {
 // the launchers below, with groups in place of strips); else 1.
 static int cols2_group(int P, int capacity) { return P > 1 && 8 * P <= capacity ? 8 : 1; }
 
-// Scratch layout of one pass: arrival counters (padded to 256 bytes), then the column maxima.
+// Scratch layout of one pass: the count of tasks that computed their strip's maxima
+// themselves (one word, padded to 256 bytes), the arrival counters (padded to 256 bytes),
+// then the column maxima.
+constexpr size_t kColsLateBytes = 256;
 static void cols2_scratch(void* ws, int64_t strips, float** colmax, uint32_t** arrive,
-                          int64_t* words) {
+                          uint32_t** late, int64_t* words) {
   const size_t cnt = ((size_t)strips * 4 + 255) & ~(size_t)255;
-  *arrive = reinterpret_cast<uint32_t*>(ws);
-  *colmax = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + cnt);
-  *words = (int64_t)(cnt / 4);
+  char* base = reinterpret_cast<char*>(ws);
+  *late = reinterpret_cast<uint32_t*>(base);
+  *arrive = reinterpret_cast<uint32_t*>(base + kColsLateBytes);
+  *colmax = reinterpret_cast<float*>(base + kColsLateBytes + cnt);
+  *words = (int64_t)((kColsLateBytes + cnt) / 4);
 }
 
 // Geometry and scratch of one column pass (rows = a.len); tasks = 0 for an empty pass.
@@ -736,10 +762,10 @@ static ColsProb cols2_prob(const FqArgs& a, void* ws, int64_t* tasks, int64_t* s
   *tasks = (a.nvec == 0 || a.len == 0) ? 0 : strips * pr.P;
   *scratch_words = 0;
   if (pr.P > 1 && *tasks > 0) {
-    cols2_scratch(ws, strips, &pr.colmax, &pr.arrive, scratch_words);
+    cols2_scratch(ws, strips, &pr.colmax, &pr.arrive, &pr.late, scratch_words);
     *scratch_words += a.nvec;
-    // polls a waiting task makes before it gives its strip up (each an atomic load and
-    // s_sleep 2): the caller's count, else 2^20
+    // polls a waiting task makes before it computes the maxima itself (each an atomic load
+    // and s_sleep 2): the caller's count, else 2^20
     pr.spins = a.polls != 0 ? a.polls : (1u << 20);
   }
   return pr;
@@ -766,11 +792,9 @@ static hipError_t launch_cols2_t(const FqArgs& a0, void* ws0, const FqArgs* a1, 
   const int64_t tasks = t0 + t1;
   if (tasks == 0) return hipSuccess;
   // one task per workgroup; the tasks of a group of gs strips (gs P tasks) are consecutive
-  // workgroups.  A waiting workgroup only waits for the other members of its own group, and
-  // the hardware dispatches workgroups in index order on each XCD: every group below the
-  // lowest undispatched workgroup is fully dispatched and finishes, freeing room for the
-  // rest, so every wait ends as long as one group fits on the device at once (gs P <= the
-  // capacity, which cols2_group ensures).
+  // workgroups, so the parts of a strip normally run side by side (one group fits on the
+  // device at once: gs P <= the capacity, which cols2_group ensures).  Termination does not
+  // rest on the dispatch order: every wait is bounded (see cols_task).
   const int P = p0.P > p1.P ? p0.P : p1.P;
   if (P > 1) {
     const int cap = cols2_capacity(reinterpret_cast<const void*>(fn));
@@ -778,6 +802,14 @@ static hipError_t launch_cols2_t(const FqArgs& a0, void* ws0, const FqArgs* a1, 
     p0.gs = p1.gs = cols2_group(P, cap);
   }
   hipLaunchKernelGGL((fq_cols2_kernel<B, QT, SR>), dim3((unsigned)tasks), dim3(1024),
+                     kColsLdsBytes, st, p0, p1, t0, tasks);
+  e = hipGetLastError();
+  if (e != hipSuccess || P == 1) return e;
+  // the repair launch: stores the strips whose tasks stopped waiting (usually none; its
+  // workgroups then only read one counter each)
+  e = allow_dynamic_lds<&fq_cols2_kernel<B, QT, SR, true>>(kColsLdsBytes);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((fq_cols2_kernel<B, QT, SR, true>), dim3((unsigned)tasks), dim3(1024),
                      kColsLdsBytes, st, p0, p1, t0, tasks);
   return hipGetLastError();
 }
@@ -834,6 +866,13 @@ static hipError_t launch_batch_t(const FqArgs* rows, const FqArgs& cw, void* ws_
   }
   hipLaunchKernelGGL((fq_batch_kernel<B, QG, QW, SR>), dim3((unsigned)grid), dim3(1024),
                      kColsLdsBytes, st, fb);
+  e = hipGetLastError();
+  if (e != hipSuccess || P == 1) return e;
+  // the repair launch over the column tasks (see launch_cols2_t)
+  e = allow_dynamic_lds<&fq_batch_kernel<B, QG, QW, SR, true>>(kColsLdsBytes);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((fq_batch_kernel<B, QG, QW, SR, true>), dim3((unsigned)fb.end_x),
+                     dim3(1024), kColsLdsBytes, st, fb);
   return hipGetLastError();
 }
 

@@ -20,7 +20,7 @@ size_t fq_cols2_ws_bytes(int64_t rows, int64_t cols, int block, int in_bf16) {
   const int64_t C = 65536 / R;
   const int64_t strips = (cols + C - 1) / C;
   const size_t cnt = ((size_t)strips * 4 + 255) & ~(size_t)255;
-  return cnt + (size_t)cols * 4;
+  return kColsLateBytes + cnt + (size_t)cols * 4;
 }
 
 bool fq_cols2_supported(int64_t rows, int64_t cols, int block, int in_bf16, size_t ws_bytes) {

@@ -24,13 +24,13 @@
  *     is a per-device cache of launch attributes and occupancy (set once, atomically), so
  *     calls are thread-safe; calls on one stream run in order.
  *   - Columns longer than 4096 rows (halo_fwht_quant's columns axis with a workspace, and
- *     the backward pass when m > 4096) are split over workgroups that wait for each other
- *     to combine their maxima.  Within one launch that wait always ends.  Where other work
- *     that waits holds the compute units (e.g. two such passes overlapping on two streams),
- *     it is bounded: after 2^20 polls (each a device-scope load and a short sleep; the
- *     exchange_polls option of the _ex calls sets another count) the workgroups give their
- *     column strip up together, and its columns get NaN scales and zero codes, never codes
- *     from partial maxima.  Order such passes on one stream to avoid it.
+ *     the backward pass when m > 4096 or n > 4096) are split over workgroups that wait for
+ *     each other to combine their maxima.  The wait is bounded: after 2^20 polls (each a
+ *     device-scope load and a short sleep; the exchange_polls option of the _ex calls sets
+ *     another count) a workgroup stops waiting and leaves its part of the column strip
+ *     unstored, and a second launch that the call enqueues right after stores every part of
+ *     such strips from the completed maxima.  The codes and scales are the same either way:
+ *     no result depends on other work that occupies the device.
  *   - Alignment: every pointer 16-byte aligned, every leading dimension a multiple of 16
  *     bytes (HALO_ERR_ALIGN otherwise).
  *   - Scales are fp32 dequant multipliers: the vector's absmax after the orthonormal
@@ -110,7 +110,9 @@ typedef enum {
  *            are clobbered.  With it, a columns-axis pass over long bf16 columns reads its
  *            input once; with ws NULL (or too small) the pass reads its input twice and gives
  *            the same codes and scales.  Calls that share one scratch must be ordered on one
- *            stream.
+ *            stream.  After such a pass completes, the first 32-bit word of ws holds the
+ *            number of workgroups that stopped waiting for the exchange (a diagnostic; the
+ *            results do not depend on it).
  * Rows-axis vectors are limited to Lp <= 16384 elements (one workgroup holds a whole row).
  * Codes are decided in fp32: m = qmax / max|b| with b the un-normalised butterfly output and
  * code = round(b * m); the 1/sqrt(block) factor cancels between b and max|b|.
@@ -240,7 +242,8 @@ typedef struct {
     uint32_t seed[2];      /* Philox key (stochastic rounding)                            */
     uint32_t counter[2];   /* Philox counter words 2 and 3 (stochastic rounding)          */
     uint32_t exchange_polls; /* columns longer than 4096 rows: polls a waiting workgroup  */
-                             /* makes before its strip is given up (0 = 2^20)             */
+                             /* makes before it stops waiting (0 = 2^20); results are the */
+                             /* same for every value                                      */
 } halo_quant_opts;
 
 /*
