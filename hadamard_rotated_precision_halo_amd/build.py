@@ -45,5 +45,39 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_host_sanitized(out: str, verbose: bool = False) -> str:
+    """The library with its host code built with AddressSanitizer and UndefinedBehaviorSanitizer
+    (-Xarch_host: the device code is built as usual and never instrumented), for the CPU test
+    that runs the C ABI's argument validation and size queries under them."""
+    flags = ["--offload-arch=gfx950", "-O1", "-Xarch_host", "-g", "-std=c++17", "-fPIC",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fsanitize=address",
+             "-Xarch_host", "-fsanitize=undefined", "-Xarch_host",
+             "-fno-sanitize-recover=undefined", "-I" + os.path.join(ROOT, "include")]
+    tmp = os.path.dirname(os.path.abspath(out))
+
+    def one(src):
+        obj = os.path.join(tmp, os.path.splitext(src)[0] + ".san.o")
+        cmd = ["hipcc", *flags, "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc (sanitized host) failed on {src}:\n{r.stderr}")
+        return obj
+
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(one, SOURCES))
+    cmd = ["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", "-Xarch_host",
+           "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-shared-libasan",
+           "-o", out, *objs]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True, capture_output=not verbose)
+    for o in objs:
+        os.remove(o)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

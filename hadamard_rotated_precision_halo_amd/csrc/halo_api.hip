@@ -11,10 +11,25 @@
 #include "halo_kernels.h"
 
 #include <cmath>
+#include <cstring>
 
 using namespace halo;
 
 namespace {
+
+// Whether an enum argument holds a value in [lo, hi].  A C caller may pass any int in an enum
+// parameter, and in C++ loading an enum object whose value lies outside the enum's range is
+// undefined, so the value is read through its object representation, before any other use.
+// (The argument is taken by reference: passing it by value would itself be such a load.)
+template <typename E>
+bool enum_in(const E& e, int lo, int hi) {
+  static_assert(sizeof(E) == sizeof(int), "C enums are int-sized");
+  int v;
+  std::memcpy(&v, &e, sizeof v);
+  return v >= lo && v <= hi;
+}
+bool dtype_ok(const halo_dtype& t) { return enum_in(t, HALO_F32, HALO_I32); }
+bool axis_ok(const halo_axis& a) { return enum_in(a, HALO_ALONG_ROWS, HALO_ALONG_COLS); }
 
 constexpr int64_t kMaxDim = int64_t(1) << 31;
 
@@ -254,6 +269,7 @@ halo_status gemm_any(const void* a, halo_dtype at, int64_t lda, const float* sa,
 extern "C" {
 
 const char* halo_status_str(halo_status s) {
+  if (!enum_in(s, HALO_OK, HALO_ERR_OPTION)) return "unknown status";
   switch (s) {
     case HALO_OK: return "ok";
     case HALO_ERR_NULL: return "a required pointer is NULL";
@@ -270,6 +286,7 @@ const char* halo_status_str(halo_status s) {
 
 size_t halo_fwht_quant_workspace_bytes(int64_t rows, int64_t cols, halo_axis axis,
                                        int32_t block, halo_dtype x_type) {
+  if (!axis_ok(axis) || !dtype_ok(x_type)) return 0;
   if (rows < 0 || cols < 0 || rows >= kMaxDim || cols >= kMaxDim || !valid_block(block))
     return 0;
   if (axis != HALO_ALONG_COLS) return 0;
@@ -280,6 +297,8 @@ halo_status halo_fwht_quant_ex(const void* x, halo_dtype x_type, int64_t rows, i
                                int64_t ldx, halo_axis axis, int32_t block, halo_dtype q_type,
                                void* q, int64_t ldq, float* scale, const halo_quant_opts* opts,
                                void* ws, size_t ws_bytes, void* stream) {
+  if (!dtype_ok(x_type) || !dtype_ok(q_type)) return HALO_ERR_DTYPE;
+  if (!axis_ok(axis)) return HALO_ERR_SHAPE;
   halo_status s = check_fq(x, x_type, rows, cols, ldx, axis, block, q_type, q, ldq, scale, opts);
   if (s != HALO_OK) return s;
   if (ws && !aligned16(ws)) return HALO_ERR_ALIGN;
@@ -291,6 +310,8 @@ halo_status halo_fwht_quant(const void* x, halo_dtype x_type, int64_t rows, int6
                             int64_t ldx, halo_axis axis, int32_t block, halo_dtype q_type,
                             void* q, int64_t ldq, float* scale, void* ws, size_t ws_bytes,
                             void* stream) {
+  if (!dtype_ok(x_type) || !dtype_ok(q_type)) return HALO_ERR_DTYPE;
+  if (!axis_ok(axis)) return HALO_ERR_SHAPE;
   return halo_fwht_quant_ex(x, x_type, rows, cols, ldx, axis, block, q_type, q, ldq, scale,
                             nullptr, ws, ws_bytes, stream);
 }
@@ -298,6 +319,7 @@ halo_status halo_fwht_quant(const void* x, halo_dtype x_type, int64_t rows, int6
 halo_status halo_gemm_i8(const int8_t* a, int64_t lda, const float* sa, const int8_t* b,
                          int64_t ldb, const float* sb, int64_t m, int64_t n, int64_t k, void* c,
                          halo_dtype c_type, int64_t ldc, void* stream) {
+  if (!dtype_ok(c_type)) return HALO_ERR_DTYPE;
   if (c_type != HALO_I32 && c_type != HALO_F32 && c_type != HALO_BF16) return HALO_ERR_DTYPE;
   halo_status s = check_gemm(a, lda, b, ldb, m, n, k, c, c_type, ldc, sa, sb, 16);
   if (s != HALO_OK) return s;
@@ -310,6 +332,7 @@ halo_status halo_gemm_fp8(const void* a, halo_dtype a_type, int64_t lda, const f
                           const void* b, halo_dtype b_type, int64_t ldb, const float* sb,
                           int64_t m, int64_t n, int64_t k, void* c, halo_dtype c_type,
                           int64_t ldc, void* stream) {
+  if (!dtype_ok(a_type) || !dtype_ok(b_type) || !dtype_ok(c_type)) return HALO_ERR_DTYPE;
   if ((a_type != HALO_E4M3 && a_type != HALO_E5M2) || (b_type != HALO_E4M3 && b_type != HALO_E5M2))
     return HALO_ERR_DTYPE;
   if (c_type != HALO_F32 && c_type != HALO_BF16) return HALO_ERR_DTYPE;
@@ -328,6 +351,7 @@ bool layer_dims_ok(int64_t m, int64_t n, int64_t k) {
 
 size_t halo_linear_workspace_bytes_ex(int64_t m, int64_t n, int64_t k, int32_t block,
                                       halo_dtype q_type, int backward) {
+  if (!dtype_ok(q_type)) return 0;
   if (!layer_dims_ok(m, n, k) || !valid_block(block)) return 0;
   if (q_type != HALO_I8 && q_type != HALO_E4M3) return 0;
   // the columns passes' scratch is sized for bf16 input (fp32 input needs none)
@@ -336,6 +360,7 @@ size_t halo_linear_workspace_bytes_ex(int64_t m, int64_t n, int64_t k, int32_t b
 
 size_t halo_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, halo_dtype q_type,
                                    int backward) {
+  if (!dtype_ok(q_type)) return 0;
   size_t most = 0;
   for (int32_t b = 1; b <= 4096; b *= 2) {
     const size_t t = halo_linear_workspace_bytes_ex(m, n, k, b, q_type, backward);
@@ -348,6 +373,7 @@ halo_status halo_linear_fwd_ex(const void* x, const void* w, halo_dtype io_type,
                                int64_t n, int64_t k, int32_t block, halo_dtype q_type, void* y,
                                halo_dtype y_type, const halo_linear_opts* opts, void* ws,
                                size_t ws_bytes, void* stream) {
+  if (!dtype_ok(io_type) || !dtype_ok(q_type) || !dtype_ok(y_type)) return HALO_ERR_DTYPE;
   if (!layer_dims_ok(m, n, k) || k == 0) return HALO_ERR_SHAPE;
   if ((m > 0 && !x) || (n > 0 && !w) || (m > 0 && n > 0 && !y)) return HALO_ERR_NULL;
   if (io_type != HALO_F32 && io_type != HALO_BF16) return HALO_ERR_DTYPE;
@@ -395,6 +421,7 @@ halo_status halo_linear_fwd_ex(const void* x, const void* w, halo_dtype io_type,
 halo_status halo_linear_fwd(const void* x, const void* w, halo_dtype io_type, int64_t m,
                             int64_t n, int64_t k, int32_t block, halo_dtype q_type, void* y,
                             halo_dtype y_type, void* ws, size_t ws_bytes, void* stream) {
+  if (!dtype_ok(io_type) || !dtype_ok(q_type) || !dtype_ok(y_type)) return HALO_ERR_DTYPE;
   return halo_linear_fwd_ex(x, w, io_type, m, n, k, block, q_type, y, y_type, nullptr, ws,
                             ws_bytes, stream);
 }
@@ -404,6 +431,7 @@ halo_status halo_linear_bwd_ex(const void* dy, const void* x, const void* w, hal
                                halo_dtype grad_q_type, void* dx, void* dw,
                                const halo_linear_opts* opts, void* ws, size_t ws_bytes,
                                void* stream) {
+  if (!dtype_ok(io_type) || !dtype_ok(q_type) || !dtype_ok(grad_q_type)) return HALO_ERR_DTYPE;
   if (!dy || !x || !w) return HALO_ERR_NULL;
   if (io_type != HALO_F32 && io_type != HALO_BF16) return HALO_ERR_DTYPE;
   if (q_type == HALO_I8) {
@@ -554,6 +582,7 @@ halo_status halo_linear_bwd(const void* dy, const void* x, const void* w, halo_d
                             int64_t m, int64_t n, int64_t k, int32_t block, halo_dtype q_type,
                             halo_dtype grad_q_type, void* dx, void* dw, void* ws,
                             size_t ws_bytes, void* stream) {
+  if (!dtype_ok(io_type) || !dtype_ok(q_type) || !dtype_ok(grad_q_type)) return HALO_ERR_DTYPE;
   return halo_linear_bwd_ex(dy, x, w, io_type, m, n, k, block, q_type, grad_q_type, dx, dw,
                             nullptr, ws, ws_bytes, stream);
 }

@@ -21,5 +21,17 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_sanitized(out: str, verbose: bool = False) -> str:
+    """The same oracle built with AddressSanitizer and UndefinedBehaviorSanitizer (gcc), for
+    the CPU test that runs the oracle's pins under them; any finding aborts."""
+    cmd = ["gcc", "-O1", "-g", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+           "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=undefined", "-fPIC", "-shared", "-o", out, SRC, "-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
