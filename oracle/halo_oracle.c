@@ -559,7 +559,9 @@ int hor_gemm_i8(const int8_t* a, const int8_t* b, int64_t m, int64_t n, int64_t 
     return OR_OK;
 }
 
-/* out[i,j] = sum_k dec(a[i,k]) * dec(b[j,k]) in fp64. */
+/* out[i,j] = sum_k dec(a[i,k]) * dec(b[j,k]) in fp64, summed in order of k.  The codes are
+ * decoded once into fp64 tables of the two operands (the same exact values), then the sums
+ * are taken. */
 int hor_gemm_fp8(const uint8_t* a, int afmt, const uint8_t* b, int bfmt, int64_t m, int64_t n,
                  int64_t k, double* out)
 {
@@ -567,14 +569,31 @@ int hor_gemm_fp8(const uint8_t* a, int afmt, const uint8_t* b, int bfmt, int64_t
     if ((afmt != OR_E4M3 && afmt != OR_E5M2) || (bfmt != OR_E4M3 && bfmt != OR_E5M2)) return OR_EARG;
     const fp8_fmt* fa = fmt_of(afmt);
     const fp8_fmt* fb = fmt_of(bfmt);
+    double ta[256], tb[256];
+    for (int c = 0; c < 256; ++c) {
+        ta[c] = fp8_decode((uint8_t)c, fa);
+        tb[c] = fp8_decode((uint8_t)c, fb);
+    }
+    double* da = (double*)malloc(nz(m * k) * sizeof(double));
+    double* db = (double*)malloc(nz(n * k) * sizeof(double));
+    if (!da || !db) {
+        free(da);
+        free(db);
+        return OR_ENOMEM;
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < m * k; ++i) da[i] = ta[a[i]];
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n * k; ++i) db[i] = tb[b[i]];
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < m; ++i)
         for (int64_t j = 0; j < n; ++j) {
             double s = 0.0;
-            for (int64_t t = 0; t < k; ++t)
-                s += fp8_decode(a[i * k + t], fa) * fp8_decode(b[j * k + t], fb);
+            for (int64_t t = 0; t < k; ++t) s += da[i * k + t] * db[j * k + t];
             out[i * n + j] = s;
         }
+    free(da);
+    free(db);
     return OR_OK;
 }
 
