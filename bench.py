@@ -9,11 +9,17 @@ whole step, rotations included.
 
 Inputs are synthetic (synth.layer: N(0,1) activations with 0.1% outlier channels x50, weights
 0.02 * N(0,1), Student-t(4) * 1e-3 gradients), already resident in HBM.  Several input sets
-rotate from step to step so that no operand stays in the 256 MB Infinity Cache.
+rotate from step to step so that no operand stays in the 256 MB Infinity Cache.  Before the
+counted warmup, steps run for --settle-s seconds: the chip's power management moves the clock
+during the first second or so of load, and the timed steps should see the clock it sustains.
+The shader clock and the board power are sampled from sysfs on a host thread while the steps
+are timed, and reported beside the result.
 
 Per-kernel figures are measured in the same run with HIP events on the launch stream: the
 INT8 GEMM (the dominant kernel, MFMA-bound) and the rows / columns rotation passes
-(HBM-bound).  The CPU baseline times the oracle on one full step of the same layer.
+(HBM-bound), each cycling through more than 512 MB of distinct inputs so that no operand is
+served from the Infinity Cache.  The CPU baseline times the oracle on full steps of the same
+layer on all host threads, a one-thread sample of it, and each pass's oracle / GPU ratio.
 
 Other modes:
   --kernels-only        launch each hot kernel --kernel-iters times next to a 64 MiB
@@ -122,6 +128,112 @@ def time_events(fn, iters, torch):
     return e0.elapsed_time(e1) / iters
 
 
+class ClockSampler:
+    """Samples the GPU's current shader clock (sysfs pp_dpm_sclk: the level marked '*') and
+    its board power (hwmon power1_input, microwatts) every `period` seconds on a host thread
+    while active.  Either reading may be missing on a machine; its summary is then None."""
+
+    def __init__(self, period=0.01):
+        import threading
+        self.period = period
+        self.sclk_path = next(iter(sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))),
+                              None)
+        dev = os.path.dirname(self.sclk_path) if self.sclk_path else None
+        self.power_path = next(iter(sorted(glob.glob(os.path.join(dev, "hwmon", "*",
+                                                                  "power1_input")))), None) \
+            if dev else None
+        self.sclk, self.power = [], []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        if self.sclk_path:
+            try:
+                with open(self.sclk_path) as f:
+                    for line in f:
+                        if "*" in line:
+                            m = re.search(r"(\d+)\s*Mhz", line, re.I)
+                            if m:
+                                self.sclk.append(int(m.group(1)))
+            except OSError:
+                pass
+        if self.power_path:
+            try:
+                with open(self.power_path) as f:
+                    self.power.append(int(f.read().strip()) / 1e6)
+            except (OSError, ValueError):
+                pass
+
+    def _run(self):
+        while not self._stop.is_set():
+            self._read()
+            time.sleep(self.period)
+
+    def __enter__(self):
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._thread.join()
+
+    @staticmethod
+    def _stats(v, nd):
+        if not v:
+            return None
+        a = np.array(v, dtype=np.float64)
+        return {"median": round(float(np.median(a)), nd), "min": round(float(a.min()), nd),
+                "max": round(float(a.max()), nd), "samples": int(a.size)}
+
+    def summary(self):
+        return {"sclk_mhz": self._stats(self.sclk, 0), "power_w": self._stats(self.power, 1),
+                "source": self.sclk_path}
+
+
+def settle(step, seconds, torch):
+    """Run steps until `seconds` have passed (in groups of 10, synchronised): the clock-settle
+    phase before the counted warmup.  Returns (steps run, seconds)."""
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            step(n)
+            n += 1
+        torch.cuda.synchronize()
+    return n, time.perf_counter() - t0
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _one_thread_sample():
+    """The oracle on one host thread (run in a child process with OMP_NUM_THREADS=1): the six
+    rotation passes of a step at full size and one product on a 256-row slab of its A
+    operand.  Returns the seconds of each part as JSON on stdout."""
+    import oracle as O
+    import synth
+    x, w, dy = synth.layer(M, N, K, seed=1001)
+    t0 = time.perf_counter()
+    qx, sx = O.fwht_quant(x, O.ROWS, BLOCK, O.I8)
+    qw, sw = O.fwht_quant(w, O.ROWS, BLOCK, O.I8)
+    O.fwht_quant(dy, O.ROWS, BLOCK, O.I8)
+    O.fwht_quant(w, O.COLS, BLOCK, O.I8)
+    O.fwht_quant(dy, O.COLS, BLOCK, O.I8)
+    O.fwht_quant(x, O.COLS, BLOCK, O.I8)
+    t1 = time.perf_counter()
+    O.dequant(O.gemm_i8(qx[:256], qw).astype(np.float64), sx[:256], sw)
+    t2 = time.perf_counter()
+    print(json.dumps({"threads": O.num_threads(), "fq_s": t1 - t0, "slab_s": t2 - t1}))
+
+
 def cpu_baseline():
     """The oracle (plain C, int64 / fp64, OpenMP over vectors and output rows) on one full
     fwd+bwd step of the same 4096^3 layer: the six rotation + quantisation passes and the three
@@ -150,11 +262,31 @@ def cpu_baseline():
         product(*fq(dy, O.COLS), *fq(x, O.COLS))     # dW = dY^T X, rotation along M
         steps += 1
     wall = time.perf_counter() - t0
-    return {"value": round(steps * STEP_GOP / 1e3 / wall, 6), "unit": "TOP/s",
-            "cores": O.num_threads(), "kind": "oracle",
-            "sample": (f"{steps} full fwd+bwd step(s) of the 4096^3 layer (seed 1001), repeated "
-                       f"to at least 10 s: rotation passes {t['fq']:.2f} s + INT8 products with "
-                       f"dequant {t['gemm']:.2f} s = {wall:.2f} s wall")}
+    out = {"value": round(steps * STEP_GOP / 1e3 / wall, 6), "unit": "TOP/s",
+           "cores": O.num_threads(), "kind": "oracle",
+           "sample": (f"{steps} full fwd+bwd step(s) of the 4096^3 layer (seed 1001), repeated "
+                      f"to at least 10 s: rotation passes {t['fq']:.2f} s + INT8 products with "
+                      f"dequant {t['gemm']:.2f} s = {wall:.2f} s wall"),
+           "cpu_model": cpu_model(), "nproc": os.cpu_count(),
+           "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
+           "per_pass_ms": {"fq": round(t["fq"] * 1e3 / (6 * steps), 2),
+                           "product": round(t["gemm"] * 1e3 / (3 * steps), 2)}}
+    # one thread, in a child process (the thread count of OpenMP is fixed at its start)
+    import subprocess
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, os.path.abspath(__file__), "--one-thread-sample"],
+                       capture_output=True, text=True, env=env, timeout=600)
+    if r.returncode == 0 and r.stdout.strip():
+        one = json.loads(r.stdout.strip().splitlines()[-1])
+        step_s = one["fq_s"] + 3 * (M / 256) * one["slab_s"]
+        out["one_thread"] = {
+            "threads": one["threads"], "value": round(STEP_GOP / 1e3 / step_s, 6),
+            "unit": "TOP/s", "fq_ms": round(one["fq_s"] * 1e3 / 6, 2),
+            "product_ms": round(one["slab_s"] * (M / 256) * 1e3, 2),
+            "sample": (f"the six rotation passes of a step at full size ({one['fq_s']:.2f} s) "
+                       f"and one INT8 product on a 256-row slab ({one['slab_s']:.2f} s); the "
+                       f"step's products extrapolated linearly by rows (x{M // 256})")}
+    return out
 
 
 def make_inputs(torch):
@@ -191,28 +323,36 @@ def measure_kernels(H, torch, sets, iters, with_copy=False):
     import ctypes
     P, ld, code = H._ptr, H._ld, H._code
     st = H._stream(None)
-    codes = [H.fwht_quant(X, axis=H.ROWS, block=BLOCK) for (X, _, _) in sets[:2]]
-    wcodes = [H.fwht_quant(W, axis=H.ROWS, block=BLOCK) for (_, W, _) in sets[:2]]
+    # every leg cycles through more than 512 MB of distinct inputs: the 18 bf16 matrices of
+    # the input sets (604 MB) for the rotation passes, and 18 pairs of 16 MiB code matrices
+    # (604 MB: rows and columns codes of those matrices) for the products
+    mats = [t for st_ in sets for t in st_]
     e4 = torch.float8_e4m3fn
-    f8x = [H.fwht_quant(X, axis=H.ROWS, block=BLOCK, q_dtype=e4) for (X, _, _) in sets[:2]]
-    f8w = [H.fwht_quant(W, axis=H.ROWS, block=BLOCK, q_dtype=e4) for (_, W, _) in sets[:2]]
+    c8 = [H.fwht_quant(t, axis=ax, block=BLOCK) for ax in (H.ROWS, H.COLS) for t in mats]
+    f8 = [H.fwht_quant(t, axis=ax, block=BLOCK, q_dtype=e4) for ax in (H.ROWS, H.COLS)
+          for t in mats]
+    half = len(mats)
+    codes, wcodes = c8[:half], c8[half:]
+    f8x, f8w = f8[:half], f8[half:]
     y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
     qbuf = torch.empty((M, K), dtype=torch.int8, device="cuda:0")
     sbuf = torch.empty(max(M, K), dtype=torch.float32, device="cuda:0")
     wsc = torch.empty(max(H.fwht_quant_workspace_bytes(M, N, H.COLS, BLOCK), 256),
                       dtype=torch.uint8, device="cuda:0")
     signs = H.hadamard_signs(K, seed=2024, device="cuda:0")
-    padded = [X[:, :K_PAD].contiguous() for (X, _, _) in sets]
+    padded = [t[:, :K_PAD].contiguous() for t in mats]
     keep = []  # option structs referenced by the prepared argument lists
 
     def gemm_args(a, b, kind_code):
         return (P(a[0]), ld(a[0]), P(a[1]), P(b[0]), ld(b[0]), P(b[1]), M, N, K, P(y),
                 code(y.dtype), ld(y), st)
 
-    gemm = _c_launcher(H, "halo_gemm_i8", [gemm_args(codes[i], wcodes[i], 0) for i in range(2)])
+    gemm = _c_launcher(H, "halo_gemm_i8", [gemm_args(codes[i], wcodes[i], 0)
+                                            for i in range(half)])
     gemm_fp8 = _c_launcher(H, "halo_gemm_fp8", [
         (P(f8x[i][0]), code(e4), ld(f8x[i][0]), P(f8x[i][1]), P(f8w[i][0]), code(e4),
-         ld(f8w[i][0]), P(f8w[i][1]), M, N, K, P(y), code(y.dtype), ld(y), st) for i in range(2)])
+         ld(f8w[i][0]), P(f8w[i][1]), M, N, K, P(y), code(y.dtype), ld(y), st)
+        for i in range(half)])
 
     def fq_args(x, axis, opts=None, ws=None):
         rows_, cols_ = x.shape
@@ -230,12 +370,11 @@ def measure_kernels(H, torch, sets, iters, with_copy=False):
         return H.QuantOpts(P(signs), H.STOCHASTIC, H._u32x2(SEED64), H._u32x2(i))
 
     fq = "halo_fwht_quant_ex"
-    rows = _c_launcher(H, fq, [fq_args(X, H.ROWS) for (X, _, _) in sets])
-    cols = _c_launcher(H, fq, [fq_args(DY, H.COLS, ws=wsc) for (_, _, DY) in sets])
-    rows_opt = _c_launcher(H, fq, [fq_args(sets[i][2], H.ROWS, sr_opts(i))
-                                   for i in range(N_SETS)])
-    cols_opt = _c_launcher(H, fq, [fq_args(sets[i][2], H.COLS, sr_opts(i), wsc)
-                                   for i in range(N_SETS)])
+    rows = _c_launcher(H, fq, [fq_args(t, H.ROWS) for t in mats])
+    cols = _c_launcher(H, fq, [fq_args(t, H.COLS, ws=wsc) for t in mats])
+    rows_opt = _c_launcher(H, fq, [fq_args(t, H.ROWS, sr_opts(i)) for i, t in enumerate(mats)])
+    cols_opt = _c_launcher(H, fq, [fq_args(t, H.COLS, sr_opts(i), wsc)
+                                   for i, t in enumerate(mats)])
     rows_pad = _c_launcher(H, fq, [fq_args(Xp, H.ROWS) for Xp in padded])
 
     legs = {"gemm_i8_4096": gemm, "gemm_fp8_4096": gemm_fp8, "fq_rows_4096": rows,
@@ -446,7 +585,14 @@ def main():
     ap.add_argument("--out", help="summary file to write")
     ap.add_argument("--last", type=int, default=0, help="trace calls per pass to average")
     ap.add_argument("--workload", help="time one named parity workload instead (see synth)")
+    ap.add_argument("--settle-s", type=float, default=2.0,
+                    help="seconds of steps before the counted warmup (clock settle)")
+    ap.add_argument("--one-thread-sample", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
+
+    if args.one_thread_sample:
+        _one_thread_sample()
+        return
 
     if args.summarize_stats:
         text = summarize_stats(args.summarize_stats, args.command, args.last)
@@ -499,18 +645,20 @@ def main():
         H.linear_fwd(X, W, BLOCK, y=y, workspace=ws_f)
         H.linear_bwd(DY, X, W, BLOCK, dx=dx, dw=dw, workspace=ws_b)
 
+    settle_steps, settle_s = settle(step, args.settle_s, torch)
     for i in range(args.warmup):
         step(i)
     st = torch.cuda.current_stream()
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        evs[i].record(st)
-        step(i)
-    evs[-1].record(st)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    with ClockSampler() as clk:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            evs[i].record(st)
+            step(i)
+        evs[-1].record(st)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
     ms_step = elapsed * 1e3 / args.steps
     value = STEP_GOP / (ms_step * 1e-3) / 1e3  # TOP/s
     per_step = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
@@ -550,7 +698,8 @@ def main():
     ms_bwd256 = time_events(bwd_256, args.steps, torch)
 
     # ---- per-kernel measurements (same kernels, same shapes, HIP events on the stream) ----
-    t = measure_kernels(H, torch, sets, args.kernel_iters)
+    with ClockSampler() as clk_k:
+        t = measure_kernels(H, torch, sets, args.kernel_iters)
     t_large = measure_large_passes(H, torch, max(5, args.kernel_iters // 6))
     t_gemm, t_rows, t_cols = t["gemm_i8_4096"], t["fq_rows_4096"], t["fq_cols_4096"]
     gemm_tops = GEMM_OPS / (t_gemm * 1e-3) / 1e12
@@ -585,6 +734,9 @@ def main():
         "step_ms": {"p10": round(float(np.percentile(per_step, 10)), 4),
                     "p50": round(float(np.percentile(per_step, 50)), 4),
                     "p90": round(float(np.percentile(per_step, 90)), 4)},
+        "settle": {"steps": settle_steps, "s": round(settle_s, 2),
+                   "what": "steps run before the counted warmup, until the clock settles"},
+        "clock": {"timed_steps": clk.summary(), "kernel_legs": clk_k.summary()},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 2), "peak": PEAK_INT8_TOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
                      "traffic": load_traffic("gemm_i8_4096"),
@@ -625,7 +777,10 @@ def main():
         },
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline()
+        cb = cpu_baseline()
+        gpu_ms = {"fq": (t_rows + t_cols) / 2, "product": t_gemm}
+        cb["oracle_over_gpu"] = {k: round(cb["per_pass_ms"][k] / gpu_ms[k], 1) for k in gpu_ms}
+        result["cpu_baseline"] = cb
     print(json.dumps(result), flush=True)
 
 
