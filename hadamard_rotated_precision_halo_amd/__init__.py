@@ -23,11 +23,13 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhalo.so"
 F32, BF16, I8, E4M3, E5M2, I32 = range(6)
 ROWS, COLS = 0, 1
 NEAREST, STOCHASTIC = 0, 1  # halo_rounding
+NOALLOC_SCRATCH_BYTES = 1 << 20  # HALO_NOALLOC_SCRATCH_BYTES
 STATUS = {0: "HALO_OK", 1: "HALO_ERR_NULL", 2: "HALO_ERR_SHAPE", 3: "HALO_ERR_BLOCK",
           4: "HALO_ERR_DTYPE", 5: "HALO_ERR_ALIGN", 6: "HALO_ERR_WORKSPACE", 7: "HALO_ERR_HIP",
           8: "HALO_ERR_OPTION"}
 
-EXPORTS = ("halo_fwht_quant", "halo_fwht_quant_ex", "halo_fwht_quant_workspace_bytes",
+EXPORTS = ("halo_fwht_quant", "halo_fwht_quant_ex", "halo_fwht_quant_noalloc",
+           "halo_fwht_quant_workspace_bytes",
            "halo_gemm_i8", "halo_gemm_fp8", "halo_linear_workspace_bytes",
            "halo_linear_workspace_bytes_ex", "halo_linear_fwd", "halo_linear_fwd_ex",
            "halo_linear_bwd", "halo_linear_bwd_ex", "halo_status_str")
@@ -82,6 +84,8 @@ def lib():
         qo, lo = ctypes.POINTER(QuantOpts), ctypes.POINTER(LinearOpts)
         L.halo_fwht_quant_ex.argtypes = [vp, e, i64, i64, i64, e, i32, e, vp, i64, vp, qo, vp, sz,
                                          vp]
+        L.halo_fwht_quant_noalloc.argtypes = [vp, e, i64, i64, i64, e, i32, e, vp, i64, vp, qo,
+                                              vp]
         L.halo_linear_workspace_bytes_ex.argtypes = [i64, i64, i64, i32, e, ctypes.c_int]
         L.halo_linear_workspace_bytes_ex.restype = sz
         L.halo_linear_fwd_ex.argtypes = [vp, vp, e, i64, i64, i64, i32, e, vp, e, lo, vp, sz, vp]
@@ -89,7 +93,8 @@ def lib():
                                          sz, vp]
         L.halo_status_str.argtypes = [e]
         L.halo_status_str.restype = ctypes.c_char_p
-        for f in ("halo_fwht_quant", "halo_fwht_quant_ex", "halo_gemm_i8", "halo_gemm_fp8",
+        for f in ("halo_fwht_quant", "halo_fwht_quant_ex", "halo_fwht_quant_noalloc",
+                  "halo_gemm_i8", "halo_gemm_fp8",
                   "halo_linear_fwd", "halo_linear_fwd_ex", "halo_linear_bwd",
                   "halo_linear_bwd_ex"):
             getattr(L, f).restype = ctypes.c_int
@@ -215,6 +220,24 @@ def fwht_quant(x, axis=ROWS, block=256, q_dtype=torch.int8, q=None, scale=None, 
                                   ctypes.byref(opts) if opts is not None else None, ws_ptr,
                                   ws_bytes, _stream(stream))
     _check(st, "halo_fwht_quant_ex")
+    return q, scale
+
+
+def fwht_quant_noalloc(x, q, scale, axis=ROWS, block=256, stream=None, signs=None,
+                       rounding="nearest", seed=0, counter=0, exchange_polls=0):
+    """fwht_quant into caller-provided q and scale with the library's fixed scratch in place of
+    a workspace (halo_fwht_quant_noalloc): nothing is allocated.  Calls that may overlap on one
+    device share that scratch and must be ordered by the caller."""
+    rows, cols = x.shape
+    opts = None
+    rnd = _rounding(rounding)
+    if signs is not None or rnd != NEAREST or exchange_polls:
+        opts = QuantOpts(_ptr(signs), rnd, _u32x2(seed), _u32x2(counter), int(exchange_polls))
+    st = lib().halo_fwht_quant_noalloc(_ptr(x), _code(x.dtype), rows, cols, _ld(x), axis,
+                                       int(block), _code(q.dtype), _ptr(q), _ld(q), _ptr(scale),
+                                       ctypes.byref(opts) if opts is not None else None,
+                                       _stream(stream))
+    _check(st, "halo_fwht_quant_noalloc")
     return q, scale
 
 

@@ -10,12 +10,31 @@
 #include "../../include/halo.h"
 #include "halo_kernels.h"
 
+#include <atomic>
 #include <cmath>
 #include <cstring>
 
 using namespace halo;
 
+// Scratch of halo_fwht_quant_noalloc: a fixed device array, one copy per device, held until
+// the process ends.  In host code its name stands for a host-side shadow, not a device
+// address: the device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[HALO_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+// Device address of `scratch` on the current device, looked up once per device (concurrent
+// first calls may both look it up and store the same address).  NULL on a HIP error.
+void* noalloc_scratch() {
+  static std::atomic<void*> addr[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+  addr[dev].store(p, std::memory_order_release);
+  return p;
+}
 
 // Whether an enum argument holds a value in [lo, hi].  A C caller may pass any int in an enum
 // parameter, and in C++ loading an enum object whose value lies outside the enum's range is
@@ -264,6 +283,10 @@ halo_status gemm_any(const void* a, halo_dtype at, int64_t lda, const float* sa,
   return from_hip(launch_gemm(g, 1, gemm_kind_fmt(at), gemm_kind_fmt(bt), out, st));
 }
 
+bool layer_dims_ok(int64_t m, int64_t n, int64_t k) {
+  return m >= 0 && n >= 0 && k >= 0 && m < kMaxDim && n < kMaxDim && k < kMaxDim;
+}
+
 }  // namespace
 
 extern "C" {
@@ -316,6 +339,22 @@ halo_status halo_fwht_quant(const void* x, halo_dtype x_type, int64_t rows, int6
                             nullptr, ws, ws_bytes, stream);
 }
 
+halo_status halo_fwht_quant_noalloc(const void* x, halo_dtype x_type, int64_t rows, int64_t cols,
+                                    int64_t ldx, halo_axis axis, int32_t block,
+                                    halo_dtype q_type, void* q, int64_t ldq, float* scale,
+                                    const halo_quant_opts* opts, void* stream) {
+  if (!dtype_ok(x_type) || !dtype_ok(q_type)) return HALO_ERR_DTYPE;
+  if (!axis_ok(axis)) return HALO_ERR_SHAPE;
+  halo_status s = check_fq(x, x_type, rows, cols, ldx, axis, block, q_type, q, ldq, scale, opts);
+  if (s != HALO_OK) return s;
+  const size_t need = halo_fwht_quant_workspace_bytes(rows, cols, axis, block, x_type);
+  if (need > HALO_NOALLOC_SCRATCH_BYTES) return HALO_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0 && !(ws = noalloc_scratch())) return HALO_ERR_HIP;
+  return run_fq(x, x_type, rows, cols, ldx, axis, block, q_type, q, ldq, scale, ws,
+                ws ? HALO_NOALLOC_SCRATCH_BYTES : 0, (hipStream_t)stream, pass_opts(opts));
+}
+
 halo_status halo_gemm_i8(const int8_t* a, int64_t lda, const float* sa, const int8_t* b,
                          int64_t ldb, const float* sb, int64_t m, int64_t n, int64_t k, void* c,
                          halo_dtype c_type, int64_t ldc, void* stream) {
@@ -343,11 +382,6 @@ halo_status halo_gemm_fp8(const void* a, halo_dtype a_type, int64_t lda, const f
                   (hipStream_t)stream);
 }
 
-namespace {
-bool layer_dims_ok(int64_t m, int64_t n, int64_t k) {
-  return m >= 0 && n >= 0 && k >= 0 && m < kMaxDim && n < kMaxDim && k < kMaxDim;
-}
-}  // namespace
 
 size_t halo_linear_workspace_bytes_ex(int64_t m, int64_t n, int64_t k, int32_t block,
                                       halo_dtype q_type, int backward) {

@@ -293,6 +293,26 @@ halo_status halo_linear_bwd_ex(const void* dy, const void* x, const void* w, hal
                                const halo_linear_opts* opts, void* ws, size_t ws_bytes,
                                void* stream);
 
+/*
+ * For callers that cannot allocate (code under HIP graph capture, tight serving loops, hosts
+ * that forbid allocation): halo_fwht_quant_ex with the columns pass's exchange scratch taken
+ * from a fixed array inside the library instead of a caller workspace, so that long bf16
+ * columns are still read once.  The call allocates and frees nothing, on the host or the
+ * device.  The array holds HALO_NOALLOC_SCRATCH_BYTES bytes, one copy per device, kept until
+ * the process ends; a pass that needs more (halo_fwht_quant_workspace_bytes(...) larger than
+ * that: columns of over 4096 rows with more than about 250,000 columns) is refused with
+ * HALO_ERR_WORKSPACE before anything is launched.  Passes that need no scratch run as
+ * halo_fwht_quant_ex.  Every call on one device shares the array and clears what it uses at
+ * its start, on its stream: calls that may overlap on one device (other streams, other host
+ * threads) race on it and must be ordered by the caller.  Other arguments, results and
+ * errors as halo_fwht_quant_ex.
+ */
+#define HALO_NOALLOC_SCRATCH_BYTES ((size_t)1 << 20)
+halo_status halo_fwht_quant_noalloc(const void* x, halo_dtype x_type, int64_t rows, int64_t cols,
+                                    int64_t ldx, halo_axis axis, int32_t block,
+                                    halo_dtype q_type, void* q, int64_t ldq, float* scale,
+                                    const halo_quant_opts* opts, void* stream);
+
 /* Static description of a status code. */
 const char* halo_status_str(halo_status s);
 
