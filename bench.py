@@ -74,10 +74,10 @@ TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic_4096.json")
 PASSES = {
     "gemm_i8_4096": ["halo::gemm_kernel<0"],
     "fq_rows_4096": ["halo::fq_rows2_kernel<unsigned short, 256, 0, false>"],
-    "fq_cols_4096": ["halo::fq_cols2_kernel<256, 0, false>"],
+    "fq_cols_4096": ["halo::fq_cols2_kernel<256, 0, false, false>"],
     "gemm_fp8_4096": ["halo::gemm_kernel<1"],
     "fq_rows_opt_4096": ["halo::fq_rows2_kernel<unsigned short, 256, 0, true>"],
-    "fq_cols_opt_4096": ["halo::fq_cols2_kernel<256, 0, true>"],
+    "fq_cols_opt_4096": ["halo::fq_cols2_kernel<256, 0, true, false>"],
     "copy_64MiB": ["neg_kernel"],
 }
 
@@ -377,6 +377,33 @@ def measure_kernels(H, torch, sets, iters, with_copy=False):
                                    for i, t in enumerate(mats)])
     rows_pad = _c_launcher(H, fq, [fq_args(Xp, H.ROWS) for Xp in padded])
 
+    # the INT8 product as the forward runs it: its codes written just before by the rows
+    # passes of that step's X and W (so they sit where the rotation left them), events
+    # around the product's launch alone
+    qx = torch.empty((M, K), dtype=torch.int8, device="cuda:0")
+    qw = torch.empty((N, K), dtype=torch.int8, device="cuda:0")
+    sxw = torch.empty(M + N, dtype=torch.float32, device="cuda:0")
+    rows_xw = _c_launcher(H, fq, [
+        (P(t), code(t.dtype), t.shape[0], t.shape[1], ld(t), H.ROWS, BLOCK, code(torch.int8),
+         P(q_), ld(q_), ctypes.c_void_p(sxw.data_ptr() + 4 * M * w_), None, None, 0, st)
+        for st_ in sets for t, q_, w_ in ((st_[0], qx, 0), (st_[1], qw, 1))])
+    gemm_xw = _c_launcher(H, "halo_gemm_i8", [
+        (P(qx), ld(qx), P(sxw), P(qw), ld(qw), ctypes.c_void_p(sxw.data_ptr() + 4 * M),
+         M, N, K, P(y), code(y.dtype), ld(y), st)])
+
+    def gemm_in_path(iters_):
+        stream = torch.cuda.current_stream()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(iters_)]
+        for i in range(iters_):
+            rows_xw(2 * i)
+            rows_xw(2 * i + 1)
+            ev[i][0].record(stream)
+            gemm_xw(0)
+            ev[i][1].record(stream)
+        ev[-1][1].synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
     legs = {"gemm_i8_4096": gemm, "gemm_fp8_4096": gemm_fp8, "fq_rows_4096": rows,
             "fq_cols_4096": cols, "fq_rows_opt_4096": rows_opt, "fq_cols_opt_4096": cols_opt,
             "fq_rows_pad_4000": rows_pad}
@@ -386,9 +413,12 @@ def measure_kernels(H, torch, sets, iters, with_copy=False):
     # three rounds over all legs, the median per leg: the clock of a power-limited chip
     # still wanders in the first few hundred milliseconds of load
     runs = {k: [] for k in legs}
+    runs["gemm_i8_4096_in_path"] = []
+    gemm_in_path(3)
     for _ in range(3):
         for k, f in legs.items():
             runs[k].append(time_events(f, iters, torch))
+        runs["gemm_i8_4096_in_path"].append(gemm_in_path(iters))
     out = {k: float(np.median(v)) for k, v in runs.items()}
     if with_copy:
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0").normal_()
@@ -701,7 +731,8 @@ def main():
     with ClockSampler() as clk_k:
         t = measure_kernels(H, torch, sets, args.kernel_iters)
     t_large = measure_large_passes(H, torch, max(5, args.kernel_iters // 6))
-    t_gemm, t_rows, t_cols = t["gemm_i8_4096"], t["fq_rows_4096"], t["fq_cols_4096"]
+    t_gemm, t_rows, t_cols = t["gemm_i8_4096_in_path"], t["fq_rows_4096"], t["fq_cols_4096"]
+    t_gemm_cold = t["gemm_i8_4096"]
     gemm_tops = GEMM_OPS / (t_gemm * 1e-3) / 1e12
     rows_gbs = FQ_BYTES / (t_rows * 1e-3) / 1e9
     cols_gbs = FQ_BYTES / (t_cols * 1e-3) / 1e9
@@ -741,7 +772,14 @@ def main():
                      "unit": "TFLOP/s", "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
                      "traffic": load_traffic("gemm_i8_4096"),
                      "kernel": "gemm_kernel<INT8, bf16 out> 4096x4096x4096",
-                     "ms_per_launch": round(t_gemm, 5), "algorithmic_ops": GEMM_OPS},
+                     "ms_per_launch": round(t_gemm, 5), "algorithmic_ops": GEMM_OPS,
+                     "measured": "as the forward runs it: codes written just before by the "
+                                 "rows passes of that step's X and W, events around the product",
+                     "cold": {"ms_per_launch": round(t_gemm_cold, 5),
+                              "frac": round(GEMM_OPS / (t_gemm_cold * 1e-3) / 1e12
+                                            / PEAK_INT8_TOPS, 4),
+                              "what": "back-to-back launches cycling 18 pairs of code matrices "
+                                      "(604 MB), none left in the Infinity Cache"}},
         "fwht_quant": {"rows": hbm(rows_gbs, t_rows, "fq_rows_4096"),
                        "cols": hbm(cols_gbs, t_cols, "fq_cols_4096")},
         "gemm_fp8": {"bound": "mfma", "achieved": round(GEMM_OPS / (t["gemm_fp8_4096"] * 1e-3) / 1e12, 2),

@@ -655,10 +655,28 @@ __device__ __forceinline__ void cols_task(const ColsProb& pr, int64_t ltask, uin
 
 // REPAIR: the follow-up launch of a pass whose strips are split over several tasks; it
 // stores the parts of strips marked late (see cols_task) and returns at once for the rest.
+// Whether any task of the passes whose late counters are given stopped waiting (read once by
+// one thread of the workgroup and shared): the repair launches return at once when none did.
+__device__ __forceinline__ bool any_late(const uint32_t* a, const uint32_t* b, const uint32_t* c) {
+  __shared__ uint32_t s_any;
+  if (threadIdx.x == 0) {
+    uint32_t n = 0;
+    if (a) n |= __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (b) n |= __hip_atomic_load(b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (c) n |= __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_any = n;
+  }
+  __syncthreads();
+  return s_any != 0;
+}
+
 template <int B, int QT, bool SR, bool REPAIR = false>
 __global__ __launch_bounds__(1024) void fq_cols2_kernel(ColsProb c0, ColsProb c1, int64_t split,
                                                         int64_t tasks) {
   extern __shared__ __attribute__((aligned(16))) uint4 lds[];
+  if constexpr (REPAIR) {
+    if (!any_late(c0.P > 1 ? c0.late : nullptr, c1.P > 1 ? c1.late : nullptr, nullptr)) return;
+  }
   for (int64_t task = blockIdx.x; task < tasks; task += gridDim.x) {
     const bool second = task >= split;
     const ColsProb pr = second ? c1 : c0;
@@ -683,14 +701,33 @@ struct FqBatch {
 template <int B, int QG, int QW, bool SR, bool REPAIR = false>
 __global__ __launch_bounds__(1024) void fq_batch_kernel(FqBatch fb) {
   extern __shared__ __attribute__((aligned(16))) uint4 lds[];
+  if constexpr (REPAIR) {
+    // a grid of at most one workgroup per compute unit, striding over the column tasks
+    if (!any_late(fb.cw.P > 1 ? fb.cw.late : nullptr, fb.cdy.P > 1 ? fb.cdy.late : nullptr,
+                  fb.cx.P > 1 ? fb.cx.late : nullptr))
+      return;
+    for (int64_t t = blockIdx.x; t < fb.end_w; t += gridDim.x) {
+      cols_task<B, QW, false, true>(fb.cw, t, lds);
+      __syncthreads();  // the next task overwrites the LDS tile
+    }
+    for (int64_t t = blockIdx.x; t < fb.end_dy - fb.end_w; t += gridDim.x) {
+      cols_task<B, QG, SR, true>(fb.cdy, t, lds);
+      __syncthreads();
+    }
+    for (int64_t t = blockIdx.x; t < fb.end_x - fb.end_dy; t += gridDim.x) {
+      cols_task<B, QW, false, true>(fb.cx, t, lds);
+      __syncthreads();
+    }
+    return;
+  }
   const int64_t bid = blockIdx.x;
   if (bid < fb.end_w) {
-    cols_task<B, QW, false, REPAIR>(fb.cw, bid, lds);
+    cols_task<B, QW, false>(fb.cw, bid, lds);
   } else if (bid < fb.end_dy) {
-    cols_task<B, QG, SR, REPAIR>(fb.cdy, bid - fb.end_w, lds);
+    cols_task<B, QG, SR>(fb.cdy, bid - fb.end_w, lds);
   } else if (bid < fb.end_x) {
-    cols_task<B, QW, false, REPAIR>(fb.cx, bid - fb.end_dy, lds);
-  } else if constexpr (!REPAIR) {
+    cols_task<B, QW, false>(fb.cx, bid - fb.end_dy, lds);
+  } else {
     rows_wave<uint16_t, B, QG, SR>(fb.rows, (bid - fb.end_x) * 16 + (threadIdx.x >> 6),
                                    threadIdx.x & 63);
   }
@@ -805,11 +842,14 @@ static hipError_t launch_cols2_t(const FqArgs& a0, void* ws0, const FqArgs* a1, 
                      kColsLdsBytes, st, p0, p1, t0, tasks);
   e = hipGetLastError();
   if (e != hipSuccess || P == 1) return e;
-  // the repair launch: stores the strips whose tasks stopped waiting (usually none; its
-  // workgroups then only read one counter each)
+  // the repair launch: stores the strips whose tasks stopped waiting.  Usually there are
+  // none, and its workgroups (at most one per compute unit, striding over the tasks) return
+  // after reading the late counters.
   e = allow_dynamic_lds<&fq_cols2_kernel<B, QT, SR, true>>(kColsLdsBytes);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((fq_cols2_kernel<B, QT, SR, true>), dim3((unsigned)tasks), dim3(1024),
+  const int cap = cols2_capacity(reinterpret_cast<const void*>(fn));
+  const int64_t rgrid = tasks < cap ? tasks : cap;
+  hipLaunchKernelGGL((fq_cols2_kernel<B, QT, SR, true>), dim3((unsigned)rgrid), dim3(1024),
                      kColsLdsBytes, st, p0, p1, t0, tasks);
   return hipGetLastError();
 }
@@ -871,7 +911,9 @@ static hipError_t launch_batch_t(const FqArgs* rows, const FqArgs& cw, void* ws_
   // the repair launch over the column tasks (see launch_cols2_t)
   e = allow_dynamic_lds<&fq_batch_kernel<B, QG, QW, SR, true>>(kColsLdsBytes);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((fq_batch_kernel<B, QG, QW, SR, true>), dim3((unsigned)fb.end_x),
+  const int cap = cols2_capacity(reinterpret_cast<const void*>(fn));
+  const int64_t rgrid = fb.end_x < cap ? fb.end_x : cap;
+  hipLaunchKernelGGL((fq_batch_kernel<B, QG, QW, SR, true>), dim3((unsigned)rgrid),
                      dim3(1024), kColsLdsBytes, st, fb);
   return hipGetLastError();
 }

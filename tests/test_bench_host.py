@@ -52,7 +52,7 @@ def test_summarize_pmc_calibrates_and_sums_each_pass(tmp_path):
     # one kernel, not the scratch fill (cols[0]) that longer column passes launch
     gemm = "void halo::gemm_kernel<0, 0, 0, 2, false, 128, 4>(halo::GemmPair)"
     cols = ["void halo::fill_zero_kernel(float*, long)",
-            "void halo::fq_cols2_kernel<256, 0, false>(halo::ColsProb, halo::ColsProb, long, long)"]
+            "void halo::fq_cols2_kernel<256, 0, false, false>(halo::ColsProb, halo::ColsProb, long, long)"]
     neg = "void at::native::neg_kernel_impl"
     _counter_csv(tmp_path / "f", "FETCH_SIZE",
                  [(gemm, 1000.0), (gemm, 3000.0), (cols[0], 1.0), (cols[1], 99.0),
