@@ -55,6 +55,7 @@ GEMM_OPS = 2 * M * N * K
 FQ_BYTES = M * K * (2 + 1) + 4 * M          # bf16 in, one code byte out, one fp32 scale/vector
 GEMM_BYTES = 2 * M * K + 2 * M * N + 4 * (M + N)  # both code operands, bf16 output, scales
 COPY_BYTES = 64 << 20                       # calibration: 64 MiB read + 64 MiB written
+COPY_REF_BYTES = 512 << 20                  # streaming reference: 512 MiB read + 512 MiB written
 KERNEL_SOURCES = ["hadamard_rotated_precision_halo_amd/csrc/gemm.hip",
                   "hadamard_rotated_precision_halo_amd/csrc/fwht_quant.hip",
                   "hadamard_rotated_precision_halo_amd/csrc/fwht_wave.h",
@@ -420,6 +421,16 @@ def measure_kernels(H, torch, sets, iters, with_copy=False):
             runs[k].append(time_events(f, iters, torch))
         runs["gemm_i8_4096_in_path"].append(gemm_in_path(iters))
     out = {k: float(np.median(v)) for k, v in runs.items()}
+    # the practical streaming rate of this HBM: torch's elementwise negation of 512 MiB into
+    # another 512 MiB (1 GiB moved per launch, two buffers cycled: nothing cache-resident)
+    big = [torch.empty(COPY_REF_BYTES // 4, dtype=torch.float32, device="cuda:0") for _ in range(4)]
+    for b_ in big:
+        b_.fill_(1.0)
+    def copy_ref(i):
+        torch.neg(big[(2 * i) % 4], out=big[(2 * i + 1) % 4])
+    copy_ref(0)
+    out["copy_ref_512MiB"] = float(np.median([time_events(copy_ref, 10, torch) for _ in range(3)]))
+    del big
     if with_copy:
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0").normal_()
         dst = torch.empty_like(src)
@@ -731,16 +742,19 @@ def main():
     with ClockSampler() as clk_k:
         t = measure_kernels(H, torch, sets, args.kernel_iters)
     t_large = measure_large_passes(H, torch, max(5, args.kernel_iters // 6))
-    t_gemm, t_rows, t_cols = t["gemm_i8_4096_in_path"], t["fq_rows_4096"], t["fq_cols_4096"]
-    t_gemm_cold = t["gemm_i8_4096"]
+    t_gemm, t_rows, t_cols = t["gemm_i8_4096"], t["fq_rows_4096"], t["fq_cols_4096"]
+    t_gemm_path = t["gemm_i8_4096_in_path"]
     gemm_tops = GEMM_OPS / (t_gemm * 1e-3) / 1e12
     rows_gbs = FQ_BYTES / (t_rows * 1e-3) / 1e9
     cols_gbs = FQ_BYTES / (t_cols * 1e-3) / 1e9
 
+    copy_gbs = 2 * COPY_REF_BYTES / (t["copy_ref_512MiB"] * 1e-3) / 1e9
+
     def hbm(gbs, ms, key, nbytes=FQ_BYTES):
         return {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": load_traffic(key),
-                "ms_per_launch": round(ms, 5), "algorithmic_bytes": nbytes}
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "frac_of_copy": round(gbs / copy_gbs, 4),
+                "traffic": load_traffic(key), "ms_per_launch": round(ms, 5),
+                "algorithmic_bytes": nbytes}
 
     def hbm_pass(key, nbytes=FQ_BYTES):
         return hbm(nbytes / (t[key] * 1e-3) / 1e9, t[key], key, nbytes)
@@ -773,15 +787,22 @@ def main():
                      "traffic": load_traffic("gemm_i8_4096"),
                      "kernel": "gemm_kernel<INT8, bf16 out> 4096x4096x4096",
                      "ms_per_launch": round(t_gemm, 5), "algorithmic_ops": GEMM_OPS,
-                     "measured": "as the forward runs it: codes written just before by the "
-                                 "rows passes of that step's X and W, events around the product",
-                     "cold": {"ms_per_launch": round(t_gemm_cold, 5),
-                              "frac": round(GEMM_OPS / (t_gemm_cold * 1e-3) / 1e12
-                                            / PEAK_INT8_TOPS, 4),
-                              "what": "back-to-back launches cycling 18 pairs of code matrices "
-                                      "(604 MB), none left in the Infinity Cache"}},
+                     "measured": "back-to-back launches cycling 18 pairs of 16 MiB code "
+                                 "matrices (604 MB), none left in the Infinity Cache",
+                     "in_path": {"ms_per_launch": round(t_gemm_path, 5),
+                                 "frac": round(GEMM_OPS / (t_gemm_path * 1e-3) / 1e12
+                                               / PEAK_INT8_TOPS, 4),
+                                 "what": "as the forward runs it: codes written just before by "
+                                         "the rows passes of that step's X and W, events around "
+                                         "the product alone"}},
         "fwht_quant": {"rows": hbm(rows_gbs, t_rows, "fq_rows_4096"),
-                       "cols": hbm(cols_gbs, t_cols, "fq_cols_4096")},
+                       "cols": hbm(cols_gbs, t_cols, "fq_cols_4096"),
+                       "copy_reference": {
+                           "achieved": round(copy_gbs, 1), "unit": "GB/s",
+                           "frac": round(copy_gbs / PEAK_HBM_GBS, 4),
+                           "what": "torch elementwise negation, 512 MiB read + 512 MiB written "
+                                   "per launch: the streaming rate a plain copy reaches here; "
+                                   "frac_of_copy of each pass is against it"}},
         "gemm_fp8": {"bound": "mfma", "achieved": round(GEMM_OPS / (t["gemm_fp8_4096"] * 1e-3) / 1e12, 2),
                      "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(GEMM_OPS / (t["gemm_fp8_4096"] * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
