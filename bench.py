@@ -70,17 +70,29 @@ LARGE_COLS_BYTES = 16384 * 14336 * 3 + 4 * 14336
 FQ_PAD_BYTES = M * K_PAD * 2 + M * K + 4 * M
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic_4096.json")
 
-# kernel-name patterns of each measured pass (rocprofv3 Kernel_Name substrings); a pass may
-# launch several kernels per call
+# kernel-name patterns of each measured pass (rocprofv3 Kernel_Name substrings; a pass may
+# launch several kernels per call) and, where one kernel serves launches of several sizes,
+# the grid (work-items) of this pass's launches: the 4096^3 products run 256 workgroups of
+# 512 work-items, the backward's paired products twice as many
+GEMM_GRID = 256 * 512
 PASSES = {
-    "gemm_i8_4096": ["halo::gemm_kernel<0"],
-    "fq_rows_4096": ["halo::fq_rows2_kernel<unsigned short, 256, 0, false>"],
-    "fq_cols_4096": ["halo::fq_cols2_kernel<256, 0, false, false>"],
-    "gemm_fp8_4096": ["halo::gemm_kernel<1"],
-    "fq_rows_opt_4096": ["halo::fq_rows2_kernel<unsigned short, 256, 0, true>"],
-    "fq_cols_opt_4096": ["halo::fq_cols2_kernel<256, 0, true, false>"],
-    "copy_64MiB": ["neg_kernel"],
+    "gemm_i8_4096": (["halo::gemm_kernel<0"], GEMM_GRID),
+    "fq_rows_4096": (["halo::fq_rows2_kernel<unsigned short, 256, 0, false>"], None),
+    "fq_cols_4096": (["halo::fq_cols2_kernel<256, 0, false, false>"], None),
+    "gemm_fp8_4096": (["halo::gemm_kernel<1"], GEMM_GRID),
+    "fq_rows_opt_4096": (["halo::fq_rows2_kernel<unsigned short, 256, 0, true>"], None),
+    "fq_cols_opt_4096": (["halo::fq_cols2_kernel<256, 0, true, false>"], None),
+    "copy_neg": (["neg_kernel"], None),  # 64 MiB calibration, or the 512 MiB copy reference
+    "fq_batch_4096": (["halo::fq_batch_kernel<256, 0, 0, false, false>"], None),
+    "gemm_i8_pair_4096": (["halo::gemm_kernel<0"], 2 * GEMM_GRID),
 }
+
+
+def pass_match(key, name, grid):
+    """Whether a dispatch of kernel `name` over `grid` work-items (None: not recorded) belongs
+    to pass `key`."""
+    pats, g = PASSES[key]
+    return any(p in name for p in pats) and (g is None or grid is None or grid == g)
 
 
 def code_text(src):
@@ -405,9 +417,23 @@ def measure_kernels(H, torch, sets, iters, with_copy=False):
         ev[-1][1].synchronize()
         return float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
+    # the layer backward, whose first launch runs its four rotation passes together (rows of
+    # dY; columns of W, dY and X): its kernels are told apart by name in the traces
+    dx = torch.empty((M, K), dtype=torch.bfloat16, device="cuda:0")
+    dw = torch.empty((N, K), dtype=torch.bfloat16, device="cuda:0")
+    wsb = torch.empty(H.linear_workspace_bytes(M, N, K, torch.int8, True, block=BLOCK),
+                      dtype=torch.uint8, device="cuda:0")
+    bwd = _c_launcher(H, "halo_linear_bwd_ex", [
+        (P(DY), P(X), P(W), code(X.dtype), M, N, K, BLOCK, code(torch.int8), code(torch.int8),
+         P(dx), P(dw), None, P(wsb), wsb.numel(), st) for (X, W, DY) in sets])
+
     legs = {"gemm_i8_4096": gemm, "gemm_fp8_4096": gemm_fp8, "fq_rows_4096": rows,
             "fq_cols_4096": cols, "fq_rows_opt_4096": rows_opt, "fq_cols_opt_4096": cols_opt,
-            "fq_rows_pad_4000": rows_pad}
+            "fq_rows_pad_4000": rows_pad, "linear_bwd_4096": bwd}
+    if with_copy:
+        # the padded rows pass shares the rows kernel and its grid: kept out of the counter
+        # runs, whose per-pass averages would mix its smaller reads in
+        del legs["fq_rows_pad_4000"]
     for f in legs.values():
         for i in range(3):
             f(i)
@@ -421,16 +447,22 @@ def measure_kernels(H, torch, sets, iters, with_copy=False):
             runs[k].append(time_events(f, iters, torch))
         runs["gemm_i8_4096_in_path"].append(gemm_in_path(iters))
     out = {k: float(np.median(v)) for k, v in runs.items()}
-    # the practical streaming rate of this HBM: torch's elementwise negation of 512 MiB into
-    # another 512 MiB (1 GiB moved per launch, two buffers cycled: nothing cache-resident)
-    big = [torch.empty(COPY_REF_BYTES // 4, dtype=torch.float32, device="cuda:0") for _ in range(4)]
-    for b_ in big:
-        b_.fill_(1.0)
-    def copy_ref(i):
-        torch.neg(big[(2 * i) % 4], out=big[(2 * i + 1) % 4])
-    copy_ref(0)
-    out["copy_ref_512MiB"] = float(np.median([time_events(copy_ref, 10, torch) for _ in range(3)]))
-    del big
+    if not with_copy:
+        # the practical streaming rate of this HBM: torch's elementwise negation of 512 MiB
+        # into another 512 MiB (1 GiB moved per launch, two pairs of buffers cycled: nothing
+        # cache-resident).  Left out of the counter runs, whose calibration kernel is the same
+        # negation on 64 MiB.
+        big = [torch.empty(COPY_REF_BYTES // 4, dtype=torch.float32, device="cuda:0")
+               for _ in range(4)]
+        for b_ in big:
+            b_.fill_(1.0)
+
+        def copy_ref(i):
+            torch.neg(big[(2 * i) % 4], out=big[(2 * i + 1) % 4])
+        copy_ref(0)
+        out["copy_ref_512MiB"] = float(np.median([time_events(copy_ref, 10, torch)
+                                                  for _ in range(3)]))
+        del big
     if with_copy:
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0").normal_()
         dst = torch.empty_like(src)
@@ -457,10 +489,11 @@ def summarize_stats(path, command, last=0):
         with open(trace) as f:
             tr = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
         lines += ["", f"per pass, last {last} calls (the event-timed measurement loop):"]
-        for key, pats in PASSES.items():
+        for key in PASSES:
             calls = {}
             for r in tr:
-                if any(p in r["Kernel_Name"] for p in pats):
+                grid = int(r["Grid_Size_X"]) if r.get("Grid_Size_X") else None
+                if pass_match(key, r["Kernel_Name"], grid):
                     d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
                     calls.setdefault(r["Kernel_Name"], []).append(d)
             if calls:
@@ -480,13 +513,15 @@ def _pmc_per_call(d, counter):
             for r in csv.DictReader(f):
                 if r["Counter_Name"] != counter:
                     continue
-                per_kernel.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+                grid = int(r["Grid_Size"]) if r.get("Grid_Size") else None
+                per_kernel.setdefault((r["Kernel_Name"], grid), []).append(
+                    float(r["Counter_Value"]))
     out = {}
-    for key, pats in PASSES.items():
+    for key in PASSES:
         tot = 0.0
         found = False
-        for name, vals in per_kernel.items():
-            if any(p in name for p in pats):
+        for (name, grid), vals in per_kernel.items():
+            if pass_match(key, name, grid):
                 tot += float(np.mean(vals))
                 found = True
         out[key] = tot if found else None
@@ -497,10 +532,11 @@ def summarize_pmc(fetch_dir, write_dir, command):
     fetch = _pmc_per_call(fetch_dir, "FETCH_SIZE")
     write = _pmc_per_call(write_dir, "WRITE_SIZE")
     # calibration: the elementwise negation of COPY_BYTES reads and writes exactly COPY_BYTES
-    f_scale = COPY_BYTES / (fetch["copy_64MiB"] * 1024.0)
-    w_scale = COPY_BYTES / (write["copy_64MiB"] * 1024.0)
+    f_scale = COPY_BYTES / (fetch["copy_neg"] * 1024.0)
+    w_scale = COPY_BYTES / (write["copy_neg"] * 1024.0)
     algo = {"gemm_i8_4096": GEMM_BYTES, "gemm_fp8_4096": GEMM_BYTES, "fq_rows_4096": FQ_BYTES,
-            "fq_cols_4096": FQ_BYTES, "fq_rows_opt_4096": FQ_BYTES, "fq_cols_opt_4096": FQ_BYTES}
+            "fq_cols_4096": FQ_BYTES, "fq_rows_opt_4096": FQ_BYTES, "fq_cols_opt_4096": FQ_BYTES,
+            "fq_batch_4096": 4 * FQ_BYTES, "gemm_i8_pair_4096": 2 * GEMM_BYTES}
     res = {"kernel_source_hash": source_hash(KERNEL_SOURCES), "command": command,
            "fetch_scale": f_scale, "write_scale": w_scale, "bytes_per_launch": {},
            "fetch_kib_raw": fetch, "write_kib_raw": write}
