@@ -18,7 +18,10 @@ are timed, and reported beside the result.
 Per-kernel figures are measured in the same run with HIP events on the launch stream: the
 INT8 GEMM (the dominant kernel, MFMA-bound) and the rows / columns rotation passes
 (HBM-bound), each cycling through more than 512 MB of distinct inputs so that no operand is
-served from the Infinity Cache.  The CPU baseline times the oracle on full steps of the same
+served from the Infinity Cache.  Beside the products, the library's matrix-core rate probe
+measures what each product's MFMA instruction alone sustains on the whole device (with the
+clock it runs at): the published peak assumes a 2.4 GHz clock the chip does not hold under a
+sustained matrix load.  The CPU baseline times the oracle on full steps of the same
 layer on all host threads, a one-thread sample of it, and each pass's oracle / GPU ratio.
 
 Other modes:
@@ -472,6 +475,36 @@ def measure_kernels(H, torch, sets, iters, with_copy=False):
     return out
 
 
+def measure_mfma_sustained(H, torch, seconds=0.4):
+    """Sustained whole-device rate (TOP/s) of each matrix-core instruction the products use,
+    from the library's rate probe: launches back to back for about `seconds` after a short
+    warm-up, HIP events on the stream, the shader clock and board power sampled meanwhile."""
+    st = torch.cuda.current_stream()
+    out = {}
+    for kind, name in H.MFMA_PROBE_KINDS.items():
+        iters = 2000
+        H.mfma_rate_probe(kind, iters, st)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.1:  # warm-up, and the launch count for `seconds`
+            H.mfma_rate_probe(kind, iters, st)
+            torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        H.mfma_rate_probe(kind, iters, st)
+        torch.cuda.synchronize()
+        n = max(10, int(seconds / max(time.perf_counter() - t0, 1e-4)))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with ClockSampler() as clk:
+            e0.record(st)
+            ops = sum(H.mfma_rate_probe(kind, iters, st) for _ in range(n))
+            e1.record(st)
+            e1.synchronize()
+        ms = e0.elapsed_time(e1)
+        out[name] = {"tops": round(ops / (ms * 1e-3) / 1e12, 1), "launches": n,
+                     "ms": round(ms, 2), "clock": clk.summary()}
+    return out
+
+
 def summarize_stats(path, command, last=0):
     """rocprofv3 kernel_stats.csv -> text table (per-kernel average duration).  With `last`,
     the kernel_trace.csv beside it also gives each pass's average over its last `last`
@@ -778,6 +811,9 @@ def main():
     with ClockSampler() as clk_k:
         t = measure_kernels(H, torch, sets, args.kernel_iters)
     t_large = measure_large_passes(H, torch, max(5, args.kernel_iters // 6))
+    mfma = measure_mfma_sustained(H, torch)
+    i8_sustained = mfma[H.MFMA_PROBE_KINDS[0]]["tops"]
+    fp8_sustained = mfma[H.MFMA_PROBE_KINDS[1]]["tops"]
     t_gemm, t_rows, t_cols = t["gemm_i8_4096"], t["fq_rows_4096"], t["fq_cols_4096"]
     t_gemm_path = t["gemm_i8_4096_in_path"]
     gemm_tops = GEMM_OPS / (t_gemm * 1e-3) / 1e12
@@ -825,6 +861,13 @@ def main():
                      "ms_per_launch": round(t_gemm, 5), "algorithmic_ops": GEMM_OPS,
                      "measured": "back-to-back launches cycling 18 pairs of 16 MiB code "
                                  "matrices (604 MB), none left in the Infinity Cache",
+                     "instruction_sustained": {
+                         "achieved": i8_sustained, "unit": "TFLOP/s",
+                         "frac": round(gemm_tops / i8_sustained, 4),
+                         "what": "v_mfma_i32_32x32x32_i8 alone on the whole device under a "
+                                 "sustained load (halo_mfma_rate_probe): the rate the chip's "
+                                 "clock allows this instruction; frac = the product's rate "
+                                 "over it"},
                      "in_path": {"ms_per_launch": round(t_gemm_path, 5),
                                  "frac": round(GEMM_OPS / (t_gemm_path * 1e-3) / 1e12
                                                / PEAK_INT8_TOPS, 4),
@@ -844,7 +887,13 @@ def main():
                      "frac": round(GEMM_OPS / (t["gemm_fp8_4096"] * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
                      "traffic": load_traffic("gemm_fp8_4096"),
                      "kernel": "gemm_kernel<FP8 E4M3 x E4M3, bf16 out> 4096x4096x4096",
-                     "ms_per_launch": round(t["gemm_fp8_4096"], 5), "algorithmic_ops": GEMM_OPS},
+                     "ms_per_launch": round(t["gemm_fp8_4096"], 5), "algorithmic_ops": GEMM_OPS,
+                     "instruction_sustained": {
+                         "achieved": fp8_sustained, "unit": "TFLOP/s",
+                         "frac": round(GEMM_OPS / (t["gemm_fp8_4096"] * 1e-3) / 1e12
+                                       / fp8_sustained, 4),
+                         "what": "v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3) alone, as above"}},
+        "mfma_sustained": mfma,
         "options": {
             "step": {"ms": round(ms_opt, 4),
                      "effective_tops": round(STEP_GOP / (ms_opt * 1e-3) / 1e3, 3),

@@ -32,7 +32,7 @@ EXPORTS = ("halo_fwht_quant", "halo_fwht_quant_ex", "halo_fwht_quant_noalloc",
            "halo_fwht_quant_workspace_bytes",
            "halo_gemm_i8", "halo_gemm_fp8", "halo_linear_workspace_bytes",
            "halo_linear_workspace_bytes_ex", "halo_linear_fwd", "halo_linear_fwd_ex",
-           "halo_linear_bwd", "halo_linear_bwd_ex", "halo_status_str")
+           "halo_linear_bwd", "halo_linear_bwd_ex", "halo_mfma_rate_probe", "halo_status_str")
 
 
 class QuantOpts(ctypes.Structure):
@@ -91,12 +91,13 @@ def lib():
         L.halo_linear_fwd_ex.argtypes = [vp, vp, e, i64, i64, i64, i32, e, vp, e, lo, vp, sz, vp]
         L.halo_linear_bwd_ex.argtypes = [vp, vp, vp, e, i64, i64, i64, i32, e, e, vp, vp, lo, vp,
                                          sz, vp]
+        L.halo_mfma_rate_probe.argtypes = [i32, i32, ctypes.POINTER(ctypes.c_int64), vp]
         L.halo_status_str.argtypes = [e]
         L.halo_status_str.restype = ctypes.c_char_p
         for f in ("halo_fwht_quant", "halo_fwht_quant_ex", "halo_fwht_quant_noalloc",
                   "halo_gemm_i8", "halo_gemm_fp8",
                   "halo_linear_fwd", "halo_linear_fwd_ex", "halo_linear_bwd",
-                  "halo_linear_bwd_ex"):
+                  "halo_linear_bwd_ex", "halo_mfma_rate_probe"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -221,6 +222,19 @@ def fwht_quant(x, axis=ROWS, block=256, q_dtype=torch.int8, q=None, scale=None, 
                                   ws_bytes, _stream(stream))
     _check(st, "halo_fwht_quant_ex")
     return q, scale
+
+
+MFMA_PROBE_KINDS = {0: "v_mfma_i32_32x32x32_i8", 1: "v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3)",
+                    2: "v_mfma_scale_f32_16x16x128_f8f6f4 (E4M3)"}
+
+
+def mfma_rate_probe(kind, iters, stream=None):
+    """One launch of the matrix-core rate probe (halo_mfma_rate_probe) on `stream`; returns the
+    operations it performs.  A measurement aid: time it with events on the same stream."""
+    ops = ctypes.c_int64(0)
+    _check(lib().halo_mfma_rate_probe(int(kind), int(iters), ctypes.byref(ops), _stream(stream)),
+           "halo_mfma_rate_probe")
+    return ops.value
 
 
 def fwht_quant_noalloc(x, q, scale, axis=ROWS, block=256, stream=None, signs=None,

@@ -291,6 +291,15 @@ bool layer_dims_ok(int64_t m, int64_t n, int64_t k) {
 
 extern "C" {
 
+halo_status halo_mfma_rate_probe(int32_t kind, int32_t iters, int64_t* ops, void* stream) {
+  if (!ops) return HALO_ERR_NULL;
+  if (kind < 0 || kind > 2 || iters < 2 || iters > (1 << 20)) return HALO_ERR_SHAPE;
+  const hipError_t e = launch_mfma_probe(kind, iters, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return HALO_ERR_HIP;
+  *ops = mfma_probe_ops(kind, iters);
+  return HALO_OK;
+}
+
 const char* halo_status_str(halo_status s) {
   if (!enum_in(s, HALO_OK, HALO_ERR_OPTION)) return "unknown status";
   switch (s) {

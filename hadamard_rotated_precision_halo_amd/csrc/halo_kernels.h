@@ -97,6 +97,11 @@ hipError_t launch_gemm(const GemmArgs& g, int kind, int afmt, int bfmt, int out,
 hipError_t launch_gemm_pair(const GemmArgs& g, const GemmArgs* g1, int kind, int afmt, int bfmt,
                             int out, hipStream_t st);
 
+// Matrix-core rate probe (mfma_probe.hip): kind 0 INT8 32x32x32, 1 FP8 32x32x64, 2 FP8
+// 16x16x128; mfma_probe_ops gives the operations one launch performs.
+hipError_t launch_mfma_probe(int kind, int iters, hipStream_t st);
+int64_t mfma_probe_ops(int kind, int iters);
+
 // Let `Kernel` launch with `bytes` of dynamic LDS on the current device.  The attribute belongs
 // to one kernel on one device, so it is set once per kernel and device (concurrent first calls
 // may both set it); a failure is returned, and tried again on the next call.

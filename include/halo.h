@@ -313,6 +313,23 @@ halo_status halo_fwht_quant_noalloc(const void* x, halo_dtype x_type, int64_t ro
                                     halo_dtype q_type, void* q, int64_t ldq, float* scale,
                                     const halo_quant_opts* opts, void* stream);
 
+/*
+ * Measurement aid, not part of the layer: the sustained rate of the matrix-core instruction a
+ * product uses, on the whole device, to set the products' measured rates beside what the
+ * instruction alone reaches under a sustained load (the published dense peaks assume the
+ * 2.4 GHz engine clock).
+ *   kind   0: v_mfma_i32_32x32x32_i8 (the INT8 product's), 1: v_mfma_scale_f32_32x32x64_f8f6f4
+ *          on E4M3 operands (the FP8 product's), 2: v_mfma_scale_f32_16x16x128_f8f6f4 on E4M3
+ *          operands.
+ *   iters  MFMA groups per wave, in [2, 1 << 20] (rounded up to even); one group is 8
+ *          independent MFMAs (16 for kind 2), on operands that change every group.
+ *   ops    receives the operations (2 x multiply-adds) the launch performs.
+ * One launch of 256 workgroups of 512 threads (two waves per SIMD, as the products run) on
+ * the stream; it reads and writes no caller memory.  Time it with events on that stream.
+ * HALO_ERR_SHAPE for kind or iters out of range, HALO_ERR_NULL for ops NULL.
+ */
+halo_status halo_mfma_rate_probe(int32_t kind, int32_t iters, int64_t* ops, void* stream);
+
 /* Static description of a status code. */
 const char* halo_status_str(halo_status s);
 

@@ -267,3 +267,11 @@ def test_linear_ex_validation(L):
     assert b(lopts(sm=BAD.value)) == ALIGN
     assert L.halo_linear_bwd_ex(P, P2, P3, BF16, m, n, k, 128, I8, I8, P, P2,
                                 ctypes.byref(lopts()), P3, wsb - 256, None) == WORKSPACE
+
+
+def test_mfma_rate_probe_validation(L):
+    ops = ctypes.c_int64(-1)
+    assert L.halo_mfma_rate_probe(0, 100, None, None) == NULL
+    for kind, iters in ((-1, 100), (3, 100), (0, 1), (0, 0), (1, (1 << 20) + 1)):
+        assert L.halo_mfma_rate_probe(kind, iters, ctypes.byref(ops), None) == SHAPE
+    assert ops.value == -1  # refused before anything is written or launched
