@@ -46,7 +46,7 @@ def code_distance(a, b, qtype):
 
 
 def assert_codes_close_to_fp64(gpu_q, ref_q, qtype, block, frac=1e-4):
-    """North-star code bar against the fp64 oracle: |dq| <= 1 everywhere and at most
+    """Code bar against the fp64 oracle: |dq| <= 1 everywhere and at most
     `frac` of the elements off by one (grid steps for FP8).  The fraction applies to rotated
     data (block >= 16); with block < 16 a bf16 input keeps its 8-bit mantissa, so values
     y * qmax / a that are exact ties in real arithmetic are common and the fp32 and fp64
@@ -71,7 +71,7 @@ def scales_close_to_fp64(gpu_s, ref_s, rtol=1e-5):
 
 def check_fq_parity(got_q, got_s, x, oaxis, block, qtype, vec_idx=None, **opts):
     """Both bars of a rotation pass against the oracle: codes and scales bit-exact to its
-    fp32 decision, and within the spec bar of its plain fp64 definition (|dq| <= 1 on
+    fp32 decision, and within the code bar of its plain fp64 definition (|dq| <= 1 on
     at most 1e-4 of the codes, scales within 1e-5 relative).  opts: the oracle's signs /
     rounding / key / ctr_hi."""
     got_s = np.asarray(got_s, dtype=np.float64)

@@ -2,7 +2,7 @@
 the benchmark times (halo_linear_fwd / halo_linear_bwd, halo_fwht_quant with its scratch,
 halo_gemm_i8 / halo_gemm_fp8).
 
-Bars (the spec levels):
+Bars:
   * layer outputs Y, dX, dW: relative Frobenius error <= 1e-2 against the oracle's fp64 path,
     and elementwise within one output rounding of its fp32-decision path (whose codes are the
     GPU's), plus the FP8 matrix cores' accumulation bound for FP8;

@@ -1,7 +1,6 @@
 """GPU parity of the layer entry points halo_linear_fwd / halo_linear_bwd against the oracle.
 
-Bars: relative Frobenius error <= 1e-2 against the oracle's fp64 quantised path (the
-spec bar); against the oracle's fp32-decision path the codes are identical, so the only
+Bars: relative Frobenius error <= 1e-2 against the oracle's fp64 quantised path; against the oracle's fp32-decision path the codes are identical, so the only
 difference left is the output rounding (bf16: 2^-8 relative per element, with slack for the
 fp32 epilogue).  Workloads are the synth layer tensors (outlier channels, Student-t grads).
 """
