@@ -30,6 +30,8 @@ Other modes:
   --summarize-stats F   turn a rocprofv3 --stats kernel_stats.csv into a text summary.
   --summarize-pmc D1 D2 turn two rocprofv3 --pmc runs of --kernels-only (FETCH_SIZE in D1,
                         WRITE_SIZE in D2) into the per-launch HBM traffic of each kernel.
+  --summarize-counters D...  any rocprofv3 --pmc runs of --kernels-only: each counter's mean
+                        per call of each pass, and the products' matrix-core figures.
 """
 import argparse
 import csv
@@ -535,6 +537,64 @@ def summarize_stats(path, command, last=0):
     return "\n".join(lines) + "\n"
 
 
+def _counter_means(d):
+    """{pass: {counter: mean value per call}} from the counter_collection.csv files under d
+    (each pass's kernels summed, each kernel averaged over its dispatches)."""
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    per = {}
+    for fn in files:
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                grid = int(r["Grid_Size"]) if r.get("Grid_Size") else None
+                per.setdefault((r["Kernel_Name"], grid, r["Counter_Name"]), []).append(
+                    float(r["Counter_Value"]))
+    out = {}
+    for key in PASSES:
+        for (name, grid, counter), vals in per.items():
+            if pass_match(key, name, grid):
+                c = out.setdefault(key, {})
+                c[counter] = c.get(counter, 0.0) + float(np.mean(vals))
+    return out
+
+
+def summarize_counters(dirs, commands):
+    """Text summary of rocprofv3 --pmc runs of --kernels-only (one directory per counter
+    pass): each counter's mean per call of each pass, and for the products the matrix-core
+    figures derived from them."""
+    merged = {}
+    for d in dirs:
+        for key, cs in _counter_means(d).items():
+            merged.setdefault(key, {}).update(cs)
+    lines = [f"command (pass {i + 1}): {c}" for i, c in enumerate(commands)]
+    lines += ["", "Average counter value per call (all XCDs summed):"]
+    for key in PASSES:
+        if key not in merged or key == "copy_neg":
+            continue
+        lines.append(f"  {key}")
+        for counter in sorted(merged[key]):
+            lines.append(f"    {counter:<32} {merged[key][counter]:>12.4g}")
+    for key, mops in (("gemm_i8_4096", "SQ_INSTS_VALU_MFMA_MOPS_I8"),
+                      ("gemm_fp8_4096", "SQ_INSTS_VALU_MFMA_MOPS_F8")):
+        c = merged.get(key, {})
+        lines += ["", f"Derived for {key}:"]
+        if mops in c:
+            lines.append(f"  MFMA ops = {mops} x 512 = {c[mops] * 512 / 1e9:.1f} G "
+                         f"(2 x 4096^3 = {GEMM_OPS / 1e9:.1f} G)")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in c and "GRBM_GUI_ACTIVE" in c:
+            per_xcd = c["GRBM_GUI_ACTIVE"] / 8
+            lines.append(f"  GRBM_GUI_ACTIVE / 8 XCDs = {per_xcd:.0f} cycles per call")
+            lines.append(f"  MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x that) = "
+                         f"{100 * c['SQ_VALU_MFMA_BUSY_CYCLES'] / (1024 * per_xcd):.1f} %")
+        if "SQ_WAIT_INST_ANY" in c and "SQ_WAVE_CYCLES" in c:
+            lines.append(f"  SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES = "
+                         f"{100 * c['SQ_WAIT_INST_ANY'] / c['SQ_WAVE_CYCLES']:.1f} %")
+        if "SQ_LDS_BANK_CONFLICT" in c:
+            lines.append(f"  LDS bank conflicts: {c['SQ_LDS_BANK_CONFLICT']:.0f}")
+    return "\n".join(lines) + "\n"
+
+
 def _pmc_per_call(d, counter):
     """Average counter value (KiB) per call of each pass, from a counter_collection.csv."""
     files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
@@ -691,6 +751,10 @@ def main():
     ap.add_argument("--kernels-only", action="store_true")
     ap.add_argument("--summarize-stats", metavar="CSV")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
+                    help="rocprofv3 --pmc output directories, one per counter pass")
+    ap.add_argument("--commands", nargs="+", default=[],
+                    help="the profiling command of each --summarize-counters pass")
     ap.add_argument("--command", default="", help="profiling command recorded in a summary")
     ap.add_argument("--out", help="summary file to write")
     ap.add_argument("--last", type=int, default=0, help="trace calls per pass to average")
@@ -706,6 +770,13 @@ def main():
 
     if args.summarize_stats:
         text = summarize_stats(args.summarize_stats, args.command, args.last)
+        if args.out:
+            with open(args.out, "w") as f:
+                f.write(text)
+        print(text, end="")
+        return
+    if args.summarize_counters:
+        text = summarize_counters(args.summarize_counters, args.commands)
         if args.out:
             with open(args.out, "w") as f:
                 f.write(text)

@@ -94,3 +94,27 @@ def test_algorithmic_bytes():
     assert bench.LARGE_BYTES == 16384 * 14336 * 3 + 4 * 16384
     assert bench.GEMM_BYTES == 2 * 4096 * 4096 + 2 * 4096 * 4096 + 4 * 8192
     assert np.isclose(bench.STEP_GOP, 3 * 2 * 4096 ** 3 / 1e9)
+
+
+def test_summarize_counters_means_and_derived(tmp_path):
+    gemm = "void halo::gemm_kernel<0, 0, 0, 2, false, 128, 4>(halo::GemmPair)"
+    d = tmp_path / "a"
+    os.makedirs(d)
+    with open(d / "p_counter_collection.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Grid_Size", "Counter_Name",
+                                          "Counter_Value"])
+        w.writeheader()
+        for v in (100.0, 300.0):  # two calls of the single product
+            w.writerow(dict(Kernel_Name=gemm, Grid_Size=bench.GEMM_GRID,
+                            Counter_Name="SQ_VALU_MFMA_BUSY_CYCLES", Counter_Value=v * 1024))
+            w.writerow(dict(Kernel_Name=gemm, Grid_Size=bench.GEMM_GRID,
+                            Counter_Name="GRBM_GUI_ACTIVE", Counter_Value=8 * 400.0))
+        # the paired products (twice the grid) must not mix in
+        w.writerow(dict(Kernel_Name=gemm, Grid_Size=2 * bench.GEMM_GRID,
+                        Counter_Name="SQ_VALU_MFMA_BUSY_CYCLES", Counter_Value=9e9))
+    text = bench.summarize_counters([str(d)], ["cmd a"])
+    assert text.startswith("command (pass 1): cmd a")
+    assert "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x that) = 50.0 %" in text
+    means = bench._counter_means(str(d))
+    assert means["gemm_i8_4096"]["SQ_VALU_MFMA_BUSY_CYCLES"] == pytest.approx(200.0 * 1024)
+    assert means["gemm_i8_pair_4096"]["SQ_VALU_MFMA_BUSY_CYCLES"] == pytest.approx(9e9)
