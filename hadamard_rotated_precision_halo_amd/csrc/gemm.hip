@@ -456,8 +456,15 @@ static hipError_t launch_t(const GemmArgs& g, const GemmArgs* g1, hipStream_t st
               : launch_cfg<KIND, AF, BF, OUT, false, BK>(g, g1, st);
 }
 
-hipError_t launch_gemm_pair(const GemmArgs& g, const GemmArgs* g1, int kind, int afmt, int bfmt,
-                            int out, hipStream_t st) {
+hipError_t launch_gemm_pair(const GemmArgs& g_in, const GemmArgs* g1_in, int kind, int afmt,
+                            int bfmt, int out, hipStream_t st) {
+  // The product with the longer contraction takes the first workgroups: its tiles run longer,
+  // and dispatching the longer tasks first leaves a shorter tail when the two products' tiles
+  // do not divide evenly over the compute units (each workgroup's outputs are its own, so the
+  // order changes no result).
+  const bool swap = g1_in && g1_in->k > g_in.k;
+  const GemmArgs& g = swap ? *g1_in : g_in;
+  const GemmArgs* g1 = swap ? &g_in : g1_in;
   if (kind == 0) {
     switch (out) {
       case 0: return launch_t<0, 0, 0, 0>(g, g1, st);
