@@ -97,6 +97,14 @@ halo_status check_signs(const uint32_t* signs) {
   return signs && !aligned16(signs) ? HALO_ERR_ALIGN : HALO_OK;
 }
 
+// Whether a rows pass over vectors of Lp rotated positions has a kernel: the wave kernel
+// (Lp a multiple of 64, one wave per 4096 positions and up to 16 per row; its stochastic
+// rounding takes bf16 input), else the older kernel, whose workgroup holds a whole row of up
+// to fq_rows_max_len(block) positions.
+bool rows_len_ok(int64_t Lp, int32_t block, bool in_bf16, bool sr) {
+  return (fq_rows2_supported(Lp, block) && (in_bf16 || !sr)) || Lp <= fq_rows_max_len(block);
+}
+
 // Validation of one rotation pass; shared by halo_fwht_quant and the layer calls.
 halo_status check_fq(const void* x, halo_dtype xt, int64_t rows, int64_t cols, int64_t ldx,
                      halo_axis axis, int32_t block, halo_dtype qt, const void* q, int64_t ldq,
@@ -118,7 +126,9 @@ halo_status check_fq(const void* x, halo_dtype xt, int64_t rows, int64_t cols, i
   if (Lp % 8 != 0) return HALO_ERR_SHAPE;
   if (axis == HALO_ALONG_ROWS && L % 8 != 0) return HALO_ERR_SHAPE;
   if (axis == HALO_ALONG_COLS && nvec % 8 != 0) return HALO_ERR_SHAPE;
-  if (axis == HALO_ALONG_ROWS && Lp > fq_rows_max_len(block)) return HALO_ERR_SHAPE;
+  const bool sr = o && o->rounding == HALO_ROUND_STOCHASTIC;
+  if (axis == HALO_ALONG_ROWS && !rows_len_ok(Lp, block, xt == HALO_BF16, sr))
+    return HALO_ERR_SHAPE;
   if (o) {
     if (o->rounding != HALO_ROUND_NEAREST_EVEN && o->rounding != HALO_ROUND_STOCHASTIC)
       return HALO_ERR_OPTION;
@@ -424,7 +434,7 @@ halo_status halo_linear_fwd_ex(const void* x, const void* w, halo_dtype io_type,
   if (y_type != HALO_F32 && y_type != HALO_BF16) return HALO_ERR_DTYPE;
   if (!valid_block(block)) return HALO_ERR_BLOCK;
   const int64_t kq = contraction_len(k, block);
-  if (k % 8 != 0 || kq > fq_rows_max_len(block)) return HALO_ERR_SHAPE;
+  if (k % 8 != 0 || !rows_len_ok(kq, block, io_type == HALO_BF16, false)) return HALO_ERR_SHAPE;
   if (!operand_fits(m, kq, kq) || !operand_fits(n, kq, kq)) return HALO_ERR_SHAPE;
   if (opts && (opts->grad_rounding != HALO_ROUND_NEAREST_EVEN &&
                opts->grad_rounding != HALO_ROUND_STOCHASTIC))
@@ -488,7 +498,8 @@ halo_status halo_linear_bwd_ex(const void* dy, const void* x, const void* w, hal
   if (!valid_block(block)) return HALO_ERR_BLOCK;
   const int64_t nq = contraction_len(n, block), mq = contraction_len(m, block);
   if (n % 8 != 0 || k % 8 != 0) return HALO_ERR_SHAPE;
-  if (dx && nq > fq_rows_max_len(block)) return HALO_ERR_SHAPE;
+  const bool sr_dy = opts && opts->grad_rounding == HALO_ROUND_STOCHASTIC;
+  if (dx && !rows_len_ok(nq, block, io_type == HALO_BF16, sr_dy)) return HALO_ERR_SHAPE;
   if (!operand_fits(m, nq, nq) || !operand_fits(k, nq, nq) || !operand_fits(n, mq, mq) ||
       !operand_fits(k, mq, mq))
     return HALO_ERR_SHAPE;

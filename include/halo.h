@@ -113,7 +113,8 @@ typedef enum {
  *            stream.  After such a pass completes, the first 32-bit word of ws holds the
  *            number of workgroups that stopped waiting for the exchange (a diagnostic; the
  *            results do not depend on it).
- * Rows-axis vectors are limited to Lp <= 16384 elements (one workgroup holds a whole row).
+ * Rows-axis vectors: Lp up to 65536 when Lp is a multiple of 64 (one workgroup of Lp / 4096
+ * waves holds a row; for stochastic rounding the input must then be bf16), else up to 16384.
  * Codes are decided in fp32: m = qmax / max|b| with b the un-normalised butterfly output and
  * code = round(b * m); the 1/sqrt(block) factor cancels between b and max|b|.
  */
@@ -179,8 +180,9 @@ size_t halo_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, halo_dtype q
  * k must be a multiple of 8 and n a multiple of 16 bytes of y_type; block as for
  * halo_fwht_quant.  When block does not divide k, X and W are padded with zeros along k (QWHA
  * page s5) and the product runs over all padded positions, which equals the product of the
- * padded operands.  The padded k (rounded up to a multiple of block and of 32) is at most 16384,
- * and each code matrix (m or n rows of the padded k) spans less than 4 GiB.
+ * padded operands.  The padded k (rounded up to a multiple of block and of 32) is a rows-axis
+ * length as in halo_fwht_quant (up to 65536 when a multiple of 64, else 16384), and each code
+ * matrix (m or n rows of the padded k) spans less than 4 GiB.
  */
 halo_status halo_linear_fwd(const void* x, const void* w, halo_dtype io_type, int64_t m,
                             int64_t n, int64_t k, int32_t block, halo_dtype q_type, void* y,
@@ -199,8 +201,9 @@ halo_status halo_linear_fwd(const void* x, const void* w, halo_dtype io_type, in
  *   dx, dw       outputs; either may be NULL to skip that product.
  *   ws           at least halo_linear_workspace_bytes(m, n, k, q_type, 1) bytes.
  * n and k must be multiples of 8, m >= 1; block as for halo_fwht_quant.  Contraction
- * dimensions that block does not divide are zero-padded as in halo_linear_fwd; the padded n
- * is at most 16384 when dx is computed, and each code matrix spans less than 4 GiB.
+ * dimensions that block does not divide are zero-padded as in halo_linear_fwd; when dx is
+ * computed the padded n is a rows-axis length as in halo_fwht_quant (with stochastic rounding
+ * of fp32 dY: at most 16384), and each code matrix spans less than 4 GiB.
  * With INT8 codes, dW's int32 sums run over the padded m: exact while every partial sum
  * stays within int32, which |codes| <= 127 guarantee up to 133144 terms (as halo_gemm_i8).
  */

@@ -87,6 +87,14 @@ def test_fwht_quant_validation(L):
     assert fq(L, axis=1, block=16, rows=64, cols=12, ldx=16, ldq=64) == SHAPE  # 12 columns
     big = 1 << 20
     assert fq(L, cols=big, ldx=big, ldq=big, block=256) == SHAPE     # beyond the rows kernel
+    # rows of up to 65536 positions when a multiple of 64 (the wave kernel: a misaligned x
+    # is the first error a call past the shape checks meets); else up to 16384
+    w64 = 1 << 16
+    assert fq(L, x=BAD, cols=w64, ldx=w64, ldq=w64) == ALIGN
+    assert fq(L, x=BAD, cols=w64 + 256, ldx=w64 + 256, ldq=w64 + 256) == SHAPE
+    assert fq(L, x=BAD, xt=F32, cols=28672, ldx=28672, ldq=28672) == ALIGN
+    assert fq(L, x=BAD, block=32, cols=20000, ldx=20000, ldq=20000) == SHAPE   # not k * 64
+    assert fq(L, x=BAD, block=32, cols=16352, ldx=16352, ldq=16352) == ALIGN   # older kernel
     assert fq(L, x=BAD) == ALIGN
     assert fq(L, q=BAD) == ALIGN
     assert fq(L, ldx=260, cols=256) == ALIGN  # 520 bytes per bf16 row
@@ -112,6 +120,9 @@ def test_fwht_quant_ex_validation(L):
     assert fqx(L, opts(signs=BAD.value)) == ALIGN
     assert fqx(L, opts(), x=NUL) == NULL                           # the plain checks still run
     assert fqx(L, opts(rounding=1), block=3) == BLOCK
+    # stochastic rounding of long fp32 rows: only the older kernel, up to 16384 positions
+    assert fqx(L, opts(rounding=1), x=BAD, xt=F32, cols=20480, ldx=20480, ldq=20480) == SHAPE
+    assert fqx(L, opts(rounding=1), x=BAD, cols=20480, ldx=20480, ldq=20480) == ALIGN
 
 
 def test_fwht_quant_workspace_bytes(L):
@@ -219,7 +230,9 @@ def test_linear_fwd_validation(L):
     assert fwd(L, qt=E5M2) == DTYPE
     assert fwd(L, yt=I32) == DTYPE
     assert fwd(L, k=244) == SHAPE              # not a multiple of 8
-    assert fwd(L, k=20000) == SHAPE            # padded k beyond the rows kernel
+    assert fwd(L, k=70000) == SHAPE            # padded k beyond the rows kernels
+    assert fwd(L, k=20000, block=32) == SHAPE  # padded k 20000: not k * 64, over 16384
+    assert fwd(L, k=20000, y=BAD) == ALIGN     # padded to 20096 = 314 * 64: the wave kernel
     assert fwd(L, m=(1 << 20) + 1, k=4096, wsb=1 << 40) == SHAPE  # X codes span over 4 GiB
     assert fwd(L, block=6) == BLOCK
     assert fwd(L, ws=NUL) == WORKSPACE
@@ -240,6 +253,8 @@ def test_linear_bwd_validation(L):
     assert bwd(L, qt=E4M3, gqt=I8) == DTYPE
     assert bwd(L, qt=E5M2, gqt=E5M2) == DTYPE
     assert bwd(L, n=244) == SHAPE              # not a multiple of 8
+    assert bwd(L, n=70000) == SHAPE            # the dY rows beyond the rows kernels
+    assert bwd(L, n=28672, dx=BAD) == ALIGN    # a 28672-wide layer's dX: the wave kernel
     assert bwd(L, k=244) == SHAPE
     assert bwd(L, m=0) == SHAPE
     assert bwd(L, block=6) == BLOCK

@@ -60,6 +60,10 @@ ROW_CASES = [
     ("f32", 128, 13, 512, O.E4M3),         # eight rows per wave, a partial last wave
     ("bf16", 64, 50, 64, O.I8),            # one lane per row
     ("f32", 4096, 3, 12288, O.E5M2),       # three waves per row
+    ("bf16", 256, 3, 28672, O.I8),         # seven waves per row (the dY rows of a wide layer)
+    ("bf16", 4096, 2, 65536, O.E5M2),      # sixteen waves: the longest row
+    ("f32", 512, 2, 20480, O.I8),          # fp32, five waves per row
+    ("bf16", 128, 2, 16448, O.E4M3),       # padded to 16512: a partial last wave
 ]
 
 

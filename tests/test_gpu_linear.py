@@ -30,6 +30,8 @@ FWD = [  # m, n, k, block, io, q
     (256, 512, 4096, 512, synth.BF16, "e4m3"),
     (64, 64, 512, 1, synth.BF16, "i8"),           # block 1: no rotation
     (0, 256, 256, 256, synth.BF16, "i8"),         # no tokens
+    (64, 96, 20000, 128, synth.BF16, "i8"),       # k padded to 20096: five waves per row
+    (32, 64, 28672, 256, synth.F32, "e4m3"),      # fp32 rows of 28672: seven waves per row
 ]
 
 
@@ -62,6 +64,7 @@ BWD = [  # m, n, k, block, io, q, gq
     (512, 512, 256, 256, synth.BF16, "e4m3", "e4m3"),
     (2048, 2048, 256, 256, synth.BF16, "i8", "i8"),    # every column pass split over 2 tasks
     (2048, 512, 256, 512, synth.BF16, "e4m3", "e5m2"),  # split dY / X passes, separate launches
+    (64, 28672, 64, 256, synth.BF16, "i8", "i8"),      # dY rows of 28672 (dX of a wide layer)
 ]
 
 

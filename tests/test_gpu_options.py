@@ -46,6 +46,8 @@ ROT_CASES = [
     ("rows", "f32", 256, 9, 1000, "i8", True, True, None),         # fp32: older rows kernel
     ("rows", "bf16", 16, 33, 1000, "i8", True, True, None),        # padded 1008: older kernel
     ("rows", "f32", 1024, 4, 3000, "e5m2", True, True, None),      # padded 3072: older kernel
+    ("rows", "bf16", 256, 3, 20480, "e5m2", True, True, None),     # five waves per row
+    ("rows", "f32", 512, 2, 16384, "i8", True, True, None),        # fp32 SR: older kernel, longest
     ("cols", "bf16", 256, 4096, 64, "i8", True, True, None),       # 4 parts per column
     ("cols", "bf16", 128, 1000, 200, "i8", True, True, None),      # padded 1000 -> 1024, 1 part
     ("cols", "bf16", 128, 5000, 72, "e5m2", True, True, None),     # padded 5120, 5 parts
@@ -157,6 +159,7 @@ BWD = [  # m, n, k, block, io, q, gq, signs, sr
     (2048, 2048, 256, 256, synth.BF16, "i8", "i8", True, True),    # column passes in 2 parts
     (256, 200, 64, 64, synth.F32, "i8", "i8", True, True),         # fp32: older kernels
     (96, 5000, 64, 4096, synth.BF16, "i8", "i8", True, True),      # n padded to 8192: long rows
+    (64, 20480, 64, 256, synth.BF16, "i8", "i8", True, True),      # dY rows of 20480
 ]
 
 
