@@ -33,9 +33,10 @@
 // counter, and waits until all P have arrived.  The tasks of a group of up to 8 strips are
 // consecutive workgroups, the parts of each strip 8 apart (one XCD), so the parts of a strip
 // normally run side by side and the input is read once and the codes written once.  No
-// result depends on that: the wait is bounded, and a task that reaches the bound computes
-// its strip's maxima itself from the input (see cols_task), so every call ends with the
-// same codes whatever else occupies the device.
+// result depends on that: the wait is bounded, a task that reaches the bound marks its strip
+// late and stops without storing, and the repair launch that follows on the stream stores
+// every part of a late strip from the then complete maxima (see cols_task), so every call
+// ends with the same codes whatever else occupies the device.
 //
 // Options (every kernel here): the randomised transform's signs ("企业官网建设流程全解析" s4.2,
 // one bit per element, applied before the butterflies), zero padding of vectors whose length
@@ -461,7 +462,7 @@ struct ColsProb {
   FqArgs a;
   float* colmax;
   uint32_t* arrive;
-  uint32_t* late;  // count of tasks that computed their strip's maxima themselves
+  uint32_t* late;  // count of tasks that stopped waiting (their strips go to the repair)
   int R, P, C;
   int gs;          // strips per task group (see cols_task), 1 or 8
   uint32_t spins;  // polls of a waiting task before it stops waiting (see cols_task)
@@ -773,8 +774,8 @@ static int cols2_capacity(const void* fn) {
 // the launchers below, with groups in place of strips); else 1.
 static int cols2_group(int P, int capacity) { return P > 1 && 8 * P <= capacity ? 8 : 1; }
 
-// Scratch layout of one pass: the count of tasks that computed their strip's maxima
-// themselves (one word, padded to 256 bytes), the arrival counters (padded to 256 bytes),
+// Scratch layout of one pass: the count of tasks that stopped waiting for the other parts of
+// their strip (one word, padded to 256 bytes), the arrival counters (padded to 256 bytes),
 // then the column maxima.
 constexpr size_t kColsLateBytes = 256;
 static void cols2_scratch(void* ws, int64_t strips, float** colmax, uint32_t** arrive,
@@ -801,8 +802,8 @@ static ColsProb cols2_prob(const FqArgs& a, void* ws, int64_t* tasks, int64_t* s
   if (pr.P > 1 && *tasks > 0) {
     cols2_scratch(ws, strips, &pr.colmax, &pr.arrive, &pr.late, scratch_words);
     *scratch_words += a.nvec;
-    // polls a waiting task makes before it computes the maxima itself (each an atomic load
-    // and s_sleep 2): the caller's count, else 2^20
+    // polls a waiting task makes before it stops waiting and leaves its strip to the repair
+    // launch (each an atomic load and s_sleep 2): the caller's count, else 2^20
     pr.spins = a.polls != 0 ? a.polls : (1u << 20);
   }
   return pr;

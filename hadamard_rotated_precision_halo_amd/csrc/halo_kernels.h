@@ -29,7 +29,7 @@ struct FqArgs {
   uint32_t key0, key1;    // Philox4x32-10 key
   uint32_t ctr2, ctr3;    // Philox counter words 2 and 3 (word 0: position / 4, word 1: vector)
   uint32_t polls;         // columns passes that exchange maxima: polls of a waiting task
-                          // before it computes its strip's maxima itself (0: the default, 2^20)
+                          // before it stops waiting (0: the default, 2^20)
 };
 
 // in_bf16: 1 for bf16 input, 0 for fp32.  qt: 0 INT8, 1 E4M3, 2 E5M2, 3 fp32 values.
