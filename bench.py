@@ -62,6 +62,7 @@ GEMM_BYTES = 2 * M * K + 2 * M * N + 4 * (M + N)  # both code operands, bf16 out
 COPY_BYTES = 64 << 20                       # calibration: 64 MiB read + 64 MiB written
 COPY_REF_BYTES = 512 << 20                  # streaming reference: 512 MiB read + 512 MiB written
 KERNEL_SOURCES = ["hadamard_rotated_precision_halo_amd/csrc/gemm.hip",
+                  "hadamard_rotated_precision_halo_amd/csrc/fwht_dual.hip",
                   "hadamard_rotated_precision_halo_amd/csrc/fwht_quant.hip",
                   "hadamard_rotated_precision_halo_amd/csrc/fwht_wave.h",
                   "hadamard_rotated_precision_halo_amd/csrc/fwht_wave.hip",
@@ -73,6 +74,7 @@ K_PAD = 4000                                # rows of 4000 elements, padded to 4
 LARGE_BYTES = 16384 * 14336 * 3 + 4 * 16384
 LARGE_COLS_BYTES = 16384 * 14336 * 3 + 4 * 14336
 FQ_PAD_BYTES = M * K_PAD * 2 + M * K + 4 * M
+DUAL_BYTES = M * N * 2 + 2 * M * N + 4 * (M + N)  # one bf16 read, two code matrices, scales
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic_4096.json")
 
 # kernel-name patterns of each measured pass (rocprofv3 Kernel_Name substrings; a pass may
@@ -90,6 +92,7 @@ PASSES = {
     "copy_neg": (["neg_kernel"], None),  # 64 MiB calibration, or the 512 MiB copy reference
     "fq_batch_4096": (["halo::fq_batch_kernel<256, 0, 0, false, false>"], None),
     "gemm_i8_pair_4096": (["halo::gemm_kernel<0"], 2 * GEMM_GRID),
+    "fq_dual_4096": (["fq_dual_kernel<256, 0, false, false>"], None),
 }
 
 
@@ -395,6 +398,16 @@ def measure_kernels(H, torch, sets, iters, with_copy=False):
                                    for i, t in enumerate(mats)])
     rows_pad = _c_launcher(H, fq, [fq_args(Xp, H.ROWS) for Xp in padded])
 
+    # both passes of a matrix from one read (halo_fwht_quant_dual), beside the rows and the
+    # columns pass above on the same matrices
+    qc_buf = torch.empty((N, M), dtype=torch.int8, device="cuda:0")
+    sc_buf = torch.empty(N, dtype=torch.float32, device="cuda:0")
+    wsd = torch.empty(max(H.fwht_quant_dual_workspace_bytes(M, N, BLOCK), 256),
+                      dtype=torch.uint8, device="cuda:0")
+    dual = _c_launcher(H, "halo_fwht_quant_dual", [
+        (P(t), code(t.dtype), M, N, ld(t), BLOCK, code(torch.int8), P(qbuf), N, P(sbuf),
+         P(qc_buf), M, P(sc_buf), None, None, P(wsd), wsd.numel(), st) for t in mats])
+
     # the INT8 product as the forward runs it: its codes written just before by the rows
     # passes of that step's X and W (so they sit where the rotation left them), events
     # around the product's launch alone
@@ -434,7 +447,7 @@ def measure_kernels(H, torch, sets, iters, with_copy=False):
 
     legs = {"gemm_i8_4096": gemm, "gemm_fp8_4096": gemm_fp8, "fq_rows_4096": rows,
             "fq_cols_4096": cols, "fq_rows_opt_4096": rows_opt, "fq_cols_opt_4096": cols_opt,
-            "fq_rows_pad_4000": rows_pad, "linear_bwd_4096": bwd}
+            "fq_rows_pad_4000": rows_pad, "linear_bwd_4096": bwd, "fq_dual_4096": dual}
     if with_copy:
         # the padded rows pass shares the rows kernel and its grid: kept out of the counter
         # runs, whose per-pass averages would mix its smaller reads in
@@ -629,7 +642,8 @@ def summarize_pmc(fetch_dir, write_dir, command):
     w_scale = COPY_BYTES / (write["copy_neg"] * 1024.0)
     algo = {"gemm_i8_4096": GEMM_BYTES, "gemm_fp8_4096": GEMM_BYTES, "fq_rows_4096": FQ_BYTES,
             "fq_cols_4096": FQ_BYTES, "fq_rows_opt_4096": FQ_BYTES, "fq_cols_opt_4096": FQ_BYTES,
-            "fq_batch_4096": 4 * FQ_BYTES, "gemm_i8_pair_4096": 2 * GEMM_BYTES}
+            "fq_batch_4096": 4 * FQ_BYTES, "gemm_i8_pair_4096": 2 * GEMM_BYTES,
+            "fq_dual_4096": DUAL_BYTES}
     res = {"kernel_source_hash": source_hash(KERNEL_SOURCES), "command": command,
            "fetch_scale": f_scale, "write_scale": w_scale, "bytes_per_launch": {},
            "fetch_kib_raw": fetch, "write_kib_raw": write}
@@ -952,7 +966,13 @@ def main():
                            "frac": round(copy_gbs / PEAK_HBM_GBS, 4),
                            "what": "torch elementwise negation, 512 MiB read + 512 MiB written "
                                    "per launch: the streaming rate a plain copy reaches here; "
-                                   "frac_of_copy of each pass is against it"}},
+                                   "frac_of_copy of each pass is against it"},
+                       "dual": hbm_pass("fq_dual_4096", DUAL_BYTES) | {
+                           "two_passes_ms": round(t_rows + t_cols, 5),
+                           "what": "halo_fwht_quant_dual: the rows and the columns codes of one "
+                                   "4096 x 4096 bf16 matrix from a single read (algorithmic: "
+                                   "one read, both code matrices and scales), beside the rows "
+                                   "pass plus the columns pass"}},
         "gemm_fp8": {"bound": "mfma", "achieved": round(GEMM_OPS / (t["gemm_fp8_4096"] * 1e-3) / 1e12, 2),
                      "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(GEMM_OPS / (t["gemm_fp8_4096"] * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),

@@ -32,7 +32,8 @@ EXPORTS = ("halo_fwht_quant", "halo_fwht_quant_ex", "halo_fwht_quant_noalloc",
            "halo_fwht_quant_workspace_bytes",
            "halo_gemm_i8", "halo_gemm_fp8", "halo_linear_workspace_bytes",
            "halo_linear_workspace_bytes_ex", "halo_linear_fwd", "halo_linear_fwd_ex",
-           "halo_linear_bwd", "halo_linear_bwd_ex", "halo_mfma_rate_probe", "halo_status_str")
+           "halo_linear_bwd", "halo_linear_bwd_ex", "halo_fwht_quant_dual",
+           "halo_fwht_quant_dual_workspace_bytes", "halo_mfma_rate_probe", "halo_status_str")
 
 
 class QuantOpts(ctypes.Structure):
@@ -92,12 +93,16 @@ def lib():
         L.halo_linear_bwd_ex.argtypes = [vp, vp, vp, e, i64, i64, i64, i32, e, e, vp, vp, lo, vp,
                                          sz, vp]
         L.halo_mfma_rate_probe.argtypes = [i32, i32, ctypes.POINTER(ctypes.c_int64), vp]
+        L.halo_fwht_quant_dual_workspace_bytes.argtypes = [i64, i64, i32, e]
+        L.halo_fwht_quant_dual_workspace_bytes.restype = sz
+        L.halo_fwht_quant_dual.argtypes = [vp, e, i64, i64, i64, i32, e, vp, i64, vp, vp, i64, vp,
+                                           qo, qo, vp, sz, vp]
         L.halo_status_str.argtypes = [e]
         L.halo_status_str.restype = ctypes.c_char_p
         for f in ("halo_fwht_quant", "halo_fwht_quant_ex", "halo_fwht_quant_noalloc",
                   "halo_gemm_i8", "halo_gemm_fp8",
                   "halo_linear_fwd", "halo_linear_fwd_ex", "halo_linear_bwd",
-                  "halo_linear_bwd_ex", "halo_mfma_rate_probe"):
+                  "halo_linear_bwd_ex", "halo_fwht_quant_dual", "halo_mfma_rate_probe"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -222,6 +227,56 @@ def fwht_quant(x, axis=ROWS, block=256, q_dtype=torch.int8, q=None, scale=None, 
                                   ws_bytes, _stream(stream))
     _check(st, "halo_fwht_quant_ex")
     return q, scale
+
+
+def fwht_quant_dual_workspace_bytes(rows, cols, block, x_dtype=torch.bfloat16):
+    return int(lib().halo_fwht_quant_dual_workspace_bytes(int(rows), int(cols), int(block),
+                                                          _code(x_dtype)))
+
+
+def _quant_opts(signs, rounding, seed, counter, exchange_polls):
+    rnd = _rounding(rounding)
+    if signs is None and rnd == NEAREST and not exchange_polls:
+        return None
+    return QuantOpts(_ptr(signs), rnd, _u32x2(seed), _u32x2(counter), int(exchange_polls))
+
+
+def fwht_quant_dual(x, block=256, q_dtype=torch.int8, qr=None, scale_r=None, qc=None,
+                    scale_c=None, workspace=None, stream=None, row_signs=None, col_signs=None,
+                    rounding="nearest", seed=0, row_counter=0, col_counter=0, exchange_polls=0):
+    """Both passes of x from one read where the shape allows (halo_fwht_quant_dual): returns
+    (qr, scale_r, qc, scale_c), the codes and scales of fwht_quant along the rows and along
+    the columns.  `row_signs` / `col_signs`: each pass's sign words (along the columns of a row
+    / the rows of a column); `rounding`, `seed`, the counters and `exchange_polls` as in
+    fwht_quant (the counter of each pass its own).  `workspace`: the scratch, allocated here
+    when None; False runs without it."""
+    rows, cols = x.shape
+    if qr is None:
+        qr = torch.empty((rows, padded_len(cols, block)), dtype=q_dtype, device=x.device)
+    if scale_r is None:
+        scale_r = torch.empty(rows, dtype=torch.float32, device=x.device)
+    if qc is None:
+        qc = torch.empty((cols, padded_len(rows, block)), dtype=q_dtype, device=x.device)
+    if scale_c is None:
+        scale_c = torch.empty(cols, dtype=torch.float32, device=x.device)
+    if workspace is False:
+        ws_ptr, ws_bytes = None, 0
+    else:
+        need = fwht_quant_dual_workspace_bytes(rows, cols, block, x.dtype)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        ws_ptr, ws_bytes = (None, 0) if workspace is None else (_ptr(workspace),
+                                                                workspace.numel())
+    ro = _quant_opts(row_signs, rounding, seed, row_counter, exchange_polls)
+    co = _quant_opts(col_signs, rounding, seed, col_counter, exchange_polls)
+    st = lib().halo_fwht_quant_dual(_ptr(x), _code(x.dtype), rows, cols, _ld(x), int(block),
+                                    _code(q_dtype), _ptr(qr), _ld(qr), _ptr(scale_r), _ptr(qc),
+                                    _ld(qc), _ptr(scale_c),
+                                    ctypes.byref(ro) if ro is not None else None,
+                                    ctypes.byref(co) if co is not None else None, ws_ptr,
+                                    ws_bytes, _stream(stream))
+    _check(st, "halo_fwht_quant_dual")
+    return qr, scale_r, qc, scale_c
 
 
 MFMA_PROBE_KINDS = {0: "v_mfma_i32_32x32x32_i8", 1: "v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3)",

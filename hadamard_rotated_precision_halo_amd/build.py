@@ -8,8 +8,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libhalo.so")
-SOURCES = ["halo_api.hip", "fwht_quant.hip", "fwht_wave.hip", "fwht_wave_sr.hip", "gemm.hip",
-           "mfma_probe.hip"]
+SOURCES = ["halo_api.hip", "fwht_quant.hip", "fwht_wave.hip", "fwht_wave_sr.hip", "fwht_dual.hip",
+           "gemm.hip", "mfma_probe.hip"]
 HEADERS = ["halo_device.h", "halo_kernels.h", "fwht_wave.h"]
 
 # -packed-fp32-ops off: hipcc -O3 would otherwise form v_pk_*_f32 from scalar float code.

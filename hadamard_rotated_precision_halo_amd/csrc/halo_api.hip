@@ -374,6 +374,46 @@ halo_status halo_fwht_quant_noalloc(const void* x, halo_dtype x_type, int64_t ro
                 ws ? HALO_NOALLOC_SCRATCH_BYTES : 0, (hipStream_t)stream, pass_opts(opts));
 }
 
+size_t halo_fwht_quant_dual_workspace_bytes(int64_t rows, int64_t cols, int32_t block,
+                                            halo_dtype x_type) {
+  if (!dtype_ok(x_type)) return 0;
+  if (rows < 0 || cols < 0 || rows >= kMaxDim || cols >= kMaxDim || !valid_block(block))
+    return 0;
+  // the single-read launch's scratch, or, for shapes it does not take, the columns pass's
+  const size_t dual = fq_dual_ws_bytes(rows, cols, block, x_type == HALO_BF16 ? 1 : 0);
+  const size_t cols_ws = fq_ws_bytes_len(padded_len(rows, block), cols, HALO_ALONG_COLS, block,
+                                         x_type);
+  return dual > cols_ws ? dual : cols_ws;
+}
+
+halo_status halo_fwht_quant_dual(const void* x, halo_dtype x_type, int64_t rows, int64_t cols,
+                                 int64_t ldx, int32_t block, halo_dtype q_type, void* qr,
+                                 int64_t ldqr, float* scale_r, void* qc, int64_t ldqc,
+                                 float* scale_c, const halo_quant_opts* row_opts,
+                                 const halo_quant_opts* col_opts, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  if (!dtype_ok(x_type) || !dtype_ok(q_type)) return HALO_ERR_DTYPE;
+  halo_status s = check_fq(x, x_type, rows, cols, ldx, HALO_ALONG_ROWS, block, q_type, qr, ldqr,
+                           scale_r, row_opts);
+  if (s != HALO_OK) return s;
+  s = check_fq(x, x_type, rows, cols, ldx, HALO_ALONG_COLS, block, q_type, qc, ldqc, scale_c,
+               col_opts);
+  if (s != HALO_OK) return s;
+  if (ws && !aligned16(ws)) return HALO_ERR_ALIGN;
+  const hipStream_t st = (hipStream_t)stream;
+  const FqArgs ar = make_fq(x, rows, cols, ldx, HALO_ALONG_ROWS, block, q_type, qr, ldqr, scale_r,
+                            pass_opts(row_opts));
+  const FqArgs ac = make_fq(x, rows, cols, ldx, HALO_ALONG_COLS, block, q_type, qc, ldqc, scale_c,
+                            pass_opts(col_opts));
+  const int inb = x_type == HALO_BF16 ? 1 : 0;
+  if (ws && fq_dual_supported(rows, cols, block, inb, qt_index(q_type), ar.sr != 0, ac.sr != 0,
+                              ws_bytes))
+    return from_hip(launch_fq_dual(ar, ac, ws, qt_index(q_type), 0, st));
+  s = run_fa(ar, x_type, HALO_ALONG_ROWS, q_type, nullptr, 0, st);
+  if (s != HALO_OK) return s;
+  return run_fa(ac, x_type, HALO_ALONG_COLS, q_type, ws, ws ? ws_bytes : 0, st);
+}
+
 halo_status halo_gemm_i8(const int8_t* a, int64_t lda, const float* sa, const int8_t* b,
                          int64_t ldb, const float* sb, int64_t m, int64_t n, int64_t k, void* c,
                          halo_dtype c_type, int64_t ldc, void* stream) {

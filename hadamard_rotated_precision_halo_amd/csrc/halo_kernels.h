@@ -53,6 +53,17 @@ hipError_t launch_fq_batch(const FqArgs* rows, const FqArgs& cw, void* ws_w, con
                            void* ws_dy, const FqArgs& cx, void* ws_x, int qg, int qw,
                            hipStream_t st);
 
+// Both passes of one bf16 matrix from a single read (fwht_dual.hip): the rows pass ar and
+// the columns pass ac of the same x (same block and code type qt), with one scratch whose
+// size fq_dual_ws_bytes gives (0: the shape is not covered: rows and cols multiples of 256,
+// block <= 256).  fq_dual_supported also asks that all 256 x 256 tiles fit on the device at
+// once and that both passes round to nearest.
+size_t fq_dual_ws_bytes(int64_t rows, int64_t cols, int block, int in_bf16);
+bool fq_dual_supported(int64_t rows, int64_t cols, int block, int in_bf16, int qt, bool sr_rows,
+                       bool sr_cols, size_t ws_bytes);
+hipError_t launch_fq_dual(const FqArgs& ar, const FqArgs& ac, void* ws, int qt, int prezeroed,
+                          hipStream_t st);
+
 // Zero n floats (also used for 32-bit counters).
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 

@@ -317,6 +317,32 @@ halo_status halo_fwht_quant_noalloc(const void* x, halo_dtype x_type, int64_t ro
                                     const halo_quant_opts* opts, void* stream);
 
 /*
+ * Both rotation passes of one matrix, from a single read of it where the shape allows: the
+ * codes and scales halo_fwht_quant_ex gives along the rows (qr [rows x Lc], leading dimension
+ * ldqr, scale_r [rows], options row_opts) and along the columns (qc [cols x Lr], ldqc,
+ * scale_c [cols], col_opts), with one block and one code type.  A layer backward needs its
+ * gradient dY both ways (rows for dX = dY W, columns for dW = dY^T X: the HALO page's
+ * rotations in the backward pass; QWHA page s2.1-s2.2, s3.1 for the transform and the
+ * quantiser); the two separate passes read dY twice.
+ *   ws   scratch of halo_fwht_quant_dual_workspace_bytes(rows, cols, block, x_type) bytes,
+ *        16-byte aligned, clobbered (its first 32-bit word then holds the number of
+ *        workgroups that stopped waiting for an exchange, as in halo_fwht_quant).
+ * The single read applies when x is bf16, rows and cols are multiples of 256, block <= 256,
+ * both passes round to nearest, all (rows / 256) x (cols / 256) tiles fit on the device at
+ * once (one per compute unit: up to 4096 x 4096 on 256 CUs) and ws is large enough; every
+ * other valid call runs the two passes one after the other, with the same results.  Each
+ * argument is validated as halo_fwht_quant_ex validates it for its pass; options as there.
+ */
+size_t halo_fwht_quant_dual_workspace_bytes(int64_t rows, int64_t cols, int32_t block,
+                                            halo_dtype x_type);
+halo_status halo_fwht_quant_dual(const void* x, halo_dtype x_type, int64_t rows, int64_t cols,
+                                 int64_t ldx, int32_t block, halo_dtype q_type, void* qr,
+                                 int64_t ldqr, float* scale_r, void* qc, int64_t ldqc,
+                                 float* scale_c, const halo_quant_opts* row_opts,
+                                 const halo_quant_opts* col_opts, void* ws, size_t ws_bytes,
+                                 void* stream);
+
+/*
  * Measurement aid, not part of the layer: the sustained rate of the matrix-core instruction a
  * product uses, on the whole device, to set the products' measured rates beside what the
  * instruction alone reaches under a sustained load (the published dense peaks assume the

@@ -290,3 +290,27 @@ def test_mfma_rate_probe_validation(L):
     for kind, iters in ((-1, 100), (3, 100), (0, 1), (0, 0), (1, (1 << 20) + 1)):
         assert L.halo_mfma_rate_probe(kind, iters, ctypes.byref(ops), None) == SHAPE
     assert ops.value == -1  # refused before anything is written or launched
+
+
+def test_fwht_quant_dual_validation(L):
+    def dual(x=P, xt=BF16, rows=256, cols=256, ldx=256, block=128, qt=I8, qr=P2, ldqr=256,
+             sr=P3, qc=P, ldqc=256, sc=P2, ws=None, wsb=0):
+        return L.halo_fwht_quant_dual(x, xt, rows, cols, ldx, block, qt, qr, ldqr, sr, qc, ldqc,
+                                      sc, None, None, ws, wsb, None)
+    assert dual(qc=NUL) == NULL
+    assert dual(sr=NUL) == NULL
+    assert dual(xt=I8) == DTYPE
+    assert dual(block=5) == BLOCK
+    assert dual(ldqr=128) == SHAPE               # row codes need 256 per row
+    assert dual(ldqc=128) == SHAPE               # column codes need 256 per column
+    assert dual(qc=BAD) == ALIGN
+    assert dual(ws=BAD, wsb=4096) == ALIGN
+    W = L.halo_fwht_quant_dual_workspace_bytes
+    # single read: late word (256 B), tile-column and tile-row counts (256 B each), maxima
+    assert W(4096, 4096, 256, BF16) == 768 + 4 * 4096 + 4 * 4096
+    assert W(8192, 8192, 256, BF16) == 768 + 4 * 8192 + 4 * 8192
+    assert W(300, 512, 256, BF16) == 0           # no single read, and short columns need none
+    assert W(8192, 520, 8, BF16) == L.halo_fwht_quant_workspace_bytes(8192, 520, 1, 8, BF16)
+    assert W(4096, 4096, 256, F32) == 0
+    assert W(4096, 4096, 512, BF16) == 0
+    assert W(-1, 4096, 256, BF16) == 0
