@@ -10,7 +10,7 @@
 // Tiling.  A 512-thread workgroup (8 wave64s, 2 x 4) owns a 256 x 256 output tile; each wave
 // owns 128 x 64 = 4 x 2 MFMA tiles of 32 x 32 with the accumulators resident in AGPRs.  K is
 // consumed in slabs of BK bytes: a slab (256 rows of each operand) is staged in LDS with
-// direct-to-LDS loads (global_load_lds_dwordx4: no VGPR staging, no ds_write) into a ring of
+// direct-to-LDS loads (buffer_load_dwordx4 ... lds: no VGPR staging, no ds_write) into a ring of
 // NSTAGE slabs filling 128 KB of the 160 KB LDS.  One barrier per slab, placed before the
 // slab's last MFMA sub-step: by then that sub-step's fragments are already in VGPRs, so the
 // slab's ring slot is refilled right after the barrier (with the slab NSTAGE ahead) while the
@@ -55,9 +55,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
-// One 16-byte direct-to-LDS load per lane: the lane's 16 bytes at g land at lds + 16 * lane.
-__device__ __forceinline__ void dma16(const void* g, lds_void* lds) {
-  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+// One 16-byte direct-to-LDS load per lane (buffer_load_dwordx4 ... lds): the lane's 16 bytes
+// at byte offset off of the resource land at lds + 16 * lane.  The buffer form rather than the
+// global one (global_load_lds_dwordx4): the compiler counts a global-to-LDS load as both a
+// memory load and an LDS access, and then makes every later LDS read wait for all outstanding
+// LDS reads (lgkmcnt(0)); the buffer form counts only as a memory load, so the fragment reads
+// keep exact lgkmcnt waits and an MFMA starts as soon as its own fragments have landed.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t off, lds_void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, off, 0, 0, 0);
+}
+
+// Raw buffer resource over [p, p + 4 GiB): no range check below that (the operands' byte spans
+// are validated to stay under 4 GiB); dword 3 selects 32-bit data, as gfx9 raw loads need.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, -1, 0x00020000);
 }
 
 // s_waitcnt immediate for vmcnt(n) with expcnt and lgkmcnt unconstrained (gfx9 encoding:
@@ -169,8 +180,7 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_kernel(GemmPair gp) {
   // Wave w's instruction i fills LDS bytes [(INST w + i) KB, +1 KB) of an operand's slab =
   // rows WROWS w + RPI i + [0, RPI); lane l lands in physical chunk l % CHUNKS of row
   // WROWS w + RPI i + l / CHUNKS and loads that row's logical chunk (l % CHUNKS) ^ swz(row).
-  const char* __restrict__ A = reinterpret_cast<const char*>(g.a);
-  const char* __restrict__ Bm = reinterpret_cast<const char*>(g.b);
+  const __amdgpu_buffer_rsrc_t ra = raw_rsrc(g.a), rb = raw_rsrc(g.b);
   uint32_t aoff[INST], boff[INST];  // byte offsets of the lane's rows (operands are < 4 GB)
   uint32_t cbo[INST];               // byte offset of the lane's chunk within a slab row
 #pragma unroll
@@ -200,8 +210,8 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_kernel(GemmPair gp) {
       const int i = q >> 1;
       uint32_t kc = kb + cbo[i];
       if constexpr (MASK) kc = min(kc, klast);
-      if (q & 1) dma16(Bm + boff[i] + kc, (lds_void*)(sb + (wave * INST + i) * 1024));
-      else dma16(A + aoff[i] + kc, (lds_void*)(sa + (wave * INST + i) * 1024));
+      if (q & 1) dma16(rb, boff[i] + kc, (lds_void*)(sb + (wave * INST + i) * 1024));
+      else dma16(ra, aoff[i] + kc, (lds_void*)(sa + (wave * INST + i) * 1024));
     }
   };
   auto stage = [&](int kt) __attribute__((always_inline)) { stage_part(kt, 0, 2 * INST); };

@@ -210,10 +210,12 @@ size_t fq_ws_bytes_len(int64_t len, int64_t nvec, halo_axis axis, int32_t block,
   return fq_cols2_ws_bytes(len, nvec, block, xt == HALO_BF16 ? 1 : 0);
 }
 
-// The GEMM kernel addresses each code operand with 32-bit byte offsets: an operand of `rows`
-// rows (leading dimension ld bytes, k bytes used per row) must span less than 4 GiB.
+// The GEMM kernel loads each code operand through a buffer resource of 2^32 - 1 bytes with
+// 32-bit byte offsets: an operand of `rows` rows (leading dimension ld bytes, k bytes used per
+// row) must end below byte 2^32 - 1 of its base (a load reaching past the resource's size would
+// read zeros).  Both ld and k are multiples of 16, so the span is at most 2^32 - 16.
 bool operand_fits(int64_t rows, int64_t ld, int64_t k) {
-  return rows <= 0 || (rows - 1) * ld + k <= (int64_t(1) << 32);
+  return rows <= 0 || (rows - 1) * ld + k < (int64_t(1) << 32);
 }
 
 halo_status check_gemm(const void* a, int64_t lda, const void* b, int64_t ldb, int64_t m,

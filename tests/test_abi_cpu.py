@@ -165,6 +165,10 @@ def test_gemm_i8_validation(L):
     big = (1 << 20) + 1                     # (big - 1) * 4096 + 4096 = 2^32 + 4096
     assert gi8(L, m=big, lda=4096, ldb=4096, k=4096) == SHAPE
     assert gi8(L, n=big, lda=4096, ldb=4096, k=4096) == SHAPE
+    # a span of exactly 2^32 bytes is refused too: its last load would end past the
+    # 2^32 - 1 bytes that the kernel's buffer resource covers
+    assert gi8(L, m=1 << 20, lda=4096, ldb=4096, k=4096) == SHAPE
+    assert gi8(L, n=1 << 20, lda=4096, ldb=4096, k=4096) == SHAPE
 
 
 def gf8(L, a=P, at=E4M3, lda=128, sa=P2, b=P3, bt=E4M3, ldb=128, sb=P2, m=64, n=64, k=128, c=P,
