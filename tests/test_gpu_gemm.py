@@ -116,6 +116,35 @@ def test_gemm_empty_and_degenerate():
     assert (c == 0).all()
 
 
+@pytest.mark.parametrize("big", ["a", "b"])
+def test_gemm_i8_operand_spanning_almost_4gib(big):
+    # The kernel loads each operand through a buffer resource with 32-bit byte offsets: an
+    # operand of 2^20 - 1 rows of 4096 bytes spans 2^32 - 4096 bytes, the largest accepted, and
+    # its last rows start just below 2^32 (rows past 2^31 / 4096 need the offsets unsigned).
+    # Its rows repeat a seeded 4099-row pattern, so every accumulator is known from the
+    # oracle's product of the pattern; every one is compared.
+    rng = np.random.default_rng(41)
+    rows, k, other = (1 << 20) - 1, 4096, 64
+    pattern = _codes(rng, 4099, k)
+    small = _codes(rng, other, k)
+    idx = torch.arange(rows, device=DEV) % pattern.shape[0]
+    big_dev = codes_to_dev(pattern, O.I8)[idx]          # torch gather: 4 GiB - 4 KiB of codes
+    small_dev = codes_to_dev(small, O.I8)
+    ref = O.gemm_i8(pattern, small)                      # [4099 x 64] int64
+    print(f"operand {big}: {rows} x {k} codes", flush=True)
+    if big == "a":
+        acc = H.gemm_i8(big_dev, None, small_dev, None, out_dtype=torch.int32)
+        want = torch.from_numpy(ref.astype(np.int32)).to(DEV)[idx]
+    else:
+        acc = padded_out(other, rows, torch.int32)
+        H.gemm_i8(small_dev, None, big_dev, None, c=acc)
+        want = torch.from_numpy(np.ascontiguousarray(ref.T).astype(np.int32)).to(DEV)[:, idx]
+    torch.cuda.synchronize()
+    assert np.abs(ref).max() < 2**31
+    bad = int((acc != want).sum().item())
+    assert bad == 0, f"{bad} accumulators differ"
+
+
 def test_gemm_i8_strided_operands_and_output():
     rng = np.random.default_rng(5)
     a_full = _codes(rng, 200, 512)
