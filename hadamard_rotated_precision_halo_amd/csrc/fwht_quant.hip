@@ -478,8 +478,8 @@ hipError_t launch_fwht_quant(const FqArgs& a, int in_bf16, int qt, int axis, voi
                              size_t ws_bytes, hipStream_t st) {
   if (axis == 0 && fq_rows2_supported(a.len, a.block) && (in_bf16 || !a.sr))
     return launch_fq_rows2(a, in_bf16, qt, st);
-  if (axis == 1 && fq_cols2_supported(a.len, a.nvec, a.block, in_bf16, ws_bytes))
-    return launch_fq_cols2(a, qt, ws, st);
+  if (axis == 1 && fq_cols2_supported(a.len, a.nvec, a.block, in_bf16, a.sr != 0, ws_bytes))
+    return launch_fq_cols2(a, in_bf16, qt, ws, st);
   if (in_bf16) {
     switch (qt) {
       case 0: return dispatch_block<uint16_t, 0>(a, axis, st);

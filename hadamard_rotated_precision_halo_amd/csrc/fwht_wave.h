@@ -529,11 +529,97 @@ __device__ __forceinline__ void cols_load(const ColsProb& pr, int64_t c0, int pa
   }
 }
 
+// fp32 input.  A task keeps the bf16 tile's geometry (R rows x C columns, 65536 values, each
+// wave one slice of 4096), but in fp32 the tile is 256 KB, so it goes through the 128 KB LDS
+// in two rounds.  Round h holds chunks 4 h .. 4 h + 3 of every lane (the 8-value chunks of
+// Slice<B>): the rows whose offset in their column segment has bit HB equal to h, HB being the
+// top bit of a block for B >= 64 (the chunk number is the top 3 bits of the offset in a block)
+// and bit 5 below that (the chunk number is offset bits 3-5).  Every element is still read
+// from HBM once: a thread issues both rounds' loads before the first is staged.
+constexpr int lg2c(int v) { return v <= 1 ? 0 : 1 + lg2c(v / 2); }
+
+// Row group (of 8 rows) of index i in round h: the group index with bit HB - 3 set to h.
+template <int B>
+__device__ __forceinline__ int f32_group(int i, int h) {
+  constexpr int SH = lg2c(B >= 64 ? B : 64) - 4;  // HB - 3
+  return ((i >> SH) << (SH + 1)) | (h << SH) | (i & ((1 << SH) - 1));
+}
+
+// LDS unit (16 bytes) holding half `half` (rows 0-3 or 4-7) of chunk j of `lane` in wave w,
+// for the round that holds chunk j: lane-major per (chunk, half), so the compute reads are
+// contiguous, with the bf16 tile's XOR on the low lane bits.
+template <int B>
+__device__ __forceinline__ int lds_unit_f32(int w, int lane, int j, int half) {
+  constexpr int JA = B >= 64 ? B / 64 : 1;
+  return w * 512 + (j & 3) * 128 + half * 64 + (lane ^ (((j * JA) ^ w) & 15));
+}
+
+// Both rounds' loads of part `part` of the strip at column c0: in round h each thread reads 8
+// rows (row group f32_group(i, h)) of 4 adjacent columns, 16 bytes per row.
+template <int B>
+__device__ __forceinline__ void cols_load_f32(const ColsProb& pr, int64_t c0, int part, int t,
+                                              uint4 (&raw)[2][8]) {
+  const FqArgs& a = pr.a;
+  const int R = pr.R, CC = pr.C / 4;         // 16-byte (4-column) chunks per tile row
+  const int cc = t % CC, i = t / CC;         // column chunk, row-group index of a round
+  const float* __restrict__ xin = reinterpret_cast<const float*>(a.x);
+  const int64_t col = c0 + cc * 4;
+  const float* p0 = xin + (col < a.nvec ? col : 0);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int64_t r0 = (int64_t)part * R + f32_group<B>(i, h) * 8;
+    const float* p = p0 + r0 * a.ldx;
+    // rows of the zero padding read row 0 instead and are zeroed below
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      raw[h][e] = *reinterpret_cast<const uint4*>(r0 + e < a.in_len ? p + e * a.ldx : p0);
+    if (a.in_len < a.len) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (r0 + e >= a.in_len) raw[h][e] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    if (a.signs) {  // the transform's signs: one bit per row, on the fp32 sign bits
+      const uint32_t b = a.signs[r0 >> 5] >> (r0 & 31);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t f = ((b >> e) & 1u) ? 0x80000000u : 0u;
+        raw[h][e].x ^= f; raw[h][e].y ^= f; raw[h][e].z ^= f; raw[h][e].w ^= f;
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ uint32_t word_of(const uint4& u, int e) {
+  return e == 0 ? u.x : e == 1 ? u.y : e == 2 ? u.z : u.w;
+}
+
+// Round h into the LDS: each of the thread's 4 columns becomes the two 16-byte halves of one
+// chunk (8 consecutive rows of that column).
+template <int B>
+__device__ __forceinline__ void cols_stage_f32(const ColsProb& pr, int t, int h,
+                                               const uint4 (&raw)[8], uint4* lds) {
+  using S = Slice<B>;
+  const int R = pr.R, CC = pr.C / 4, cpw = 4096 / R;
+  const int cc = t % CC, g8 = f32_group<B>(t / CC, h);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int cl = cc * 4 + e;               // column within the tile
+    const int wr = cl / cpw, ciw = cl % cpw;
+    int ln, j;
+    S::where(ciw * R + g8 * 8, ln, j);
+    lds[lds_unit_f32<B>(wr, ln, j, 0)] = make_uint4(word_of(raw[0], e), word_of(raw[1], e),
+                                                    word_of(raw[2], e), word_of(raw[3], e));
+    lds[lds_unit_f32<B>(wr, ln, j, 1)] = make_uint4(word_of(raw[4], e), word_of(raw[5], e),
+                                                    word_of(raw[6], e), word_of(raw[7], e));
+  }
+}
+
 // One task (one R-row part of one column strip) of a column pass, run by a whole workgroup of
 // 16 waves.
 // REPAIR: the second launch of an exchanging pass (see below): only the tasks of strips marked
 // late run, with the column maxima complete by then.
-template <int B, int QT, bool SR, bool REPAIR = false>
+// F32: fp32 input (two LDS rounds, see cols_load_f32); else bf16.
+template <int B, int QT, bool SR, bool REPAIR = false, bool F32 = false>
 __device__ __forceinline__ void cols_task(const ColsProb& pr, int64_t ltask, uint4* lds) {
   using S = Slice<B>;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -576,16 +662,37 @@ __device__ __forceinline__ void cols_task(const ColsProb& pr, int64_t ltask, uin
     if (!s_mark) return;
   }
 
-  // ---- load R rows x C columns, transposed into LDS ---------------------------------------
-  cols_load<B>(pr, c0, part, t, lds);
-  __syncthreads();
+  // ---- load R rows x C columns, transposed into LDS, into the wave's slices ---------------
+  float v[64];
+  if constexpr (F32) {
+    uint4 raw[2][8];
+    cols_load_f32<B>(pr, c0, part, t, raw);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      cols_stage_f32<B>(pr, t, h, raw[h], lds);
+      __syncthreads();
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int j = 4 * h + jj;
+        const uint4 lo = lds[lds_unit_f32<B>(w, lane, j, 0)];
+        const uint4 hi = lds[lds_unit_f32<B>(w, lane, j, 1)];
+        v[j * 8 + 0] = __uint_as_float(lo.x); v[j * 8 + 1] = __uint_as_float(lo.y);
+        v[j * 8 + 2] = __uint_as_float(lo.z); v[j * 8 + 3] = __uint_as_float(lo.w);
+        v[j * 8 + 4] = __uint_as_float(hi.x); v[j * 8 + 5] = __uint_as_float(hi.y);
+        v[j * 8 + 6] = __uint_as_float(hi.z); v[j * 8 + 7] = __uint_as_float(hi.w);
+      }
+      if (h == 0) __syncthreads();  // round 1 overwrites the LDS tile
+    }
+  } else {
+    cols_load<B>(pr, c0, part, t, lds);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) unpack_bf16x8(lds[lds_slot<B>(w, lane, j)], &v[j * 8]);
+  }
 
   // ---- rotate the wave's column segments --------------------------------------------------
   const int seg = S::off(lane, 0) / R;       // column segment of this lane within the wave
   const int64_t pos0 = (int64_t)part * R - (int64_t)seg * R;  // + off(lane, j): row index
-  float v[64];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) unpack_bf16x8(lds[lds_slot<B>(w, lane, j)], &v[j * 8]);
   const float sgn = rotate64<B>(v, lane);
   const int64_t col = c0 + w * cpw + seg;
   const bool valid = col < ncols;
@@ -671,7 +778,7 @@ __device__ __forceinline__ bool any_late(const uint32_t* a, const uint32_t* b, c
   return s_any != 0;
 }
 
-template <int B, int QT, bool SR, bool REPAIR = false>
+template <int B, int QT, bool SR, bool REPAIR = false, bool F32 = false>
 __global__ __launch_bounds__(1024) void fq_cols2_kernel(ColsProb c0, ColsProb c1, int64_t split,
                                                         int64_t tasks) {
   extern __shared__ __attribute__((aligned(16))) uint4 lds[];
@@ -681,7 +788,7 @@ __global__ __launch_bounds__(1024) void fq_cols2_kernel(ColsProb c0, ColsProb c1
   for (int64_t task = blockIdx.x; task < tasks; task += gridDim.x) {
     const bool second = task >= split;
     const ColsProb pr = second ? c1 : c0;
-    cols_task<B, QT, SR, REPAIR>(pr, task - (second ? split : 0), lds);
+    cols_task<B, QT, SR, REPAIR, F32>(pr, task - (second ? split : 0), lds);
     __syncthreads();  // the next task overwrites the LDS tile
   }
 }
@@ -809,11 +916,11 @@ static ColsProb cols2_prob(const FqArgs& a, void* ws, int64_t* tasks, int64_t* s
   return pr;
 }
 
-template <int B, int QT, bool SR>
+template <int B, int QT, bool SR, bool F32>
 static hipError_t launch_cols2_t(const FqArgs& a0, void* ws0, const FqArgs* a1, void* ws1,
                                  int prezeroed, hipStream_t st) {
-  auto* fn = &fq_cols2_kernel<B, QT, SR>;
-  hipError_t e = allow_dynamic_lds<&fq_cols2_kernel<B, QT, SR>>(kColsLdsBytes);
+  auto* fn = &fq_cols2_kernel<B, QT, SR, false, F32>;
+  hipError_t e = allow_dynamic_lds<&fq_cols2_kernel<B, QT, SR, false, F32>>(kColsLdsBytes);
   if (e != hipSuccess) return e;
   int64_t t0 = 0, t1 = 0, w0 = 0, w1 = 0;
   ColsProb p0 = cols2_prob(a0, ws0, &t0, &w0);
@@ -839,27 +946,27 @@ static hipError_t launch_cols2_t(const FqArgs& a0, void* ws0, const FqArgs* a1, 
     if (cap < P) return hipErrorInvalidConfiguration;
     p0.gs = p1.gs = cols2_group(P, cap);
   }
-  hipLaunchKernelGGL((fq_cols2_kernel<B, QT, SR>), dim3((unsigned)tasks), dim3(1024),
+  hipLaunchKernelGGL((fq_cols2_kernel<B, QT, SR, false, F32>), dim3((unsigned)tasks), dim3(1024),
                      kColsLdsBytes, st, p0, p1, t0, tasks);
   e = hipGetLastError();
   if (e != hipSuccess || P == 1) return e;
   // the repair launch: stores the strips whose tasks stopped waiting.  Usually there are
   // none, and its workgroups (at most one per compute unit, striding over the tasks) return
   // after reading the late counters.
-  e = allow_dynamic_lds<&fq_cols2_kernel<B, QT, SR, true>>(kColsLdsBytes);
+  e = allow_dynamic_lds<&fq_cols2_kernel<B, QT, SR, true, F32>>(kColsLdsBytes);
   if (e != hipSuccess) return e;
   const int cap = cols2_capacity(reinterpret_cast<const void*>(fn));
   const int64_t rgrid = tasks < cap ? tasks : cap;
-  hipLaunchKernelGGL((fq_cols2_kernel<B, QT, SR, true>), dim3((unsigned)rgrid), dim3(1024),
+  hipLaunchKernelGGL((fq_cols2_kernel<B, QT, SR, true, F32>), dim3((unsigned)rgrid), dim3(1024),
                      kColsLdsBytes, st, p0, p1, t0, tasks);
   return hipGetLastError();
 }
 
-template <int QT, bool SR>
+template <int QT, bool SR, bool F32 = false>
 static hipError_t cols2_block(const FqArgs& a0, void* ws0, const FqArgs* a1, void* ws1,
                               int prezeroed, hipStream_t st) {
 #define HALO_C2_CASE(BB) \
-  case BB: return launch_cols2_t<BB, QT, SR>(a0, ws0, a1, ws1, prezeroed, st);
+  case BB: return launch_cols2_t<BB, QT, SR, F32>(a0, ws0, a1, ws1, prezeroed, st);
   switch (a0.block) {
     HALO_C2_CASE(1) HALO_C2_CASE(2) HALO_C2_CASE(4) HALO_C2_CASE(8) HALO_C2_CASE(16)
     HALO_C2_CASE(32) HALO_C2_CASE(64) HALO_C2_CASE(128) HALO_C2_CASE(256) HALO_C2_CASE(512)

@@ -11,8 +11,7 @@ bool fq_rows2_supported(int64_t len, int block) {
   return block >= 1 && block <= 4096 && len % block == 0;
 }
 
-size_t fq_cols2_ws_bytes(int64_t rows, int64_t cols, int block, int in_bf16) {
-  if (!in_bf16) return 0;
+size_t fq_cols2_ws_bytes(int64_t rows, int64_t cols, int block) {
   const int R = cols2_rows_per_task(rows, block);
   if (R == 0) return 0;
   const int64_t P = rows / R;
@@ -23,23 +22,35 @@ size_t fq_cols2_ws_bytes(int64_t rows, int64_t cols, int block, int in_bf16) {
   return kColsLateBytes + cnt + (size_t)cols * 4;
 }
 
-bool fq_cols2_supported(int64_t rows, int64_t cols, int block, int in_bf16, size_t ws_bytes) {
-  if (!in_bf16 || rows <= 0 || cols <= 0) return false;
+bool fq_cols2_supported(int64_t rows, int64_t cols, int block, int in_bf16, bool sr,
+                        size_t ws_bytes) {
+  // fp32 input with stochastic rounding is left to the two-sweep kernel
+  if ((!in_bf16 && sr) || rows <= 0 || cols <= 0) return false;
   const int R = cols2_rows_per_task(rows, block);
   if (R == 0) return false;
   if (rows / R == 1) return true;
   // the parts of a strip wait for each other, so all of them must fit on the device at once;
   // longer columns take the two-sweep kernel, which never waits
   const int cap = cols2_capacity(reinterpret_cast<const void*>(&fq_cols2_kernel<256, 0, false>));
-  return rows / R <= cap && ws_bytes >= fq_cols2_ws_bytes(rows, cols, block, in_bf16);
+  return rows / R <= cap && ws_bytes >= fq_cols2_ws_bytes(rows, cols, block);
 }
 
 bool fq_batch_rows_ok(int64_t len) { return len >= 64 && len <= 4096 && 4096 % len == 0; }
 
-hipError_t launch_fq_cols2_pair(const FqArgs& a0, void* ws0, const FqArgs* a1, void* ws1, int qt,
-                                int prezeroed, hipStream_t st) {
-  // the two passes of one launch share the rounding mode
+hipError_t launch_fq_cols2_pair(const FqArgs& a0, void* ws0, const FqArgs* a1, void* ws1,
+                                int in_bf16, int qt, int prezeroed, hipStream_t st) {
+  // the two passes of one launch share the rounding mode and the input type
   if (a1 && a1->sr != a0.sr) return hipErrorInvalidValue;
+  if (!in_bf16) {
+    if (a0.sr) return hipErrorInvalidValue;
+    switch (qt) {
+      case 0: return cols2_block<0, false, true>(a0, ws0, a1, ws1, prezeroed, st);
+      case 1: return cols2_block<1, false, true>(a0, ws0, a1, ws1, prezeroed, st);
+      case 2: return cols2_block<2, false, true>(a0, ws0, a1, ws1, prezeroed, st);
+      case 3: return cols2_block<3, false, true>(a0, ws0, a1, ws1, prezeroed, st);
+    }
+    return hipErrorInvalidValue;
+  }
   if (a0.sr && qt != 3) return cols2_dispatch_sr(a0, ws0, a1, ws1, qt, prezeroed, st);
   switch (qt) {
     case 0: return cols2_block<0, false>(a0, ws0, a1, ws1, prezeroed, st);
@@ -50,8 +61,8 @@ hipError_t launch_fq_cols2_pair(const FqArgs& a0, void* ws0, const FqArgs* a1, v
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_fq_cols2(const FqArgs& a, int qt, void* ws, hipStream_t st) {
-  return launch_fq_cols2_pair(a, ws, nullptr, nullptr, qt, 0, st);
+hipError_t launch_fq_cols2(const FqArgs& a, int in_bf16, int qt, void* ws, hipStream_t st) {
+  return launch_fq_cols2_pair(a, ws, nullptr, nullptr, in_bf16, qt, 0, st);
 }
 
 hipError_t launch_fq_batch(const FqArgs* rows, const FqArgs& cw, void* ws_w, const FqArgs& cdy,

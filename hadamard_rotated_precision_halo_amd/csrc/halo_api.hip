@@ -205,9 +205,10 @@ halo_status run_fq(const void* x, halo_dtype xt, int64_t rows, int64_t cols, int
 
 // Scratch of one rotation pass (the single-read columns kernel's partial maxima and counters);
 // len: the rotated (padded) length.
-size_t fq_ws_bytes_len(int64_t len, int64_t nvec, halo_axis axis, int32_t block, halo_dtype xt) {
+// The same for bf16 and fp32 input.
+size_t fq_ws_bytes_len(int64_t len, int64_t nvec, halo_axis axis, int32_t block) {
   if (axis != HALO_ALONG_COLS) return 0;
-  return fq_cols2_ws_bytes(len, nvec, block, xt == HALO_BF16 ? 1 : 0);
+  return fq_cols2_ws_bytes(len, nvec, block);
 }
 
 // The GEMM kernel loads each code operand through a buffer resource of 2^32 - 1 bytes with
@@ -247,7 +248,7 @@ struct WsPlan {
   size_t scr_w, scr_dy, scr_x;  // sub-region sizes, in this order
 };
 
-WsPlan plan_ws(int64_t m, int64_t n, int64_t k, int backward, int32_t block, halo_dtype io) {
+WsPlan plan_ws(int64_t m, int64_t n, int64_t k, int backward, int32_t block) {
   WsPlan p{};
   size_t sizes[9];
   int cnt = 0;
@@ -274,9 +275,9 @@ WsPlan plan_ws(int64_t m, int64_t n, int64_t k, int backward, int32_t block, hal
     o += round256(sizes[i]);
   }
   if (backward) {
-    p.scr_w = round256(fq_ws_bytes_len(nq, k, HALO_ALONG_COLS, block, io));   // W columns along n
-    p.scr_dy = round256(fq_ws_bytes_len(mq, n, HALO_ALONG_COLS, block, io));  // dY columns along m
-    p.scr_x = round256(fq_ws_bytes_len(mq, k, HALO_ALONG_COLS, block, io));   // X columns along m
+    p.scr_w = round256(fq_ws_bytes_len(nq, k, HALO_ALONG_COLS, block));   // W columns along n
+    p.scr_dy = round256(fq_ws_bytes_len(mq, n, HALO_ALONG_COLS, block));  // dY columns along m
+    p.scr_x = round256(fq_ws_bytes_len(mq, k, HALO_ALONG_COLS, block));   // X columns along m
   }
   p.scratch_off = o;
   p.scratch_bytes = p.scr_w + p.scr_dy + p.scr_x;
@@ -334,7 +335,7 @@ size_t halo_fwht_quant_workspace_bytes(int64_t rows, int64_t cols, halo_axis axi
   if (rows < 0 || cols < 0 || rows >= kMaxDim || cols >= kMaxDim || !valid_block(block))
     return 0;
   if (axis != HALO_ALONG_COLS) return 0;
-  return fq_ws_bytes_len(padded_len(rows, block), cols, axis, block, x_type);
+  return fq_ws_bytes_len(padded_len(rows, block), cols, axis, block);
 }
 
 halo_status halo_fwht_quant_ex(const void* x, halo_dtype x_type, int64_t rows, int64_t cols,
@@ -383,8 +384,7 @@ size_t halo_fwht_quant_dual_workspace_bytes(int64_t rows, int64_t cols, int32_t 
     return 0;
   // the single-read launch's scratch, or, for shapes it does not take, the columns pass's
   const size_t dual = fq_dual_ws_bytes(rows, cols, block, x_type == HALO_BF16 ? 1 : 0);
-  const size_t cols_ws = fq_ws_bytes_len(padded_len(rows, block), cols, HALO_ALONG_COLS, block,
-                                         x_type);
+  const size_t cols_ws = fq_ws_bytes_len(padded_len(rows, block), cols, HALO_ALONG_COLS, block);
   return dual > cols_ws ? dual : cols_ws;
 }
 
@@ -449,8 +449,7 @@ size_t halo_linear_workspace_bytes_ex(int64_t m, int64_t n, int64_t k, int32_t b
   if (!dtype_ok(q_type)) return 0;
   if (!layer_dims_ok(m, n, k) || !valid_block(block)) return 0;
   if (q_type != HALO_I8 && q_type != HALO_E4M3) return 0;
-  // the columns passes' scratch is sized for bf16 input (fp32 input needs none)
-  return plan_ws(m, n, k, backward ? 1 : 0, block, HALO_BF16).total;
+  return plan_ws(m, n, k, backward ? 1 : 0, block).total;
 }
 
 size_t halo_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, halo_dtype q_type,
@@ -484,7 +483,7 @@ halo_status halo_linear_fwd_ex(const void* x, const void* w, halo_dtype io_type,
   if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return HALO_ERR_ALIGN;
   if ((n * esize(y_type)) % 16 != 0) return HALO_ERR_ALIGN;
   if (opts && check_signs(opts->signs_k) != HALO_OK) return HALO_ERR_ALIGN;
-  const WsPlan p = plan_ws(m, n, k, 0, block, io_type);
+  const WsPlan p = plan_ws(m, n, k, 0, block);
   if (!ws || ws_bytes < p.total) return HALO_ERR_WORKSPACE;
   if (!aligned16(ws)) return HALO_ERR_ALIGN;
   char* base = static_cast<char*>(ws);
@@ -552,7 +551,7 @@ halo_status halo_linear_bwd_ex(const void* dy, const void* x, const void* w, hal
   if ((dx && !aligned16(dx)) || (dw && !aligned16(dw))) return HALO_ERR_ALIGN;
   if (opts && (check_signs(opts->signs_n) != HALO_OK || check_signs(opts->signs_m) != HALO_OK))
     return HALO_ERR_ALIGN;
-  const WsPlan p = plan_ws(m, n, k, 1, block, io_type);
+  const WsPlan p = plan_ws(m, n, k, 1, block);
   if (!ws || ws_bytes < p.total) return HALO_ERR_WORKSPACE;
   if (!aligned16(ws)) return HALO_ERR_ALIGN;
   char* base = static_cast<char*>(ws);
@@ -603,8 +602,8 @@ halo_status halo_linear_bwd_ex(const void* dy, const void* x, const void* w, hal
   // one column pass: single-read when covered (its scratch already clear), else two reads
   auto cols_pass = [&](const FqArgs& a, halo_dtype qt, void* sws, size_t sbytes) {
     if (s != HALO_OK) return;
-    if (fq_cols2_supported(a.len, a.nvec, block, inb, sbytes))
-      s = from_hip(launch_fq_cols2_pair(a, sws, nullptr, nullptr, qt_index(qt), 1, st));
+    if (fq_cols2_supported(a.len, a.nvec, block, inb, a.sr != 0, sbytes))
+      s = from_hip(launch_fq_cols2_pair(a, sws, nullptr, nullptr, inb, qt_index(qt), 1, st));
     else
       s = run_fa(a, io_type, HALO_ALONG_COLS, qt, nullptr, 0, st);
   };
@@ -626,8 +625,9 @@ halo_status halo_linear_bwd_ex(const void* dy, const void* x, const void* w, hal
   };
   const int qg = qt_index(grad_q_type), qw = qt_index(q_type);
   const bool pair_ok = (qg == 0 && qw == 0) || (qg == 2 && qw == 1) || (qg == 1 && qw == 1);
-  if (dx && dw && inb && pair_ok && fq_cols2_supported(nq, k, block, 1, p.scr_w) &&
-      fq_cols2_supported(mq, n, block, 1, p.scr_dy) && fq_cols2_supported(mq, k, block, 1, p.scr_x)) {
+  if (dx && dw && inb && pair_ok && fq_cols2_supported(nq, k, block, 1, false, p.scr_w) &&
+      fq_cols2_supported(mq, n, block, 1, cdy.sr != 0, p.scr_dy) &&
+      fq_cols2_supported(mq, k, block, 1, false, p.scr_x)) {
     // every rotation pass of the backward in one launch (or two, when the dY rows are long):
     // the passes overlap on the device, then the two products
     const bool rows_in = fq_batch_rows_ok(nq);
@@ -645,11 +645,11 @@ halo_status halo_linear_bwd_ex(const void* dy, const void* x, const void* w, hal
     clear_scratch();
     if (dx) cols_pass(cw, q_type, scr_w, p.scr_w);
     if (dw) {
-      const bool c1 = fq_cols2_supported(mq, n, block, inb, p.scr_dy);
-      const bool c2 = fq_cols2_supported(mq, k, block, inb, p.scr_x);
+      const bool c1 = fq_cols2_supported(mq, n, block, inb, cdy.sr != 0, p.scr_dy);
+      const bool c2 = fq_cols2_supported(mq, k, block, inb, cx.sr != 0, p.scr_x);
       if (s == HALO_OK && c1 && c2 && grad_q_type == q_type && cdy.sr == cx.sr) {
         // dY and X columns in one launch
-        s = from_hip(launch_fq_cols2_pair(cdy, scr_dy, &cx, scr_x, qt_index(q_type), 1, st));
+        s = from_hip(launch_fq_cols2_pair(cdy, scr_dy, &cx, scr_x, inb, qt_index(q_type), 1, st));
       } else {
         cols_pass(cdy, grad_q_type, scr_dy, p.scr_dy);
         cols_pass(cx, q_type, scr_x, p.scr_x);

@@ -39,10 +39,13 @@ hipError_t launch_fwht_quant(const FqArgs& a, int in_bf16, int qt, int axis, voi
                              size_t ws_bytes, hipStream_t st);
 
 // Scratch bytes the single-read columns kernel needs for columns of `rows` elements (0 when
-// it needs none or does not cover the shape).
-size_t fq_cols2_ws_bytes(int64_t rows, int64_t cols, int block, int in_bf16);
-bool fq_cols2_supported(int64_t rows, int64_t cols, int block, int in_bf16, size_t ws_bytes);
-hipError_t launch_fq_cols2(const FqArgs& a, int qt, void* ws, hipStream_t st);
+// it needs none or does not cover the shape), for bf16 and fp32 input alike.
+size_t fq_cols2_ws_bytes(int64_t rows, int64_t cols, int block);
+// Whether the single-read columns kernel takes the pass (bf16 or fp32 input; fp32 with
+// stochastic rounding is not covered) given ws_bytes of scratch.
+bool fq_cols2_supported(int64_t rows, int64_t cols, int block, int in_bf16, bool sr,
+                        size_t ws_bytes);
+hipError_t launch_fq_cols2(const FqArgs& a, int in_bf16, int qt, void* ws, hipStream_t st);
 
 // The rotation passes of a layer backward in one launch (bf16 input): the rows of dY (codes
 // qg; may be NULL, else fq_batch_rows_ok(len) must hold) and the single-read column passes of
@@ -82,10 +85,11 @@ struct FqPair {
 };
 hipError_t launch_fq_rows2_pair(const FqPair& a, int in_bf16, int qt, hipStream_t st);
 
-// Up to two single-read column passes over columns of the same length, block and code type in
-// one launch (a1 may be NULL).  prezeroed: the scratch of both was cleared earlier on st.
-hipError_t launch_fq_cols2_pair(const FqArgs& a0, void* ws0, const FqArgs* a1, void* ws1, int qt,
-                                int prezeroed, hipStream_t st);
+// Up to two single-read column passes over columns of the same length, block, input type
+// (in_bf16) and code type in one launch (a1 may be NULL).  prezeroed: the scratch of both was
+// cleared earlier on st.
+hipError_t launch_fq_cols2_pair(const FqArgs& a0, void* ws0, const FqArgs* a1, void* ws1,
+                                int in_bf16, int qt, int prezeroed, hipStream_t st);
 
 // Longest row the single-pass rows kernel takes for this block size.
 int64_t fq_rows_max_len(int block);

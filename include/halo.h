@@ -107,9 +107,9 @@ typedef enum {
  *   ldq      leading dimension of q in elements.
  *   ws       optional device scratch of ws_bytes >= halo_fwht_quant_workspace_bytes(...)
  *            bytes (16-byte aligned), caller-owned; its contents on entry do not matter and
- *            are clobbered.  With it, a columns-axis pass over long bf16 columns reads its
- *            input once; with ws NULL (or too small) the pass reads its input twice and gives
- *            the same codes and scales.  Calls that share one scratch must be ordered on one
+ *            are clobbered.  With it, a columns-axis pass over long columns reads its input
+ *            once; with ws NULL (or too small) the pass reads its input twice and gives the
+ *            same codes and scales (as does fp32 input with stochastic rounding).  Calls that share one scratch must be ordered on one
  *            stream.  After such a pass completes, the first 32-bit word of ws holds the
  *            number of workgroups that stopped waiting for the exchange (a diagnostic; the
  *            results do not depend on it).
@@ -124,8 +124,9 @@ halo_status halo_fwht_quant(const void* x, halo_dtype x_type, int64_t rows, int6
                             void* stream);
 
 /*
- * Scratch bytes halo_fwht_quant can use for this shape (0 when it needs none: rows axis,
- * fp32 input, or columns short enough for one workgroup).  Invalid arguments give 0.
+ * Scratch bytes halo_fwht_quant can use for this shape (0 when it needs none: rows axis, or
+ * columns short enough for one workgroup; the same for bf16 and fp32 input).  Invalid
+ * arguments give 0.
  */
 size_t halo_fwht_quant_workspace_bytes(int64_t rows, int64_t cols, halo_axis axis,
                                        int32_t block, halo_dtype x_type);

@@ -45,7 +45,75 @@ def code_distance(a, b, qtype):
     return np.abs(fp8_ordinal(a) - fp8_ordinal(b))
 
 
-def assert_codes_close_to_fp64(gpu_q, ref_q, qtype, block, frac=1e-4):
+# FP8 grids: mantissa bits and the exponent of the smallest normal value.
+FP8_GRID = {O.E4M3: (3, -6), O.E5M2: (2, -14)}
+
+
+def fp8_step(t, qtype):
+    """Spacing of the FP8 grid at magnitude |t| (in code units; the subnormal spacing below
+    the smallest normal)."""
+    mb, emin = FP8_GRID[qtype]
+    e = np.floor(np.log2(np.maximum(np.abs(t), 2.0 ** emin)))
+    return 2.0 ** (e - mb)
+
+
+def fp32_rotation_code_bound(x, oaxis, block, qtype, opts=None):
+    """Exact real code values t = y * qmax / a of the oracle's fp64 definition, and an a-priori
+    bound e on how far the code value of an fp32 computation (fp32 butterflies, m = fl(qmax /
+    a32), fl(y32 * m)) can lie from t.  Each fp32 butterfly output is within
+    gamma_k * S of the exact sum (k = log2(block) stages, S = sum of |x| over its block); the
+    absmax a32 inherits that error from its own block, which moves m by at most
+    gamma_k * S_max / a + u; the product adds u.  Hence, per element,
+        |c32 - t| <= gamma_k * S * qmax / a + |t| * (gamma_k * S_max / a + 2 u),
+    with a the unnormalised absmax (the 1/sqrt(block) cancels).  Returns (t, e)."""
+    opts = dict(opts or {})
+    opts.pop("rounding", None)
+    y, a = O.fwht_quant(x, oaxis, block, O.F64, precision=64, **opts)   # normalised values
+    qmax = {O.E4M3: 448.0, O.E5M2: 57344.0}[qtype]
+    xv = np.abs(np.asarray(x, dtype=np.float64))
+    if x.dtype == np.uint16:
+        import synth
+        xv = np.abs(synth.bf16_to_f32(x).astype(np.float64))
+    if oaxis == O.COLS:
+        xv = xv.T
+    nvec, L = xv.shape
+    Lp = y.shape[1]
+    xp = np.zeros((nvec, Lp))
+    xp[:, :L] = xv
+    S = xp.reshape(nvec, Lp // block, block).sum(axis=2)               # [nvec, blocks]
+    Smax = S.max(axis=1, initial=0.0)
+    S_el = np.repeat(S, block, axis=1)                                  # per element
+    au = a * np.sqrt(block)                                             # unnormalised absmax
+    safe = np.where(au > 0, au, 1.0)
+    t = np.where(a[:, None] > 0, y / np.where(a > 0, a, 1.0)[:, None] * qmax, 0.0)
+    u = 2.0 ** -24
+    k = max(1, int(np.log2(block)))
+    g = k * u / (1 - k * u)
+    e = (g * S_el * qmax / safe[:, None] + np.abs(t) * (g * Smax / safe + 2 * u)[:, None]) * 1.01
+    return t, np.where(a[:, None] > 0, e, 0.0)
+
+
+def assert_fp8_codes_close_to_exact(gpu_q, x, oaxis, block, qtype, stochastic=False, opts=None):
+    """FP8 codes of fp32 input against the exact real code value t of the fp64 definition: the
+    decoded code lies within half a grid step (a whole step for stochastic rounding) plus the
+    fp32 rotation's error bound of t.  This is the code bar read for fp32 input: where the
+    fp32 butterflies' rounding (within the FWHT bar) spans more than a grid step -- near zero,
+    where the E5M2 subnormal spacing is 2^-16 code units -- the fp32 and fp64 decisions
+    legitimately differ by several steps."""
+    t, e = fp32_rotation_code_bound(x, oaxis, block, qtype, opts)
+    g = fp8_table(qtype)[np.asarray(gpu_q)]
+    step = fp8_step(np.abs(t) + e, qtype)
+    lim = (step if stochastic else step / 2) + e
+    bad = np.abs(g - t) > lim * (1 + 1e-12)
+    assert not bad.any(), f"{int(bad.sum())} codes beyond the fp32 bound of the exact value"
+
+
+def fp8_table(qtype):
+    return O.fp8_table(qtype)
+
+
+def assert_codes_close_to_fp64(gpu_q, ref_q, qtype, block, frac=1e-4, x=None, oaxis=None,
+                               opts=None):
     """Code bar against the fp64 oracle: |dq| <= 1 everywhere and at most
     `frac` of the elements off by one (grid steps for FP8).  The fraction applies to rotated
     data (block >= 16); with block < 16 a bf16 input keeps its 8-bit mantissa, so values
@@ -53,8 +121,17 @@ def assert_codes_close_to_fp64(gpu_q, ref_q, qtype, block, frac=1e-4):
     decisions legitimately split them -- there only the +-1 bound is checked.  Two flips are
     always allowed: on a few thousand codes one fp32-vs-fp64 split near a rounding midpoint is
     an ordinary event, not a sign of a wrong kernel (those are caught bit-exactly against the
-    fp32-decision oracle)."""
+    fp32-decision oracle).  With fp32 input x (axis oaxis, oracle options opts) and FP8 codes,
+    each code is held to the exact value within half a grid step plus the fp32 rotation's
+    error bound (assert_fp8_codes_close_to_exact) instead of one grid step, and every code that
+    differs from the fp64 decision counts once against the fraction."""
     d = code_distance(gpu_q, ref_q, qtype)
+    if x is not None and x.dtype == np.float32 and qtype in FP8_GRID:
+        # fp32 input, FP8 codes: each code against the exact value and the fp32 rotation's
+        # error bound instead of one grid step (see assert_fp8_codes_close_to_exact)
+        sr = bool(opts) and opts.get("rounding") == O.STOCHASTIC
+        assert_fp8_codes_close_to_exact(gpu_q, x, oaxis, block, qtype, sr, opts)
+        d = np.minimum(d, 1)
     assert d.max(initial=0) <= 1, f"code off by {d.max()}"
     if block >= 16:
         n1 = int((d == 1).sum())
@@ -85,7 +162,7 @@ def check_fq_parity(got_q, got_s, x, oaxis, block, qtype, vec_idx=None, **opts):
         assert err.max(initial=0) <= 1e-5
         scales_close_to_fp64(got_s, s64)
         return
-    assert_codes_close_to_fp64(got_q, r64, qtype, block)
+    assert_codes_close_to_fp64(got_q, r64, qtype, block, x=x, oaxis=oaxis, opts=opts)
     scales_close_to_fp64(got_s, s64)
 
 

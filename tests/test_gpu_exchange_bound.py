@@ -34,12 +34,13 @@ def _late_tasks(ws):
     return int(ws[:4].view(torch.int32).item())
 
 
-@pytest.mark.parametrize("qt", [O.I8, O.E4M3])
-def test_columns_pass_exact_when_tasks_stop_waiting(qt):
+@pytest.mark.parametrize("qt,io", [(O.I8, "bf16"), (O.E4M3, "bf16"), (O.I8, "f32")])
+def test_columns_pass_exact_when_tasks_stop_waiting(qt, io):
     # 48 tasks per 64-column strip, 6 strips: tasks 240-287 (strip 5) straddle the first wave
     rows, cols, b = 49152, 384, 256
     rng = np.random.default_rng(808)
-    x_np = synth.bf16_bits(synth.grads(rng, rows, cols))
+    g = synth.grads(rng, rows, cols)
+    x_np = synth.bf16_bits(g) if io == "bf16" else g.astype(np.float32)
     ref_q, ref_s = O.fwht_quant(x_np, O.COLS, b, qt, precision=32)
     x = to_dev(x_np)
     ws = torch.empty(H.fwht_quant_workspace_bytes(rows, cols, H.COLS, b), dtype=torch.uint8,

@@ -75,7 +75,7 @@ def test_rows_match_oracle(io, block, rows, cols, qtype):
     assert np.array_equal(q, r32), f"{int((q != r32).sum())} codes differ from the fp32 decision"
     assert np.array_equal(s, s32)
     r64, s64 = O.fwht_quant(x, O.ROWS, block, qtype, precision=64)
-    assert_codes_close_to_fp64(q, r64, qtype, block)
+    assert_codes_close_to_fp64(q, r64, qtype, block, x=x, oaxis=O.ROWS)
     np.testing.assert_allclose(s, s64, rtol=1e-5)
 
 
@@ -104,6 +104,20 @@ COL_CASES = [
     ("bf16", 256, 768, 64, O.I8),         # 256-row parts, 3 per strip
     ("bf16", 256, 2048, 96, O.E4M3),      # whole 2048-row columns, 32-column strips
     ("bf16", 128, 8192, 200, O.I8),       # 8 parts per strip, partial last strip
+    # fp32 input: the same tiles through the LDS in two rounds (the rows whose offset bit
+    # log2(max(block, 64)) - 1 is 0, then 1), every element read once
+    ("f32", 256, 4096, 64, O.I8),         # whole 4096-row columns, 16-column strips
+    ("f32", 256, 4096, 520, O.E4M3),      # partial last strip
+    ("f32", 1, 64, 16, O.I8),             # 64-row tiles of 1024 columns
+    ("f32", 8, 64, 16, O.E4M3),
+    ("f32", 32, 128, 24, O.E5M2),
+    ("f32", 64, 192, 24, O.E5M2),         # 64-row parts, 3 per strip
+    ("f32", 1024, 2048, 16, O.I8),
+    ("f32", 4096, 4096, 8, O.E4M3),       # one block per column
+    ("f32", 4096, 8192, 8, O.I8),         # 2 parts per strip
+    ("f32", 128, 8192, 72, O.E4M3),       # 8 parts per strip
+    ("f32", 512, 512, 136, O.F64),        # the rotated values themselves
+    ("f32", 256, 768, 64, O.I8),          # 256-row parts, 3 per strip
 ]
 
 
@@ -116,7 +130,7 @@ def test_cols_match_oracle(io, block, rows, cols, qtype):
     assert np.array_equal(q, r32), f"{int((q != r32).sum())} codes differ from the fp32 decision"
     assert np.array_equal(s, s32)
     r64, s64 = O.fwht_quant(x, O.COLS, block, qtype, precision=64)
-    assert_codes_close_to_fp64(q, r64, qtype, block)
+    assert_codes_close_to_fp64(q, r64, qtype, block, x=x, oaxis=O.COLS)
     np.testing.assert_allclose(s, s64, rtol=1e-5)
 
 

@@ -60,12 +60,17 @@ def _bf16(rows, cols, seed, kind="act"):
     return to_dev(synth.bf16_bits(a))
 
 
-@pytest.mark.parametrize("axis,rows,cols,block", [(H.ROWS, 96, 4096, 256),
-                                                  (H.ROWS, 40, 11008, 128),
-                                                  (H.COLS, 4096, 200, 256),
-                                                  (H.COLS, 8192, 136, 128)])
-def test_rotation_pass_guards(axis, rows, cols, block):
-    x = _bf16(rows, cols, seed=rows + cols, kind="grad")
+@pytest.mark.parametrize("axis,rows,cols,block,io", [(H.ROWS, 96, 4096, 256, "bf16"),
+                                                     (H.ROWS, 40, 11008, 128, "bf16"),
+                                                     (H.COLS, 4096, 200, 256, "bf16"),
+                                                     (H.COLS, 8192, 136, 128, "bf16"),
+                                                     (H.COLS, 4096, 200, 256, "f32"),
+                                                     (H.COLS, 8192, 136, 128, "f32")])
+def test_rotation_pass_guards(axis, rows, cols, block, io):
+    if io == "bf16":
+        x = _bf16(rows, cols, seed=rows + cols, kind="grad")
+    else:
+        x = to_dev(synth.grads(np.random.default_rng(rows + cols), rows, cols).astype(np.float32))
     nvec, L = (rows, cols) if axis == H.ROWS else (cols, rows)
     lp = H.padded_len(L, block)
     ref_q, ref_s = H.fwht_quant(x, axis=axis, block=block)

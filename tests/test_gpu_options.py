@@ -54,7 +54,10 @@ ROT_CASES = [
     ("cols", "bf16", 512, 3000, 40, "e4m3", False, True, None),    # padded 3072, 3 parts
     ("cols", "bf16", 4096, 5000, 16, "e4m3", True, True, None),    # padded 8192, 2 parts
     ("cols", "bf16", 256, 4096, 64, "i8", True, False, None),      # signs only
-    ("cols", "f32", 256, 700, 24, "i8", True, True, None),         # fp32: two-read kernel
+    ("cols", "f32", 256, 700, 24, "i8", True, True, None),         # fp32 SR: two-read kernel
+    ("cols", "f32", 256, 4096, 64, "i8", True, False, None),       # fp32: single read, signs
+    ("cols", "f32", 128, 5000, 72, "e5m2", True, False, None),     # fp32: padded 5120, 5 parts
+    ("cols", "f32", 4096, 5000, 16, "e4m3", False, False, None),   # fp32: padded 8192, 2 parts
     ("cols", "bf16", 16, 13, 64, "i8", True, True, None),          # 13 rows padded to 16
     ("cols", "bf16", 256, 2000, 64, "e5m2", True, True, False),    # no scratch: two-read kernel
 ]
@@ -82,7 +85,7 @@ def test_rotation_options_match_oracle(axis, io, block, rows, cols, q, signs, sr
     assert np.array_equal(got, r32), f"{int((got != r32).sum())} codes differ from the fp32 path"
     assert np.array_equal(gs, s32)
     r64, s64 = O.fwht_quant(x, ax_o, block, qt, precision=64, **ok)
-    assert_codes_close_to_fp64(got, r64, qt, block)
+    assert_codes_close_to_fp64(got, r64, qt, block, x=x, oaxis=ax_o, opts=ok)
     np.testing.assert_allclose(gs, s64, rtol=1e-5)
 
 
