@@ -75,6 +75,7 @@ LARGE_BYTES = 16384 * 14336 * 3 + 4 * 16384
 LARGE_COLS_BYTES = 16384 * 14336 * 3 + 4 * 14336
 FQ_PAD_BYTES = M * K_PAD * 2 + M * K + 4 * M
 DUAL_BYTES = M * N * 2 + 2 * M * N + 4 * (M + N)  # one bf16 read, two code matrices, scales
+FQ_F32_BYTES = M * K * (4 + 1) + 4 * K       # fp32 columns in, one code byte out, scales
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic_4096.json")
 
 # kernel-name patterns of each measured pass (rocprofv3 Kernel_Name substrings; a pass may
@@ -85,14 +86,15 @@ GEMM_GRID = 256 * 512
 PASSES = {
     "gemm_i8_4096": (["halo::gemm_kernel<0"], GEMM_GRID),
     "fq_rows_4096": (["halo::fq_rows2_kernel<unsigned short, 256, 0, false>"], None),
-    "fq_cols_4096": (["halo::fq_cols2_kernel<256, 0, false, false>"], None),
+    "fq_cols_4096": (["halo::fq_cols2_kernel<256, 0, false, false, false>"], None),
     "gemm_fp8_4096": (["halo::gemm_kernel<1"], GEMM_GRID),
     "fq_rows_opt_4096": (["halo::fq_rows2_kernel<unsigned short, 256, 0, true>"], None),
-    "fq_cols_opt_4096": (["halo::fq_cols2_kernel<256, 0, true, false>"], None),
+    "fq_cols_opt_4096": (["halo::fq_cols2_kernel<256, 0, true, false, false>"], None),
     "copy_neg": (["neg_kernel"], None),  # 64 MiB calibration, or the 512 MiB copy reference
     "fq_batch_4096": (["halo::fq_batch_kernel<256, 0, 0, false, false>"], None),
     "gemm_i8_pair_4096": (["halo::gemm_kernel<0"], 2 * GEMM_GRID),
     "fq_dual_4096": (["fq_dual_kernel<256, 0, false, false>"], None),
+    "fq_cols_f32_4096": (["halo::fq_cols2_kernel<256, 0, false, false, true>"], None),
 }
 
 
@@ -397,6 +399,9 @@ def measure_kernels(H, torch, sets, iters, with_copy=False):
     cols_opt = _c_launcher(H, fq, [fq_args(t, H.COLS, sr_opts(i), wsc)
                                    for i, t in enumerate(mats)])
     rows_pad = _c_launcher(H, fq, [fq_args(Xp, H.ROWS) for Xp in padded])
+    # the columns pass on fp32 input: 9 of the matrices in fp32 (604 MB cycled)
+    mats32 = [t.float() for t in mats[:9]]
+    cols_f32 = _c_launcher(H, fq, [fq_args(t, H.COLS, ws=wsc) for t in mats32])
 
     # both passes of a matrix from one read (halo_fwht_quant_dual), beside the rows and the
     # columns pass above on the same matrices
@@ -447,7 +452,8 @@ def measure_kernels(H, torch, sets, iters, with_copy=False):
 
     legs = {"gemm_i8_4096": gemm, "gemm_fp8_4096": gemm_fp8, "fq_rows_4096": rows,
             "fq_cols_4096": cols, "fq_rows_opt_4096": rows_opt, "fq_cols_opt_4096": cols_opt,
-            "fq_rows_pad_4000": rows_pad, "linear_bwd_4096": bwd, "fq_dual_4096": dual}
+            "fq_rows_pad_4000": rows_pad, "linear_bwd_4096": bwd, "fq_dual_4096": dual,
+            "fq_cols_f32_4096": cols_f32}
     if with_copy:
         # the padded rows pass shares the rows kernel and its grid: kept out of the counter
         # runs, whose per-pass averages would mix its smaller reads in
@@ -643,7 +649,7 @@ def summarize_pmc(fetch_dir, write_dir, command):
     algo = {"gemm_i8_4096": GEMM_BYTES, "gemm_fp8_4096": GEMM_BYTES, "fq_rows_4096": FQ_BYTES,
             "fq_cols_4096": FQ_BYTES, "fq_rows_opt_4096": FQ_BYTES, "fq_cols_opt_4096": FQ_BYTES,
             "fq_batch_4096": 4 * FQ_BYTES, "gemm_i8_pair_4096": 2 * GEMM_BYTES,
-            "fq_dual_4096": DUAL_BYTES}
+            "fq_dual_4096": DUAL_BYTES, "fq_cols_f32_4096": FQ_F32_BYTES}
     res = {"kernel_source_hash": source_hash(KERNEL_SOURCES), "command": command,
            "fetch_scale": f_scale, "write_scale": w_scale, "bytes_per_launch": {},
            "fetch_kib_raw": fetch, "write_kib_raw": write}
@@ -972,7 +978,11 @@ def main():
                            "what": "halo_fwht_quant_dual: the rows and the columns codes of one "
                                    "4096 x 4096 bf16 matrix from a single read (algorithmic: "
                                    "one read, both code matrices and scales), beside the rows "
-                                   "pass plus the columns pass"}},
+                                   "pass plus the columns pass"},
+                       "cols_f32": hbm_pass("fq_cols_f32_4096", FQ_F32_BYTES) | {
+                           "what": "the columns pass on fp32 input (4 B read + 1 B code per "
+                                   "element): the same single-read tasks, the tile staged "
+                                   "through the LDS in two rounds"}},
         "gemm_fp8": {"bound": "mfma", "achieved": round(GEMM_OPS / (t["gemm_fp8_4096"] * 1e-3) / 1e12, 2),
                      "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(GEMM_OPS / (t["gemm_fp8_4096"] * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),

@@ -51,20 +51,23 @@ def test_summarize_pmc_calibrates_and_sums_each_pass(tmp_path):
     # (scale 1); the GEMM pass has two dispatches per call averaged; the columns pass is its
     # one kernel, not the scratch fill (cols[0]) that longer column passes launch
     gemm = "void halo::gemm_kernel<0, 0, 0, 2, false, 128, 4>(halo::GemmPair)"
+    # (the fp32-input instantiation of the same kernel is its own pass)
     cols = ["void halo::fill_zero_kernel(float*, long)",
-            "void halo::fq_cols2_kernel<256, 0, false, false>(halo::ColsProb, halo::ColsProb, long, long)"]
+            "void halo::fq_cols2_kernel<256, 0, false, false, false>(halo::ColsProb, halo::ColsProb, long, long)",
+            "void halo::fq_cols2_kernel<256, 0, false, false, true>(halo::ColsProb, halo::ColsProb, long, long)"]
     neg = "void at::native::neg_kernel_impl"
     _counter_csv(tmp_path / "f", "FETCH_SIZE",
                  [(gemm, 1000.0), (gemm, 3000.0), (cols[0], 1.0), (cols[1], 99.0),
-                  (neg, 32768.0)])
+                  (cols[2], 7.0), (neg, 32768.0)])
     _counter_csv(tmp_path / "w", "WRITE_SIZE",
                  [(gemm, 500.0), (gemm, 500.0), (cols[0], 2.0), (cols[1], 48.0),
-                  (neg, 65536.0)])
+                  (cols[2], 5.0), (neg, 65536.0)])
     res, text = bench.summarize_pmc(str(tmp_path / "f"), str(tmp_path / "w"), "cmd")
     assert res["fetch_scale"] == pytest.approx(2.0) and res["write_scale"] == pytest.approx(1.0)
     b = res["bytes_per_launch"]
     assert b["gemm_i8_4096"] == int(round(2000.0 * 1024 * 2 + 500.0 * 1024))
     assert b["fq_cols_4096"] == int(round(99.0 * 1024 * 2 + 48.0 * 1024))
+    assert b["fq_cols_f32_4096"] == int(round(7.0 * 1024 * 2 + 5.0 * 1024))
     assert "fq_rows_4096" not in b  # no counters for it: left out, never zero
     assert res["kernel_source_hash"] == bench.source_hash(bench.KERNEL_SOURCES)
     assert text.startswith("command: cmd")
