@@ -27,7 +27,8 @@
 // consecutive rows of 8 adjacent columns, transposes them in registers with v_perm_b32 (8 rows
 // of one column in one 16-byte word) and writes them to LDS in the order the compute waves
 // read them (bank-conflict-free by an XOR swizzle); the waves then run the slice computation
-// on column segments of R rows.  When a column is longer than R, the P = rows / R workgroups
+// on column segments of R rows.  fp32 input keeps the tile's geometry and passes it through
+// the LDS in two rounds of half the rows each (see cols_load_f32).  When a column is longer than R, the P = rows / R workgroups
 // of one column strip combine their partial maxima through device-scope atomics: each
 // max-reduces its maxima into the strip's column maxima, increments the strip's arrival
 // counter, and waits until all P have arrived.  The tasks of a group of up to 8 strips are
