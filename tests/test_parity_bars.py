@@ -47,3 +47,28 @@ def test_fp32_input_fp8_bar_rejects_moved_codes(qt, steps):
         with pytest.raises(AssertionError):
             P.assert_codes_close_to_fp64(bad.reshape(q32.shape), q64, qt, 256, x=x,
                                          oaxis=O.COLS, opts=opts)
+
+
+def test_ties_repeated_by_padding_do_not_count():
+    # 16 bf16 rows padded to one block of 4096: each rotated column holds 16 distinct values,
+    # each 256 times.  Three of them are exact ties (t = k + 1/2) that the fp32 decision
+    # (m = fl32(127 / a)) rounds away from even: 768 codes differ from fp64, 0.15 %, all
+    # undecidable in fp32.  The bar accepts them; a moved code elsewhere still fails.
+    rng = np.random.default_rng(5617)
+    x = synth.bf16_bits(synth.activations(rng, 16, 128))
+    q32, _ = O.fwht_quant(x, O.COLS, 4096, O.I8, precision=32)
+    q64, _ = O.fwht_quant(x, O.COLS, 4096, O.I8, precision=64)
+    d = P.code_distance(q32, q64, O.I8)
+    t, e = P.fp32_rotation_code_bound(x, O.COLS, 4096, O.I8)
+    und = P.undecidable_in_fp32(t, e, O.I8)
+    assert (d == 1).sum() > 1e-4 * d.size and (d[~und] == 0).all()
+    assert np.all(np.abs(t[d == 1] - np.floor(t[d == 1]) - 0.5) == 0.0)  # exact ties
+    P.assert_codes_close_to_fp64(q32, q64, O.I8, 4096, x=x, oaxis=O.COLS)
+    with pytest.raises(AssertionError):  # the plain fraction rejects them
+        P.assert_codes_close_to_fp64(q32, q64, O.I8, 4096)
+    bad = q32.copy()
+    far = np.argwhere(~und & (np.abs(t) < 120))
+    for i, j in far[:60]:            # 60 decidable codes moved by one: over the 52 allowed
+        bad[i, j] += 1
+    with pytest.raises(AssertionError):
+        P.assert_codes_close_to_fp64(bad, q64, O.I8, 4096, x=x, oaxis=O.COLS)
