@@ -64,6 +64,7 @@ ROW_CASES = [
     ("bf16", 4096, 2, 65536, O.E5M2),      # sixteen waves: the longest row
     ("f32", 512, 2, 20480, O.I8),          # fp32, five waves per row
     ("bf16", 128, 2, 16448, O.E4M3),       # padded to 16512: a partial last wave
+    ("bf16", 4096, 64, 16, O.I8),          # 16 columns padded to one block of 4096
 ]
 
 
@@ -118,6 +119,9 @@ COL_CASES = [
     ("f32", 128, 8192, 72, O.E4M3),       # 8 parts per strip
     ("f32", 512, 512, 136, O.F64),        # the rotated values themselves
     ("f32", 256, 768, 64, O.I8),          # 256-row parts, 3 per strip
+    # 16 rows padded to one block of 4096: 16 distinct rotated values per column, each 256
+    # times, so one exact tie repeats across 256 codes
+    ("bf16", 4096, 16, 128, O.I8),
 ]
 
 
@@ -125,7 +129,7 @@ COL_CASES = [
 def test_cols_match_oracle(io, block, rows, cols, qtype):
     x = _input(rows, cols, io, seed=rows * 5 + cols, kind="grad")
     q, s = _run(x, H.COLS, block, qtype)
-    assert q.shape == (cols, rows)
+    assert q.shape == (cols, O.padded_len(rows, block))
     r32, s32 = O.fwht_quant(x, O.COLS, block, qtype, precision=32)
     assert np.array_equal(q, r32), f"{int((q != r32).sum())} codes differ from the fp32 decision"
     assert np.array_equal(s, s32)
