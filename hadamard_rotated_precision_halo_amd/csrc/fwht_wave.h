@@ -306,14 +306,9 @@ __device__ __forceinline__ void load_slice(const FqArgs& a, const Tin* vp, int64
   }
 }
 
-// Quantisation multiplier and stored scale from the vector's absmax.
-template <int QT>
-__device__ __forceinline__ float quant_mul(const FqArgs& a, float mx) {
-  if constexpr (QT == 3) return a.inv_sqrt_b;
-  else return mx > 0.f ? a.qmax / mx : 0.f;
-}
-// The same for the lane's 64 values v of a vector: a vector of tiny values has them scaled
-// first (code_mul).
+// Quantisation multiplier from the vector's absmax, for the lane's 64 values v of a vector
+// (the rotated values' 1/sqrt(block) in the fp32 value mode): a vector of tiny values has them
+// scaled first (code_mul).
 template <int QT>
 __device__ __forceinline__ float quant_mul_v(const FqArgs& a, float mx, float* v) {
   if constexpr (QT == 3) {

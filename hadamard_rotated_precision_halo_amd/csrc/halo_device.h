@@ -217,10 +217,4 @@ __device__ __forceinline__ float sr_value(float t, uint32_t w, float qmax) {
   return (fl + up) * s;
 }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs).
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
-
 }  // namespace halo

@@ -229,12 +229,6 @@ def rel_fro(a, b):
     return np.linalg.norm(a - b) / (den if den > 0 else 1.0)
 
 
-def bf16_round_np(x):
-    """fp64 -> nearest-even bf16 value (through fp32), as float64."""
-    import synth
-    return synth.bf16_to_f32(synth.bf16_bits(np.asarray(x, dtype=np.float32))).astype(np.float64)
-
-
 # Philox key and counter words 2-3 of the stochastic-rounding tests, as the oracle takes them
 # and as the binding's 64-bit seed / counter
 KEY, CTR = (0x3C6EF372, 0xA54FF53A), (0x510E527F, 0x9B05688C)
