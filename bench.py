@@ -700,6 +700,85 @@ def measure_large_passes(H, torch, iters):
     return out
 
 
+def workload_passes(cfg):
+    """The rotation passes and products of one workload: rotation passes (name, source, axis,
+    code key) and products (name, pass giving a, pass giving b)."""
+    fq, products = [], []
+    if cfg["fwd"]:
+        fq += [("x_rows", "x", 0, "q"), ("w_rows", "w", 0, "q")]
+        products += [("y", "x_rows", "w_rows")]
+    if cfg["bwd"]:
+        fq += [("dy_rows", "dy", 0, "gq"), ("w_cols", "w", 1, "q"), ("dy_cols", "dy", 1, "gq"),
+               ("x_cols", "x", 1, "q")]
+        products += [("dx", "dy_rows", "w_cols"), ("dw", "dy_cols", "x_cols")]
+    return fq, products
+
+
+def workload_per_pass(H, torch, cfg, host, dev_src, iters=20):
+    """Each pass of a workload alone, on the GPU (HIP events over `iters` back-to-back calls
+    through the binding, outputs preallocated) and by the oracle on the host cores: rotation
+    passes at full size, products on the first 256 rows of their a operand with the oracle's
+    own codes, scaled linearly by rows ("extrapolated").  Returns the cpu_baseline object."""
+    import oracle as O
+    b = cfg["block"]
+    tq = {"i8": torch.int8, "e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
+    oq = {"i8": O.I8, "e4m3": O.E4M3, "e5m2": O.E5M2}
+    fq, products = workload_passes(cfg)
+    passes, gpu_codes, cpu_codes = {}, {}, {}
+    for pname, src, axis, key in fq:
+        x = dev_src[src]
+        rows, cols = x.shape
+        nvec, L = (rows, cols) if axis == 0 else (cols, rows)
+        q = torch.empty((nvec, H.padded_len(L, b)), dtype=tq[cfg[key]], device="cuda:0")
+        sc = torch.empty(nvec, dtype=torch.float32, device="cuda:0")
+        need = H.fwht_quant_workspace_bytes(rows, cols, axis, b, x.dtype)
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda:0") if need else False
+
+        def call(i, x=x, axis=axis, key=key, q=q, sc=sc, ws=ws):
+            H.fwht_quant(x, axis=axis, block=b, q_dtype=tq[cfg[key]], q=q, scale=sc,
+                         workspace=ws)
+        for i in range(3):
+            call(i)
+        g_ms = time_events(call, iters, torch)
+        gpu_codes[pname] = (q, sc, cfg[key])
+        t0 = time.perf_counter()
+        cpu_codes[pname] = O.fwht_quant(host[src], axis, b, oq[cfg[key]])
+        c_ms = (time.perf_counter() - t0) * 1e3
+        passes[pname] = {"gpu_ms": round(g_ms, 4), "cpu_ms": round(c_ms, 1),
+                         "ratio": round(c_ms / g_ms, 1), "extrapolated": False}
+    for pname, pa, pb in products:
+        qa, sa, ka = gpu_codes[pa]
+        qb, sb, kb = gpu_codes[pb]
+        c = torch.empty((qa.shape[0], qb.shape[0]), dtype=torch.bfloat16, device="cuda:0")
+
+        def call(i, qa=qa, sa=sa, qb=qb, sb=sb, c=c, ka=ka):
+            if ka == "i8":
+                H.gemm_i8(qa, sa, qb, sb, c=c)
+            else:
+                H.gemm_fp8(qa, sa, qb, sb, c=c)
+        for i in range(3):
+            call(i)
+        g_ms = time_events(call, iters, torch)
+        (ca, csa), (cb, csb) = cpu_codes[pa], cpu_codes[pb]
+        rows = min(256, ca.shape[0])
+        t0 = time.perf_counter()
+        if ka == "i8":
+            acc = O.gemm_i8(ca[:rows], cb).astype(np.float64)
+        else:
+            acc = O.gemm_fp8(ca[:rows], oq[ka], cb, oq[kb])
+        O.dequant(acc, csa[:rows], csb)
+        c_ms = (time.perf_counter() - t0) * 1e3 * ca.shape[0] / rows
+        passes[pname] = {"gpu_ms": round(g_ms, 4), "cpu_ms": round(c_ms, 1),
+                         "ratio": round(c_ms / g_ms, 1), "extrapolated": rows < ca.shape[0]}
+    return {"kind": "oracle", "unit": "ms", "cores": O.num_threads(), "cpu_model": cpu_model(),
+            "passes": passes,
+            "sample": "each rotation pass at full size; each product on the first 256 rows of "
+                      "its a operand (the oracle's own codes), scaled by rows where marked "
+                      "extrapolated; GPU: the same pass alone, HIP events over back-to-back calls "
+                      "on one input (operands under 256 MB may stay in the Infinity Cache, so "
+                      "these are warm-cache GPU times, unlike the headline line's legs)"}
+
+
 def bench_workload(name, args):
     """One named workload (fwd and / or bwd, as its configuration lists) on the inputs of the
     full-size parity tests (same seeded generator): one JSON line with times and rates.  These
@@ -723,7 +802,7 @@ def bench_workload(name, args):
 
     X, W = dev(x), dev(w)
     DY = dev(dy) if cfg["bwd"] else None
-    del x, w, dy
+    host = {"x": x, "w": w, "dy": dy}
     io = torch.float32 if cfg["io"] == synth.F32 else torch.bfloat16
     out = {"metric": "HALO linear effective TOP/s", "unit": "TOP/s", "workload": name,
            "m": m, "n": n, "k": k, "block": b, "codes": [cfg["q"], cfg["gq"]],
@@ -758,6 +837,10 @@ def bench_workload(name, args):
         total_ms, total_gop = total_ms + ms, total_gop + 2 * gop
     out["ms_per_step"] = round(total_ms, 4)
     out["value"] = round(total_gop / total_ms, 1)  # GOP per ms = TOP/s
+    if not args.no_cpu_baseline:
+        print(f"{name}: each pass alone, GPU and oracle", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = workload_per_pass(H, torch, cfg, host,
+                                                {"x": X, "w": W, "dy": DY})
     print(json.dumps(out), flush=True)
 
 

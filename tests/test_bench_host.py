@@ -121,3 +121,16 @@ def test_summarize_counters_means_and_derived(tmp_path):
     means = bench._counter_means(str(d))
     assert means["gemm_i8_4096"]["SQ_VALU_MFMA_BUSY_CYCLES"] == pytest.approx(200.0 * 1024)
     assert means["gemm_i8_pair_4096"]["SQ_VALU_MFMA_BUSY_CYCLES"] == pytest.approx(9e9)
+
+
+def test_workload_passes_follow_the_configuration():
+    import synth
+    fq, prods = bench.workload_passes(synth.WORKLOADS["c4_fwdbwd_8192x4096x11008_bf16_b128_i8"])
+    assert [p[0] for p in fq] == ["x_rows", "w_rows", "dy_rows", "w_cols", "dy_cols", "x_cols"]
+    assert prods == [("y", "x_rows", "w_rows"), ("dx", "dy_rows", "w_cols"),
+                     ("dw", "dy_cols", "x_cols")]
+    # every product's operands come from passes along the same contraction dimension
+    axis_src = {p[0]: (p[1], p[2]) for p in fq}
+    assert axis_src["dy_cols"] == ("dy", 1) and axis_src["x_cols"] == ("x", 1)
+    fq, prods = bench.workload_passes(synth.WORKLOADS["c1_fwd_256x1024x1024_f32_b1024_i8"])
+    assert len(fq) == 2 and prods == [("y", "x_rows", "w_rows")]
