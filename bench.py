@@ -1039,8 +1039,10 @@ def main():
                          "achieved": i8_sustained, "unit": "TFLOP/s",
                          "frac": round(gemm_tops / i8_sustained, 4),
                          "what": "v_mfma_i32_32x32x32_i8 alone on the whole device under a "
-                                 "sustained load (halo_mfma_rate_probe): the rate the chip's "
-                                 "clock allows this instruction; frac = the product's rate "
+                                 "sustained load, on operands drawn like the product's codes, "
+                                 "a different fragment pair for every MFMA "
+                                 "(halo_mfma_rate_probe): the rate the chip's clock allows "
+                                 "this instruction on such data; frac = the product's rate "
                                  "over it"},
                      "in_path": {"ms_per_launch": round(t_gemm_path, 5),
                                  "frac": round(GEMM_OPS / (t_gemm_path * 1e-3) / 1e12

@@ -355,7 +355,10 @@ halo_status halo_fwht_quant_dual(const void* x, halo_dtype x_type, int64_t rows,
  *          on E4M3 operands (the FP8 product's), 2: v_mfma_scale_f32_16x16x128_f8f6f4 on E4M3
  *          operands.
  *   iters  MFMA groups per wave, in [2, 1 << 20] (rounded up to even); one group is 8
- *          independent MFMAs (16 for kind 2), on operands that change every group.
+ *          independent MFMAs (16 for kind 2), one per (a, b) fragment pair of a product's
+ *          wave tile, so every MFMA takes a different operand pair; the operands are codes
+ *          drawn like the products' (rotated, absmax-scaled data), since how much their bits
+ *          toggle sets the clock the chip holds.
  *   ops    receives the operations (2 x multiply-adds) the launch performs.
  * One launch of 256 workgroups of 512 threads (two waves per SIMD, as the products run) on
  * the stream; it reads and writes no caller memory.  Time it with events on that stream.
