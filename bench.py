@@ -539,9 +539,23 @@ def summarize_stats(path, command, last=0):
                      f"{float(r['MinNs']) / 1e3:>9.2f} {float(r['MaxNs']) / 1e3:>9.2f} "
                      f"{float(r['Percentage']):>6.2f}  {r['Name'][:150]}")
     trace = path.replace("kernel_stats.csv", "kernel_trace.csv")
-    if last and os.path.exists(trace):
+    if os.path.exists(trace):
+        # one kernel serves launches of different sizes (a product and the backward's paired
+        # products, rotation passes of different shapes): split each kernel by launch grid
         with open(trace) as f:
             tr = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
+        by = {}
+        for r in tr:
+            grid = int(r["Grid_Size_X"]) if r.get("Grid_Size_X") else 0
+            wg = int(r["Workgroup_Size_X"]) if r.get("Workgroup_Size_X") else 0
+            d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            by.setdefault((r["Kernel_Name"], grid, wg), []).append(d)
+        lines += ["", "by kernel and launch grid (from the trace):",
+                  f"{'calls':>6} {'avg us':>9} {'min us':>9} {'max us':>9} {'workgroups':>10}  kernel"]
+        for (name, grid, wg), v in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+            lines.append(f"{len(v):>6} {float(np.mean(v)):>9.2f} {min(v):>9.2f} {max(v):>9.2f} "
+                         f"{grid // wg if wg else 0:>10}  {name[:120]}")
+    if last and os.path.exists(trace):
         lines += ["", f"per pass, last {last} calls (the event-timed measurement loop):"]
         for key in PASSES:
             calls = {}
