@@ -213,16 +213,25 @@ class ClockSampler:
                 "source": self.sclk_path}
 
 
-def settle(step, seconds, torch):
+def settle(step, seconds, torch, sampler=None):
     """Run steps until `seconds` have passed (in groups of 10, synchronised): the clock-settle
-    phase before the counted warmup.  Returns (steps run, seconds)."""
+    phase before the counted warmup.  With a ClockSampler, the shader clock and board power
+    are sampled over the phase's second half, the steady state of the same steps (sampling
+    sysfs while steps run slows them by about 2 %, so the counted steps run unsampled).
+    Returns (steps run, seconds)."""
     t0 = time.perf_counter()
     n = 0
+    started = False
     while time.perf_counter() - t0 < seconds:
+        if sampler is not None and not started and time.perf_counter() - t0 >= seconds / 2:
+            sampler.__enter__()
+            started = True
         for _ in range(10):
             step(n)
             n += 1
         torch.cuda.synchronize()
+    if started:
+        sampler.__exit__(None, None, None)
     return n, time.perf_counter() - t0
 
 
@@ -943,20 +952,20 @@ def main():
         H.linear_fwd(X, W, BLOCK, y=y, workspace=ws_f)
         H.linear_bwd(DY, X, W, BLOCK, dx=dx, dw=dw, workspace=ws_b)
 
-    settle_steps, settle_s = settle(step, args.settle_s, torch)
+    clk = ClockSampler()
+    settle_steps, settle_s = settle(step, args.settle_s, torch, sampler=clk)
     for i in range(args.warmup):
         step(i)
     st = torch.cuda.current_stream()
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    with ClockSampler() as clk:
-        t0 = time.perf_counter()
-        for i in range(args.steps):
-            evs[i].record(st)
-            step(i)
-        evs[-1].record(st)
-        torch.cuda.synchronize()
-        elapsed = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        evs[i].record(st)
+        step(i)
+    evs[-1].record(st)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
     ms_step = elapsed * 1e3 / args.steps
     value = STEP_GOP / (ms_step * 1e-3) / 1e3  # TOP/s
     per_step = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
@@ -1041,7 +1050,11 @@ def main():
                     "p90": round(float(np.percentile(per_step, 90)), 4)},
         "settle": {"steps": settle_steps, "s": round(settle_s, 2),
                    "what": "steps run before the counted warmup, until the clock settles"},
-        "clock": {"timed_steps": clk.summary(), "kernel_legs": clk_k.summary()},
+        "clock": {"steps": clk.summary() | {
+                      "what": "sampled every 10 ms over the second half of the clock-settle "
+                              "phase: the same steps in steady state (the counted steps run "
+                              "unsampled: sampling slows them by about 2 %)"},
+                  "kernel_legs": clk_k.summary()},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 2), "peak": PEAK_INT8_TOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
                      "traffic": load_traffic("gemm_i8_4096"),
