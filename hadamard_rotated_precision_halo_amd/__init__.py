@@ -145,6 +145,60 @@ def _ld(t):
     return t.stride(0)
 
 
+def _require(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _matrix(t, name, shape, dtype=None, contiguous=False):
+    """A 2-D matrix argument of exactly `shape` (and `dtype`): row-major with unit column stride
+    and a row stride of at least its width, or contiguous for the layer calls, which take no
+    leading dimension.  The kernels trust the shapes the call passes: a tensor smaller than
+    that would be read or written past its end."""
+    _require(isinstance(t, torch.Tensor) and t.dim() == 2, f"{name} must be a 2-D tensor")
+    _require(tuple(t.shape) == tuple(shape),
+             f"{name} has shape {tuple(t.shape)}, the call needs {tuple(shape)}")
+    if dtype is not None:
+        _require(t.dtype == dtype, f"{name} has dtype {t.dtype}, the call needs {dtype}")
+    if contiguous:
+        _require(t.is_contiguous(), f"{name} must be contiguous (row-major, no row padding)")
+    elif t.numel() > 0:
+        _require(t.stride(1) == 1 and t.stride(0) >= t.shape[1],
+                 f"{name} must be row-major with unit column stride")
+
+
+def _vector(t, name, n, dtype):
+    """A contiguous 1-D argument of at least n entries of dtype."""
+    _require(isinstance(t, torch.Tensor) and t.dim() == 1 and t.dtype == dtype
+             and t.is_contiguous() and t.numel() >= n,
+             f"{name} must be a contiguous 1-D {dtype} tensor of at least {n} entries")
+
+
+def _bytes(t, name):
+    """A workspace: a contiguous 1-D uint8 tensor (its size is checked by the library)."""
+    _require(isinstance(t, torch.Tensor) and t.dim() == 1 and t.dtype == torch.uint8
+             and t.is_contiguous(), f"{name} must be a contiguous 1-D uint8 tensor")
+
+
+def _same_gpu(ref, **tensors):
+    """The reference input on a GPU and every other tensor argument on the same device."""
+    _require(isinstance(ref, torch.Tensor) and ref.is_cuda, "the inputs must be GPU tensors")
+    for name, t in tensors.items():
+        if t is not None:
+            _require(t.device == ref.device, f"{name} is on {t.device}, the inputs on {ref.device}")
+
+
+def _sign_words(length):
+    return -(-int(length) // 32)
+
+
+def contraction_len(dim, block):
+    """Contraction length of a layer product: the dimension padded with zeros to a multiple of
+    the block and of 32; a layer call's sign array covers this length."""
+    step = max(int(block), 32)
+    return -(-int(dim) // step) * step
+
+
 def padded_len(length, block):
     """Rotated length of a vector of `length` elements: rounded up to a multiple of block
     (the zero padding)."""
@@ -201,12 +255,22 @@ def fwht_quant(x, axis=ROWS, block=256, q_dtype=torch.int8, q=None, scale=None, 
     before it stops waiting (the strip is then stored by a follow-up launch, with the same
     codes); 0 = the library's default.
     """
+    _require(isinstance(x, torch.Tensor) and x.dim() == 2, "x must be a 2-D tensor")
     rows, cols = x.shape
     nvec, L = (rows, cols) if axis == ROWS else (cols, rows)
+    Lp = padded_len(L, block)
     if q is None:
-        q = torch.empty((nvec, padded_len(L, block)), dtype=q_dtype, device=x.device)
+        q = torch.empty((nvec, Lp), dtype=q_dtype, device=x.device)
+    _matrix(q, "q", (nvec, Lp))
     if scale is None:
         scale = torch.empty(nvec, dtype=torch.float32, device=x.device)
+    _vector(scale, "scale", nvec, torch.float32)
+    if signs is not None:
+        _vector(signs, "signs", _sign_words(Lp), torch.int32)
+    if workspace is not None and workspace is not False:
+        _bytes(workspace, "workspace")
+    _same_gpu(x, q=q, scale=scale, signs=signs,
+              workspace=workspace if workspace is not False else None)
     if workspace is False:
         ws_ptr, ws_bytes = None, 0
     else:
@@ -250,6 +314,7 @@ def fwht_quant_dual(x, block=256, q_dtype=torch.int8, qr=None, scale_r=None, qc=
     / the rows of a column); `rounding`, `seed`, the counters and `exchange_polls` as in
     fwht_quant (the counter of each pass its own).  `workspace`: the scratch, allocated here
     when None; False runs without it."""
+    _require(isinstance(x, torch.Tensor) and x.dim() == 2, "x must be a 2-D tensor")
     rows, cols = x.shape
     if qr is None:
         qr = torch.empty((rows, padded_len(cols, block)), dtype=q_dtype, device=x.device)
@@ -259,6 +324,18 @@ def fwht_quant_dual(x, block=256, q_dtype=torch.int8, qr=None, scale_r=None, qc=
         qc = torch.empty((cols, padded_len(rows, block)), dtype=q_dtype, device=x.device)
     if scale_c is None:
         scale_c = torch.empty(cols, dtype=torch.float32, device=x.device)
+    _matrix(qr, "qr", (rows, padded_len(cols, block)), dtype=q_dtype)
+    _matrix(qc, "qc", (cols, padded_len(rows, block)), dtype=q_dtype)
+    _vector(scale_r, "scale_r", rows, torch.float32)
+    _vector(scale_c, "scale_c", cols, torch.float32)
+    if row_signs is not None:
+        _vector(row_signs, "row_signs", _sign_words(padded_len(cols, block)), torch.int32)
+    if col_signs is not None:
+        _vector(col_signs, "col_signs", _sign_words(padded_len(rows, block)), torch.int32)
+    if workspace is not None and workspace is not False:
+        _bytes(workspace, "workspace")
+    _same_gpu(x, qr=qr, qc=qc, scale_r=scale_r, scale_c=scale_c, row_signs=row_signs,
+              col_signs=col_signs, workspace=workspace if workspace is not False else None)
     if workspace is False:
         ws_ptr, ws_bytes = None, 0
     else:
@@ -297,7 +374,15 @@ def fwht_quant_noalloc(x, q, scale, axis=ROWS, block=256, stream=None, signs=Non
     """fwht_quant into caller-provided q and scale with the library's fixed scratch in place of
     a workspace (halo_fwht_quant_noalloc): nothing is allocated.  Calls that may overlap on one
     device share that scratch and must be ordered by the caller."""
+    _require(isinstance(x, torch.Tensor) and x.dim() == 2, "x must be a 2-D tensor")
     rows, cols = x.shape
+    nvec, L = (rows, cols) if axis == ROWS else (cols, rows)
+    Lp = padded_len(L, block)
+    _matrix(q, "q", (nvec, Lp))
+    _vector(scale, "scale", nvec, torch.float32)
+    if signs is not None:
+        _vector(signs, "signs", _sign_words(Lp), torch.int32)
+    _same_gpu(x, q=q, scale=scale, signs=signs)
     opts = None
     rnd = _rounding(rounding)
     if signs is not None or rnd != NEAREST or exchange_polls:
@@ -312,10 +397,18 @@ def fwht_quant_noalloc(x, q, scale, axis=ROWS, block=256, stream=None, signs=Non
 
 def gemm_i8(a, sa, b, sb, out_dtype=torch.bfloat16, c=None, stream=None):
     """c = (a . b^T) * sa[:, None] * sb[None, :] with int8 codes (int32 raw if out is int32)."""
+    _require(isinstance(a, torch.Tensor) and a.dim() == 2 and isinstance(b, torch.Tensor)
+             and b.dim() == 2, "a and b must be 2-D tensors")
     m, k = a.shape
     n = b.shape[0]
+    _matrix(b, "b", (n, k))
     if c is None:
         c = torch.empty((m, n), dtype=out_dtype, device=a.device)
+    _matrix(c, "c", (m, n))
+    if c.dtype != torch.int32:  # the raw int32 output takes no scales
+        _vector(sa, "sa", m, torch.float32)
+        _vector(sb, "sb", n, torch.float32)
+    _same_gpu(a, b=b, c=c, sa=sa, sb=sb)
     st = lib().halo_gemm_i8(_ptr(a), _ld(a), _ptr(sa), _ptr(b), _ld(b), _ptr(sb), m, n, k,
                             _ptr(c), _code(c.dtype), _ld(c), _stream(stream))
     _check(st, "halo_gemm_i8")
@@ -324,10 +417,18 @@ def gemm_i8(a, sa, b, sb, out_dtype=torch.bfloat16, c=None, stream=None):
 
 def gemm_fp8(a, sa, b, sb, out_dtype=torch.bfloat16, c=None, stream=None):
     """c = (dec(a) . dec(b)^T) * sa[:, None] * sb[None, :] with fp8 codes (E4M3 / E5M2)."""
+    _require(isinstance(a, torch.Tensor) and a.dim() == 2 and isinstance(b, torch.Tensor)
+             and b.dim() == 2, "a and b must be 2-D tensors")
     m, k = a.shape
     n = b.shape[0]
+    _matrix(b, "b", (n, k))
     if c is None:
         c = torch.empty((m, n), dtype=out_dtype, device=a.device)
+    _matrix(c, "c", (m, n))
+    if c.dtype != torch.int32:  # the raw int32 output takes no scales
+        _vector(sa, "sa", m, torch.float32)
+        _vector(sb, "sb", n, torch.float32)
+    _same_gpu(a, b=b, c=c, sa=sa, sb=sb)
     st = lib().halo_gemm_fp8(_ptr(a), _code(a.dtype), _ld(a), _ptr(sa), _ptr(b), _code(b.dtype),
                              _ld(b), _ptr(sb), m, n, k, _ptr(c), _code(c.dtype), _ld(c),
                              _stream(stream))
@@ -354,10 +455,20 @@ def linear_fwd(x, w, block, q_dtype=torch.int8, y=None, y_dtype=None, workspace=
                stream=None, signs_k=None):
     """Y = X W^T with both operands rotated and quantised along K (the layer's forward);
     signs_k: the randomised transform's sign words along K (see hadamard_signs) or None."""
+    _require(isinstance(x, torch.Tensor) and x.dim() == 2 and isinstance(w, torch.Tensor)
+             and w.dim() == 2, "x and w must be 2-D tensors")
     m, k = x.shape
     n = w.shape[0]
+    _matrix(x, "x", (m, k), contiguous=True)
+    _matrix(w, "w", (n, k), dtype=x.dtype, contiguous=True)
     if y is None:
         y = torch.empty((m, n), dtype=y_dtype or x.dtype, device=x.device)
+    _matrix(y, "y", (m, n), contiguous=True)
+    if signs_k is not None:
+        _vector(signs_k, "signs_k", _sign_words(contraction_len(k, block)), torch.int32)
+    if workspace is not None:
+        _bytes(workspace, "workspace")
+    _same_gpu(x, w=w, y=y, signs_k=signs_k, workspace=workspace)
     need = linear_workspace_bytes(m, n, k, q_dtype, False, block)
     ws = _workspace(need, x.device, workspace)
     opts = LinearOpts(_ptr(signs_k), None, None, NEAREST) if signs_k is not None else None
@@ -378,13 +489,30 @@ def linear_bwd(dy, x, w, block, q_dtype=torch.int8, grad_q_dtype=None, want_dx=T
     grad_rounding: "nearest" or "stochastic" rounding of the dY codes (Philox key `seed`,
     counter words 2-3 `counter`; the columns of dY draw with counter word 3 ^ 2^31).
     exchange_polls: as in fwht_quant, for the columns along m."""
+    _require(all(isinstance(t, torch.Tensor) and t.dim() == 2 for t in (dy, x, w)),
+             "dy, x and w must be 2-D tensors")
     m, k = x.shape
     n = w.shape[0]
+    _matrix(x, "x", (m, k), contiguous=True)
+    _matrix(w, "w", (n, k), dtype=x.dtype, contiguous=True)
+    _matrix(dy, "dy", (m, n), dtype=x.dtype, contiguous=True)
     grad_q_dtype = grad_q_dtype or q_dtype
     if want_dx and dx is None:
         dx = torch.empty((m, k), dtype=x.dtype, device=x.device)
     if want_dw and dw is None:
         dw = torch.empty((n, k), dtype=x.dtype, device=x.device)
+    if want_dx:
+        _matrix(dx, "dx", (m, k), contiguous=True)
+    if want_dw:
+        _matrix(dw, "dw", (n, k), contiguous=True)
+    if signs_n is not None:
+        _vector(signs_n, "signs_n", _sign_words(contraction_len(n, block)), torch.int32)
+    if signs_m is not None:
+        _vector(signs_m, "signs_m", _sign_words(contraction_len(m, block)), torch.int32)
+    if workspace is not None:
+        _bytes(workspace, "workspace")
+    _same_gpu(x, dy=dy, w=w, dx=dx if want_dx else None, dw=dw if want_dw else None,
+              signs_n=signs_n, signs_m=signs_m, workspace=workspace)
     need = linear_workspace_bytes(m, n, k, q_dtype, True, block)
     ws = _workspace(need, x.device, workspace)
     rnd = _rounding(grad_rounding)
