@@ -188,9 +188,11 @@ class ClockSampler:
                 pass
 
     def _run(self):
-        while not self._stop.is_set():
+        # waiting on the stop event (not sleeping) lets __exit__ return at once, without an
+        # idle gap on the GPU while the caller joins the thread
+        self._read()
+        while not self._stop.wait(self.period):
             self._read()
-            time.sleep(self.period)
 
     def __enter__(self):
         self._thread.start()
@@ -216,21 +218,26 @@ class ClockSampler:
 def settle(step, seconds, torch, sampler=None):
     """Run steps until `seconds` have passed (in groups of 10, synchronised): the clock-settle
     phase before the counted warmup.  With a ClockSampler, the shader clock and board power
-    are sampled over the phase's second half, the steady state of the same steps (sampling
-    sysfs while steps run slows them by about 2 %, so the counted steps run unsampled).
-    Returns (steps run, seconds)."""
+    are sampled from 40 % to 80 % of the phase, the steady state of the same steps (sampling
+    sysfs while steps run slows them by about 2 %, so the counted steps run unsampled); the
+    phase's last fifth runs unsampled, so the steps that follow start from the same steady
+    state.  Returns (steps run, seconds)."""
     t0 = time.perf_counter()
     n = 0
-    started = False
+    state = 0  # 0: before sampling, 1: sampling, 2: done
     while time.perf_counter() - t0 < seconds:
-        if sampler is not None and not started and time.perf_counter() - t0 >= seconds / 2:
+        el = time.perf_counter() - t0
+        if sampler is not None and state == 0 and el >= 0.4 * seconds:
             sampler.__enter__()
-            started = True
+            state = 1
+        elif state == 1 and el >= 0.8 * seconds:
+            sampler.__exit__(None, None, None)
+            state = 2
         for _ in range(10):
             step(n)
             n += 1
         torch.cuda.synchronize()
-    if started:
+    if state == 1:
         sampler.__exit__(None, None, None)
     return n, time.perf_counter() - t0
 
@@ -1051,7 +1058,7 @@ def main():
         "settle": {"steps": settle_steps, "s": round(settle_s, 2),
                    "what": "steps run before the counted warmup, until the clock settles"},
         "clock": {"steps": clk.summary() | {
-                      "what": "sampled every 10 ms over the second half of the clock-settle "
+                      "what": "sampled every 10 ms from 40 % to 80 % of the clock-settle "
                               "phase: the same steps in steady state (the counted steps run "
                               "unsampled: sampling slows them by about 2 %)"},
                   "kernel_legs": clk_k.summary()},
