@@ -262,8 +262,12 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_kernel(GemmPair gp) {
       else dst->lo = v;
     }
   };
+  // front: every fragment read right after the sub-step's first MFMA instead of one or two
+  // per MFMA.  For the sub-step before the slab barrier: the barrier must wait for these
+  // reads (the slab's ring slot is refilled after it), so issuing them first gives them the
+  // whole sub-step to land (same-box A/Bs: 0.2-0.9 % faster).
   auto ordered_step = [&](const Frag* da, const Frag* db, int rkt, int rks, Frag* nda, Frag* ndb,
-                          int lkt, bool loads) __attribute__((always_inline)) {
+                          int lkt, bool loads, bool front) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < NMF; ++t) {
       const int i = t / FA, j = t % FA;
@@ -272,8 +276,10 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_kernel(GemmPair gp) {
       else  // first operand = b tile (format BF), second = a tile (format AF); scales 2^0
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(db[i], da[j], acc[i][j], BF,
                                                                     AF, 0, 127, 0, 127);
+      const int r0 = front ? (t == 0 ? 0 : FRAG_READS) : t * FRAG_READS / NMF;
+      const int r1 = front ? FRAG_READS : (t + 1) * FRAG_READS / NMF;
 #pragma unroll
-      for (int q = t * FRAG_READS / NMF; q < (t + 1) * FRAG_READS / NMF; ++q)
+      for (int q = r0; q < r1; ++q)
         read_one(rkt, rks, q, nda, ndb);
       if (loads) stage_part(lkt, t * 2 * INST / NMF, (t + 1) * 2 * INST / NMF);
       __builtin_amdgcn_sched_barrier(0);
@@ -285,11 +291,13 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_kernel(GemmPair gp) {
     for (int ks = 0; ks < KS; ++ks) {
       const int cur = (P0 + ks) & 1;
       if (ks + 1 < KS) {
-        ordered_step(fa[cur], fb[cur], kt, ks + 1, fa[cur ^ 1], fb[cur ^ 1], 0, false);
+        ordered_step(fa[cur], fb[cur], kt, ks + 1, fa[cur ^ 1], fb[cur ^ 1], 0, false,
+                     ks + 2 == KS);
       } else {
         __builtin_amdgcn_s_waitcnt(HALO_VMCNT(2 * INST * (NSTAGE - 2)));  // slab kt + 1 landed
         __syncthreads();
-        ordered_step(fa[cur], fb[cur], kt + 1, 0, fa[cur ^ 1], fb[cur ^ 1], kt + NSTAGE, true);
+        ordered_step(fa[cur], fb[cur], kt + 1, 0, fa[cur ^ 1], fb[cur ^ 1], kt + NSTAGE, true,
+                     false);
       }
     }
   };
