@@ -98,12 +98,14 @@ def fp32_rotation_code_bound(x, oaxis, block, qtype, opts=None, vec_idx=None):
 
 def assert_fp8_codes_close_to_exact(gpu_q, x, oaxis, block, qtype, stochastic=False, opts=None,
                                     vec_idx=None):
-    """FP8 codes of fp32 input against the exact real code value t of the fp64 definition: the
-    decoded code lies within half a grid step (a whole step for stochastic rounding) plus the
-    fp32 rotation's error bound of t.  This is the code bar read for fp32 input: where the
-    fp32 butterflies' rounding (within the FWHT bar) spans more than a grid step -- near zero,
+    """FP8 codes against the exact real code value t of the fp64 definition: the decoded code
+    lies within half a grid step (a whole step for stochastic rounding) plus the fp32
+    rotation's error bound of t.  This is the code bar read for FP8 codes: where the fp32
+    butterflies' rounding (within the FWHT bar) spans more than a grid step -- near zero,
     where the E5M2 subnormal spacing is 2^-16 code units -- the fp32 and fp64 decisions
-    legitimately differ by several steps."""
+    legitimately differ by several steps.  The butterflies round for fp32 input, and for bf16
+    input too once a block's sums need more than fp32's 24 bits (inputs spanning several
+    binades, blocks of thousands)."""
     t, e = fp32_rotation_code_bound(x, oaxis, block, qtype, opts, vec_idx)
     g = fp8_table(qtype)[np.asarray(gpu_q)]
     step = fp8_step(np.abs(t) + e, qtype)
@@ -138,9 +140,10 @@ def assert_codes_close_to_fp64(gpu_q, ref_q, qtype, block, frac=1e-4, x=None, oa
     always allowed: on a few thousand codes one fp32-vs-fp64 split near a rounding midpoint is
     an ordinary event, not a sign of a wrong kernel (those are caught bit-exactly against the
     fp32-decision oracle).  With the input x given (axis oaxis, oracle options opts):
-    - fp32 input with FP8 codes: each code is held to the exact value within half a grid step
-      plus the fp32 rotation's error bound (assert_fp8_codes_close_to_exact) instead of one
-      grid step;
+    - FP8 codes: each code is held to the exact value within half a grid step plus the fp32
+      rotation's error bound (assert_fp8_codes_close_to_exact) instead of one grid step, for
+      fp32 and bf16 input alike (the fp32 butterflies round once a block's sums need more
+      than 24 bits, and near zero the FP8 grid is far finer than that rounding);
     - nearest rounding: the fraction counts only codes that fp32 arithmetic can decide, those
       whose exact value lies farther than the fp32 path's error bound from a rounding midpoint
       (undecidable_in_fp32; exact ties are the common case, and on padding-dominated vectors one
@@ -153,9 +156,9 @@ def assert_codes_close_to_fp64(gpu_q, ref_q, qtype, block, frac=1e-4, x=None, oa
         return
     d = code_distance(gpu_q, ref_q, qtype)
     sr = bool(opts) and opts.get("rounding") == O.STOCHASTIC
-    if x is not None and x.dtype == np.float32 and qtype in FP8_GRID:
-        # fp32 input, FP8 codes: each code against the exact value and the fp32 rotation's
-        # error bound instead of one grid step (see assert_fp8_codes_close_to_exact)
+    if x is not None and qtype in FP8_GRID:
+        # FP8 codes: each code against the exact value and the fp32 rotation's error bound
+        # instead of one grid step (see assert_fp8_codes_close_to_exact)
         assert_fp8_codes_close_to_exact(gpu_q, x, oaxis, block, qtype, sr, opts, vec_idx)
         d = np.minimum(d, 1)
     assert d.max(initial=0) <= 1, f"code off by {d.max()}"
@@ -260,3 +263,29 @@ def bound_ok(got, ref, rel, extra=0.0):
 
 def to_np64(t):
     return t.float().cpu().numpy().astype(np.float64)
+
+
+def random_rotation_case(case):
+    """Seeded random rotation pass number `case`: random valid sizes, block, code type, input
+    type, signs and rounding, all drawn from its own generator (the GPU random-shape test and
+    the CPU bar tests replay the same cases).  Returns a dict with axis (0 rows, 1 columns),
+    io, qt, block, rows, cols, sr, words (sign words or None) and x (bf16 bits or fp32)."""
+    import synth
+    rng = np.random.default_rng(5000 + case)
+    axis = int(rng.integers(0, 2))
+    io = synth.BF16 if rng.random() < 0.75 else synth.F32
+    qt = (O.I8, O.E4M3, O.E5M2)[int(rng.integers(0, 3))]
+    b = 1 << int(rng.integers(0, 13))
+    # sizes the library takes: lengths and code rows in whole 16-byte units
+    if axis == 0:
+        rows, cols = int(rng.integers(1, 300)), 16 * int(rng.integers(1, 350))
+    else:
+        long_cols = rng.random() < 0.3  # columns longer than 4096: partial maxima exchanged
+        rows = 16 * int(rng.integers(257, 560) if long_cols else rng.integers(1, 120))
+        cols = 8 * int(rng.integers(1, 40 if long_cols else 120))
+    signs, sr = rng.random() < 0.4, rng.random() < 0.3
+    L = cols if axis == 0 else rows
+    words = synth.sign_words(O.padded_len(L, b), seed=case) if signs else None
+    a = synth.activations(rng, rows, cols)
+    x = synth.bf16_bits(a) if io == synth.BF16 else a
+    return dict(axis=axis, io=io, qt=qt, block=b, rows=rows, cols=cols, sr=sr, words=words, x=x)

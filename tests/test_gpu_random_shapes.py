@@ -15,12 +15,9 @@ import hadamard_rotated_precision_halo_amd as H
 import oracle as O
 import synth
 from parity_util import COUNTER64, CTR, KEY, Q_TORCH, SEED64, bound_ok, check_fq_parity, \
-    codes_to_np, fp8_extra, rel_fro, signs_dev, to_dev, to_np64
+    codes_to_np, fp8_extra, random_rotation_case, rel_fro, signs_dev, to_dev, to_np64
 
 pytestmark = pytest.mark.gpu
-
-QTS = [O.I8, O.E4M3, O.E5M2]
-
 
 def _block(rng):
     return 1 << int(rng.integers(0, 13))
@@ -28,26 +25,12 @@ def _block(rng):
 
 @pytest.mark.parametrize("case", range(24))
 def test_random_rotation_pass(case):
-    rng = np.random.default_rng(5000 + case)
-    axis = int(rng.integers(0, 2))
-    io = synth.BF16 if rng.random() < 0.75 else synth.F32
-    qt, b = QTS[int(rng.integers(0, 3))], _block(rng)
-    # sizes the library takes: lengths and code rows in whole 16-byte units
-    if axis == 0:
-        rows, cols = int(rng.integers(1, 300)), 16 * int(rng.integers(1, 350))
-    else:
-        long_cols = rng.random() < 0.3  # columns longer than 4096: partial maxima exchanged
-        rows = 16 * int(rng.integers(257, 560) if long_cols else rng.integers(1, 120))
-        cols = 8 * int(rng.integers(1, 40 if long_cols else 120))
-    signs, sr = rng.random() < 0.4, rng.random() < 0.3
-    L = cols if axis == 0 else rows
-    words = synth.sign_words(O.padded_len(L, b), seed=case) if signs else None
-    a = synth.activations(rng, rows, cols)
-    x = synth.bf16_bits(a) if io == synth.BF16 else a
-    print(f"case {case}: axis {axis} io {io} {rows}x{cols} block {b} code {qt} signs {signs} "
-          f"sr {sr}", flush=True)
+    c = random_rotation_case(case)
+    axis, b, qt, x, words, sr = c["axis"], c["block"], c["qt"], c["x"], c["words"], c["sr"]
+    print(f"case {case}: axis {axis} io {c['io']} {c['rows']}x{c['cols']} block {b} code {qt} "
+          f"signs {words is not None} sr {sr}", flush=True)
     q, s = H.fwht_quant(to_dev(x), axis=H.ROWS if axis == 0 else H.COLS, block=b,
-                        q_dtype=Q_TORCH[qt], signs=signs_dev(words) if signs else None,
+                        q_dtype=Q_TORCH[qt], signs=signs_dev(words) if words is not None else None,
                         rounding="stochastic" if sr else "nearest", seed=SEED64,
                         counter=COUNTER64)
     torch.cuda.synchronize()

@@ -1,11 +1,12 @@
 """CPU checks of the parity bars themselves (tests/parity_util.py), with the oracle standing in
 for the GPU: a bar must accept what a correct fp32 computation gives and reject planted errors.
 
-The fp32-input FP8 code bar: with fp32 input the butterflies round (bf16 sums do not), and near
-zero the E5M2 grid (2^-16 code units apart) is much finer than that rounding, so the oracle's
-own fp32-decision codes may sit several grid steps from its fp64 decision there.  The bar
-holds every code to the exact value within half a grid step plus an a-priori bound on the fp32
-rotation's error; it must accept those codes and still reject a code moved by a few steps.
+The FP8 code bar: where the fp32 butterflies round (fp32 input; bf16 input too once a block's
+sums need more than 24 bits), near zero the E5M2 grid (2^-16 code units apart) is much finer
+than that rounding, so the oracle's own fp32-decision codes may sit several grid steps from its
+fp64 decision there.  The bar holds every code to the exact value within half a grid step plus
+an a-priori bound on the fp32 rotation's error; it must accept those codes and still reject a
+code moved by a few steps.
 """
 import numpy as np
 import pytest
@@ -72,3 +73,29 @@ def test_ties_repeated_by_padding_do_not_count():
         bad[i, j] += 1
     with pytest.raises(AssertionError):
         P.assert_codes_close_to_fp64(bad, q64, O.I8, 4096, x=x, oaxis=O.COLS)
+
+
+def test_bf16_input_fp8_code_near_zero():
+    # random rotation case 1902: 41 bf16 rows of 4160 with outlier channels, block 4096 (rows
+    # padded to 8192), E5M2 codes, signs.  The block's sums need more than fp32's 24 bits, so
+    # the fp32 butterflies round; one code's exact value is -0.0017 code units against an fp32
+    # bound of 0.42, and the fp32 decision (the GPU's, bit for bit) lands 23 E5M2 steps from
+    # the fp64 one.  The value bar accepts it; a code moved beyond the bound still fails.
+    c = P.random_rotation_case(1902)
+    x, b, qt, words = c["x"], c["block"], c["qt"], c["words"]
+    assert c["axis"] == 0 and x.dtype == np.uint16 and qt == O.E5M2 and not c["sr"]
+    opts = dict(signs=words, rounding=O.RNE)
+    q32, _ = O.fwht_quant(x, O.ROWS, b, qt, precision=32, **opts)
+    q64, _ = O.fwht_quant(x, O.ROWS, b, qt, precision=64, **opts)
+    d = P.code_distance(q32, q64, qt)
+    assert d.max() > 1                  # the case the bar exists for
+    P.assert_codes_close_to_fp64(q32, q64, qt, b, x=x, oaxis=O.ROWS, opts=opts)
+    i = np.unravel_index(np.argmax(d), d.shape)
+    t, e = P.fp32_rotation_code_bound(x, O.ROWS, b, qt, opts)
+    assert abs(t[i]) < e[i]             # undecidable in fp32: the bound exceeds the value
+    table = O.fp8_table(qt)
+    far = t[i] + 4 * e[i] + 1.0         # a value well beyond the bound
+    bad = q32.copy()
+    bad[i] = int(np.nanargmin(np.abs(table - far)))
+    with pytest.raises(AssertionError):
+        P.assert_codes_close_to_fp64(bad, q64, qt, b, x=x, oaxis=O.ROWS, opts=opts)
