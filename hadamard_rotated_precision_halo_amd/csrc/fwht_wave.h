@@ -279,6 +279,57 @@ __device__ __forceinline__ void store_slice(const FqArgs& a, const float* v, flo
   }
 }
 
+// Staged code stores.  In the slice layout a store instruction of store_slice writes the
+// wave's codes as 16 runs of 32 bytes (chunk j of the lanes of each block); written
+// contiguously, 16 bytes per lane and 1 KB per instruction, the same codes leave the CU in
+// fewer, whole-line requests.  A wave whose codes form one contiguous run (rows of 4096 or
+// more positions) writes its chunks into its own LDS area at their slice offsets and reads
+// them back contiguously.  Every 256 bytes of the area are followed by 32 bytes of padding, so
+// the 8-byte chunk writes of 32 lanes (8 blocks, 32 contiguous bytes each) and the 16-byte
+// read-back both touch all 64 banks once.
+constexpr int kStageBytes = 4096 + 16 * 32;  // LDS bytes per wave
+
+__device__ __forceinline__ int stage_off(int b) { return b + (b >> 8) * 32; }
+
+// The 8 codes of chunk j of the lane (nearest, or stochastic rounding as store_chunk8_sr).
+template <int QT, bool SR>
+__device__ __forceinline__ uint2 chunk_codes(const FqArgs& a, const float* y, float mul,
+                                             int64_t vec, int64_t pos) {
+  if constexpr (SR) {
+    uint32_t w[8];
+    sr_words8(vec, pos, a.key0, a.key1, a.ctr2, a.ctr3, w);
+    float t[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t[e] = sr_value<QT>(mulz(y[e], mul), w[e], a.qmax);
+    return encode8<QT>(t, 1.f);
+  } else {
+    return encode8<QT>(y, mul);
+  }
+}
+
+// store_slice for code types through the wave's LDS area `st`: the codes at slice offsets
+// [0, n) (n a multiple of 16; the lanes holding them call this) go to elements base + [0, n)
+// of the code array.
+template <int B, int QT, bool SR>
+__device__ __forceinline__ void store_slice_staged(const FqArgs& a, const float* v, float mul,
+                                                   int64_t base, int lane, int64_t vec,
+                                                   int64_t pos0, int n, uint8_t* st) {
+  using S = Slice<B>;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int o = S::off(lane, j);
+    *reinterpret_cast<uint2*>(st + stage_off(o)) =
+        chunk_codes<QT, SR>(a, &v[j * 8], mul, vec, pos0 + o);
+  }
+  // the wave's LDS accesses complete in order: the reads see every lane's writes
+  uint8_t* q = reinterpret_cast<uint8_t*>(a.q) + base;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int b = i * 1024 + lane * 16;
+    if (b < n) *reinterpret_cast<uint4*>(q + b) = *reinterpret_cast<const uint4*>(st + stage_off(b));
+  }
+}
+
 // Load the 8 chunks of a lane: chunk j at position pos0 + off(lane, j) of the vector whose
 // element 0 is at vp.  The loads are unconditional (a chunk of the zero padding, at and past
 // in_len, reads chunk 0 instead), so they issue back to back; only passes with padding then
@@ -368,6 +419,10 @@ template <typename Tin, int B, int QT, bool SR>
 __global__ __launch_bounds__(1024) void fq_rows2_kernel(FqPair pp, int multi) {
   using S = Slice<B>;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  // code types: each wave's staging area for contiguous code stores (launched with
+  // nw * kStageBytes of dynamic LDS)
+  extern __shared__ __attribute__((aligned(16))) uint8_t s_stage[];
+  uint8_t* st = s_stage + (int)__builtin_amdgcn_readfirstlane(w) * kStageBytes;
   if (pp.zero) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < pp.nzero; i += stride)
@@ -377,6 +432,20 @@ __global__ __launch_bounds__(1024) void fq_rows2_kernel(FqPair pp, int multi) {
   const FqArgs a = second ? pp.p1 : pp.p0;
   const int bid = (int)(blockIdx.x - (second ? pp.split : 0));
   if (!multi) {
+    if (QT != 3 && a.len == 4096) {
+      // one whole row per wave: its codes are one contiguous run of 4096 bytes
+      const int64_t row = (int64_t)bid * nw + w;
+      if (row >= a.nvec) return;
+      const Tin* rp = reinterpret_cast<const Tin*>(a.x) + row * a.ldx;
+      float v[64];
+      load_slice<Tin, B>(a, rp, 0, lane, true, v);
+      const float sgn = rotate64<B>(v, lane);
+      const float mx = lane_max(absmax64(v), 6);
+      if (lane == 0) a.scale[row] = stored_scale<QT>(a, mx);
+      const float mul = quant_mul_v<QT>(a, mx, v) * sgn;
+      store_slice_staged<B, QT, SR>(a, v, mul, row * a.ldq, lane, row, 0, 4096, st);
+      return;
+    }
     rows_wave<Tin, B, QT, SR>(a, (int64_t)bid * nw + w, lane);
     return;
   }
@@ -398,9 +467,20 @@ __global__ __launch_bounds__(1024) void fq_rows2_kernel(FqPair pp, int multi) {
     for (int i = 0; i < nw; ++i) mx = __builtin_fmaxf(mx, s_wmax[i]);
   }
   if (w == 0 && lane == 0) a.scale[row] = stored_scale<QT>(a, mx);
-  if (!valid) return;
-  const float mul = quant_mul_v<QT>(a, mx, v) * sgn;
-  store_slice<B, QT, SR>(a, v, mul, row * a.ldq + col0, lane, row, col0);
+  if constexpr (QT != 3) {
+    // the wave's codes: positions [col0, min(col0 + 4096, len)) of the row, contiguous (len is
+    // a multiple of 64 here, so the run is a multiple of 16 bytes).  Every lane takes part:
+    // the read-back gives bytes to lanes by position, and lanes past the row end write their
+    // chunks past the run, which is not stored
+    const float mul = quant_mul_v<QT>(a, mx, v) * sgn;
+    const int64_t rest = a.len - col0;
+    store_slice_staged<B, QT, SR>(a, v, mul, row * a.ldq + col0, lane, row, col0,
+                                  (int)(rest < 4096 ? rest : 4096), st);
+  } else {
+    if (!valid) return;
+    const float mul = quant_mul_v<QT>(a, mx, v) * sgn;
+    store_slice<B, QT, SR>(a, v, mul, row * a.ldq + col0, lane, row, col0);
+  }
 }
 
 // Workgroups of one rows pass (0 for an empty one).
@@ -426,8 +506,13 @@ static hipError_t launch_rows2_t(FqPair pp, hipStream_t st) {
   // beat one single-wave workgroup per row: 11.74 against 11.43 us per 4096^2 pass)
   const int multi = L > 4096 ? 1 : 0;
   const int nw = multi ? (int)((L + 4095) / 4096) : 4;
-  hipLaunchKernelGGL((fq_rows2_kernel<Tin, B, QT, SR>), dim3((unsigned)grid), dim3(64 * nw), 0, st,
-                     pp, multi);
+  const int lds = QT != 3 && (multi || L == 4096) ? nw * kStageBytes : 0;
+  if (lds > 65536) {
+    const hipError_t e = allow_dynamic_lds<&fq_rows2_kernel<Tin, B, QT, SR>>(16 * kStageBytes);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((fq_rows2_kernel<Tin, B, QT, SR>), dim3((unsigned)grid), dim3(64 * nw), lds,
+                     st, pp, multi);
   return hipGetLastError();
 }
 
